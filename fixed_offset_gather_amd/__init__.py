@@ -1,0 +1,345 @@
+"""Python binding of libsfa: sparse fixed-offset attention on MI355X.
+
+Argument marshalling only.  Every step of the attention runs in the HIP
+kernels of ``libsfa.so`` (built in-tree by ``fixed_offset_gather_amd.build``);
+the host producers (offsets, schedules, Christoffel offsets, power-law edge
+lists, rotary table) run in the same library's C++ code.  PyTorch supplies
+device memory and the current stream.  There is no fallback: if the library
+is missing, importing this package raises.
+
+Tensor layouts: q, o, dout, dq [B, n, Hq, D]; k, v, dk, dv [B, n, Hkv, D];
+lse float32 [B, Hq, n].  dtype float32 or bfloat16, contiguous, on a GPU.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+# torch ships its own HIP runtime with the same soname as the system one.
+# Importing torch first makes libsfa bind to that already-loaded runtime, so
+# the process holds a single HIP runtime and the library launches on the
+# devices and streams torch created.
+import torch  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsfa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libsfa.so is not built; run `python -m fixed_offset_gather_amd.build` "
+        "(hipcc, gfx950).  There is no CPU fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SFA_OK = 0
+SFA_ERR_ARG = -1
+SFA_ERR_CAPACITY = -2
+SFA_ERR_UNSUPPORTED = -3
+SFA_ERR_HIP = -4
+SFA_F32 = 0
+SFA_BF16 = 1
+MAX_OFFSETS = 128
+MAX_SLOTS = 192
+SCHEDULES = {"fixed": 0, "linear": 1, "coprime": 2}
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_vp = ctypes.c_void_p
+
+
+class SfaAttn(ctypes.Structure):
+    """Mirror of ``sfa_attn`` in include/sfa.h."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+        ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("n_off", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("off_lo", _i32p), ("off_frac", _f32p), ("rope", _vp),
+    ]
+
+
+def _sig(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_c = ctypes
+_sig("sfa_last_error", _c.c_char_p, [])
+_sig("sfa_version", _c.c_int, [])
+_sig("sfa_base_fib", _c.c_int, [_i32p, _c.c_int])
+_sig("sfa_base_pow2", _c.c_int, [_i32p, _c.c_int])
+_sig("sfa_offsets_scaled", _c.c_int, [_i32p, _c.c_int, _c.c_double, _i32p, _f32p])
+_sig("sfa_offsets_fib", _c.c_int, [_c.c_double, _i32p, _f32p, _c.c_int])
+_sig("sfa_offsets_pow2", _c.c_int, [_c.c_double, _i32p, _f32p, _c.c_int])
+_sig("sfa_stagger_alpha", _c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_double)])
+_sig("sfa_alpha_of_theta", _c.c_int, [_c.c_double, _c.POINTER(_c.c_double), _c.POINTER(_c.c_double)])
+_sig("sfa_offsets_christoffel", _c.c_int, [_c.c_int, _c.c_int, _i32p, _c.c_int])
+_sig("sfa_edges_powerlaw", _c.c_int, [_c.c_int, _c.c_int, _c.c_double, _c.c_int, _c.c_int,
+                                      _c.c_uint64, _i32p, _i32p])
+_sig("sfa_rope_table", _c.c_int, [_c.c_int, _c.c_int, _c.c_double, _f32p])
+_sig("sfa_fwd", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _vp, _vp, _vp, _vp])
+_sig("sfa_fwd_edges", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _c.c_int, _vp, _vp, _vp, _vp, _vp, _vp])
+_sig("sfa_bwd_workspace_bytes", _c.c_size_t, [_c.POINTER(SfaAttn)])
+_sig("sfa_bwd", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                           _vp, _i32p, _c.c_double, _vp, _vp, _c.c_size_t, _vp])
+_sig("sfa_profile_enable", _c.c_int, [_c.c_int])
+_sig("sfa_profile_read", _c.c_int, [_c.c_char_p, _c.POINTER(_c.c_double), _c.POINTER(_c.c_int64)])
+_sig("sfa_profile_reset", _c.c_int, [])
+
+
+class SfaError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        msg = _lib.sfa_last_error().decode(errors="replace")
+        super().__init__("%s failed (%d): %s" % (fn, code, msg))
+
+
+def _check(fn, rc):
+    if rc < 0:
+        raise SfaError(fn, rc)
+    return rc
+
+
+def library():
+    """The loaded ctypes library (for ABI tests)."""
+    return _lib
+
+
+def _ip(a):
+    return a.ctypes.data_as(_i32p)
+
+
+def _fp(a):
+    return a.ctypes.data_as(_f32p)
+
+
+# ------------------------------------------------------------ host producers
+
+def base_fib():
+    out = np.zeros(15, dtype=np.int32)
+    _check("sfa_base_fib", _lib.sfa_base_fib(_ip(out), 15))
+    return out
+
+
+def base_pow2():
+    out = np.zeros(11, dtype=np.int32)
+    _check("sfa_base_pow2", _lib.sfa_base_pow2(_ip(out), 11))
+    return out
+
+
+def offsets_scaled(base, alpha):
+    base = np.ascontiguousarray(base, dtype=np.int32)
+    lo = np.zeros(len(base), dtype=np.int32)
+    frac = np.zeros(len(base), dtype=np.float32)
+    _check("sfa_offsets_scaled",
+           _lib.sfa_offsets_scaled(_ip(base), len(base), float(alpha), _ip(lo), _fp(frac)))
+    return lo, frac
+
+
+def offsets_fib(alpha):
+    lo = np.zeros(15, dtype=np.int32)
+    frac = np.zeros(15, dtype=np.float32)
+    _check("sfa_offsets_fib", _lib.sfa_offsets_fib(float(alpha), _ip(lo), _fp(frac), 15))
+    return lo, frac
+
+
+def offsets_pow2(alpha):
+    lo = np.zeros(11, dtype=np.int32)
+    frac = np.zeros(11, dtype=np.float32)
+    _check("sfa_offsets_pow2", _lib.sfa_offsets_pow2(float(alpha), _ip(lo), _fp(frac), 11))
+    return lo, frac
+
+
+def stagger_alpha(schedule, layer, L=16, S=7):
+    out = ctypes.c_double()
+    sched = SCHEDULES[schedule] if isinstance(schedule, str) else int(schedule)
+    _check("sfa_stagger_alpha", _lib.sfa_stagger_alpha(sched, layer, L, S, ctypes.byref(out)))
+    return out.value
+
+
+def alpha_of_theta(theta):
+    a, d = ctypes.c_double(), ctypes.c_double()
+    _check("sfa_alpha_of_theta", _lib.sfa_alpha_of_theta(float(theta), ctypes.byref(a), ctypes.byref(d)))
+    return a.value, d.value
+
+
+def offsets_christoffel(m, k):
+    out = np.zeros(max(m, 1), dtype=np.int32)
+    cnt = _check("sfa_offsets_christoffel", _lib.sfa_offsets_christoffel(m, k, _ip(out), len(out)))
+    return out[:cnt].copy()
+
+
+def edges_powerlaw(n, r, sigma, draws, width, seed):
+    edges = np.zeros((n, width), dtype=np.int32)
+    count = np.zeros(n, dtype=np.int32)
+    _check("sfa_edges_powerlaw",
+           _lib.sfa_edges_powerlaw(n, r, float(sigma), draws, width, int(seed) & (2**64 - 1),
+                                   _ip(edges), _ip(count)))
+    return edges, count
+
+
+def rope_table(n, head_dim, theta):
+    """Host float32 [n, head_dim/2, 2] (cos, sin) table built in fp64."""
+    out = np.zeros((n, head_dim // 2, 2), dtype=np.float32)
+    _check("sfa_rope_table", _lib.sfa_rope_table(n, head_dim, float(theta), _fp(out)))
+    return out
+
+
+# ------------------------------------------------------------ device calls
+
+def _torch():
+    import torch
+    return torch
+
+
+def rope_table_device(n, head_dim, theta, device="cuda"):
+    """Rotary table copied to the device (None for theta == 0)."""
+    if not theta:
+        return None
+    torch = _torch()
+    return torch.from_numpy(rope_table(n, head_dim, theta)).to(device)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SFA_F32
+    if t.dtype == torch.bfloat16:
+        return SFA_BF16
+    raise TypeError("tensors must be float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _require(t, name, dtype=None, shape=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+class Problem:
+    """Holds an ``sfa_attn`` and the host arrays it points to."""
+
+    def __init__(self, q, k, window=0, lo=None, frac=None, rope=None, scale=0.0):
+        B, n, hq, d = q.shape
+        hkv = k.shape[2]
+        self.lo = np.ascontiguousarray(np.zeros(0) if lo is None else lo, dtype=np.int32)
+        self.frac = np.ascontiguousarray(np.zeros(0) if frac is None else frac, dtype=np.float32)
+        if self.lo.shape != self.frac.shape:
+            raise ValueError("lo and frac must have the same length")
+        if rope is not None:
+            _require(rope, "rope", _torch().float32, (n, d // 2, 2))
+        self.rope = rope
+        self.c = SfaAttn(B, n, hq, hkv, d, _dtype_code(q), int(window), len(self.lo), float(scale), 0,
+                         _ip(self.lo), _fp(self.frac), None if rope is None else rope.data_ptr())
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def fwd(q, k, v, window=0, lo=None, frac=None, rope=None, scale=0.0, want_lse=False, out=None, lse=None):
+    """Forward over the window 0..window plus shared offsets (lo, frac)."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, nm, q.dtype)
+    if k.shape != v.shape:
+        raise ValueError("k and v shapes differ")
+    B, n, hq, d = q.shape
+    pr = Problem(q, k, window, lo, frac, rope, scale)
+    o = torch.empty_like(q) if out is None else out
+    _require(o, "out", q.dtype, q.shape)
+    if want_lse and lse is None:
+        lse = torch.empty((B, hq, n), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, (B, hq, n))
+    _check("sfa_fwd", _lib.sfa_fwd(pr.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(q)))
+    return (o, lse) if (want_lse or lse is not None) else o
+
+
+def fwd_edges(q, k, v, edges, count, rope=None, scale=0.0, want_lse=False, out=None):
+    """Forward over per-query edge lists (device int32 [n, width], [n])."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, nm, q.dtype)
+    B, n, hq, d = q.shape
+    _require(edges, "edges", torch.int32)
+    _require(count, "count", torch.int32, (n,))
+    if edges.dim() != 2 or edges.shape[0] != n:
+        raise ValueError("edges must be [n, width]")
+    pr = Problem(q, k, 0, None, None, rope, scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, hq, n), dtype=torch.float32, device=q.device) if want_lse else None
+    _check("sfa_fwd_edges", _lib.sfa_fwd_edges(pr.ref(), _ptr(edges), _ptr(count), int(edges.shape[1]),
+                                               _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(q)))
+    return (o, lse) if want_lse else o
+
+
+def bwd_workspace_bytes(q, k, window=0, lo=None, frac=None, rope=None, scale=0.0):
+    pr = Problem(q, k, window, lo, frac, rope, scale)
+    nb = _lib.sfa_bwd_workspace_bytes(pr.ref())
+    if nb == 0 and q.numel() > 0:
+        raise SfaError("sfa_bwd_workspace_bytes", SFA_ERR_ARG)
+    return nb
+
+
+def bwd(q, k, v, lse, dout, window=0, lo=None, frac=None, rope=None, scale=0.0,
+        base=None, alpha=None, workspace=None, want_dd=True):
+    """Backward: returns (dq, dk, dv, dd or None, dtheta or None)."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _require(t, nm, q.dtype)
+    B, n, hq, d = q.shape
+    _require(lse, "lse", torch.float32, (B, hq, n))
+    pr = Problem(q, k, window, lo, frac, rope, scale)
+    nb = _lib.sfa_bwd_workspace_bytes(pr.ref())
+    if workspace is None:
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nr = len(pr.lo)
+    dd = torch.empty(max(nr, 1), dtype=torch.float32, device=q.device) if (want_dd and nr) else None
+    dth = None
+    base_arr = None
+    if base is not None and alpha is not None:
+        base_arr = np.ascontiguousarray(base, dtype=np.int32)
+        if len(base_arr) != nr:
+            raise ValueError("base must have one entry per offset")
+        dth = torch.empty(1, dtype=torch.float32, device=q.device)
+    _check("sfa_bwd", _lib.sfa_bwd(
+        pr.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(dd), None if base_arr is None else _ip(base_arr), float(alpha or 0.0), _ptr(dth),
+        _ptr(workspace), workspace.numel(), _stream(q)))
+    return dq, dk, dv, dd, dth
+
+
+# ------------------------------------------------------------ timing
+
+def profile_enable(on=True):
+    _lib.sfa_profile_enable(1 if on else 0)
+
+
+def profile_reset():
+    _lib.sfa_profile_reset()
+
+
+def profile_read(kernel):
+    """(total milliseconds, launches) recorded for the named kernel."""
+    ms, cnt = ctypes.c_double(), ctypes.c_int64()
+    _check("sfa_profile_read", _lib.sfa_profile_read(kernel.encode(), ctypes.byref(ms), ctypes.byref(cnt)))
+    return ms.value, cnt.value

@@ -1,0 +1,265 @@
+// C ABI of the device entry points: validation (complete before any HIP
+// call), slot-table construction, workspace layout, launch and timing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "sfa_internal.h"
+
+namespace sfa {
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int validate_problem(const sfa_attn* a, Problem* p) {
+  if (!a) return fail(SFA_ERR_ARG, "problem is NULL");
+  if (a->batch < 0 || a->seqlen < 0) return fail(SFA_ERR_ARG, "batch and seqlen must be >= 0");
+  if (a->hq < 1 || a->hkv < 1 || a->hq % a->hkv)
+    return fail(SFA_ERR_ARG, "hq must be a positive multiple of hkv");
+  const int G = a->hq / a->hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(SFA_ERR_UNSUPPORTED, "group size hq/hkv = %d not in {1,2,4,8}", G);
+  if (a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64)
+    return fail(SFA_ERR_UNSUPPORTED, "head_dim %d not in {16,32,64}", a->head_dim);
+  if (a->head_dim / G < 2) return fail(SFA_ERR_UNSUPPORTED, "head_dim / group < 2");
+  if (a->dtype != SFA_F32 && a->dtype != SFA_BF16) return fail(SFA_ERR_ARG, "unknown dtype %d", a->dtype);
+  if (a->window < 0) return fail(SFA_ERR_ARG, "window must be >= 0");
+  if (a->n_off < 0 || a->n_off > SFA_MAX_OFFSETS)
+    return fail(SFA_ERR_UNSUPPORTED, "n_off %d not in [0, %d]", a->n_off, SFA_MAX_OFFSETS);
+  if (int64_t(a->window) + 1 + a->n_off > SFA_MAX_SLOTS)
+    return fail(SFA_ERR_UNSUPPORTED, "window + 1 + n_off exceeds %d slots", SFA_MAX_SLOTS);
+  if (a->reserved != 0) return fail(SFA_ERR_ARG, "reserved field must be 0");
+  if (!std::isfinite(a->scale) || a->scale < 0.f) return fail(SFA_ERR_ARG, "scale must be finite and >= 0");
+  if (a->n_off > 0 && (!a->off_lo || !a->off_frac)) return fail(SFA_ERR_ARG, "offset arrays are NULL");
+  for (int k = 0; k < a->n_off; ++k) {
+    if (a->off_lo[k] < 0 || a->off_lo[k] >= (1 << 30)) return fail(SFA_ERR_ARG, "off_lo[%d] out of range", k);
+    const float f = a->off_frac[k];
+    if (!(f >= 0.f && f < 1.f)) return fail(SFA_ERR_ARG, "off_frac[%d] not in [0,1)", k);
+  }
+  if (a->rope && (reinterpret_cast<uintptr_t>(a->rope) & 7u)) return fail(SFA_ERR_ARG, "rope table not 8-byte aligned");
+  const int64_t elems = int64_t(a->batch) * a->seqlen * a->hq * a->head_dim;
+  if (elems >= (int64_t(1) << 40)) return fail(SFA_ERR_UNSUPPORTED, "tensor too large");
+  p->B = a->batch;
+  p->n = a->seqlen;
+  p->hq = a->hq;
+  p->hkv = a->hkv;
+  p->D = a->head_dim;
+  p->G = G;
+  p->dtype = a->dtype;
+  p->window = a->window;
+  p->n_off = a->n_off;
+  p->scale = a->scale > 0.f ? a->scale : float(1.0 / std::sqrt(double(a->head_dim)));
+  p->rope = a->rope;
+  return SFA_OK;
+}
+
+int build_slots(const sfa_attn* a, SlotTable* t) {
+  struct S {
+    int32_t lo;
+    float frac;
+    int16_t rung;
+  };
+  std::vector<S> v;
+  v.reserve(size_t(a->window) + 1 + size_t(a->n_off));
+  for (int s = 0; s <= a->window; ++s) v.push_back({s, 0.f, -1});
+  for (int k = 0; k < a->n_off; ++k) v.push_back({a->off_lo[k], a->off_frac[k], int16_t(k)});
+  std::stable_sort(v.begin(), v.end(), [](const S& x, const S& y) { return x.lo < y.lo; });
+  std::memset(t, 0, sizeof(*t));
+  t->count = int32_t(v.size());
+  t->n_rungs = a->n_off;
+  for (size_t s = 0; s < v.size(); ++s) {
+    t->lo[s] = v[s].lo;
+    t->frac[s] = v[s].frac;
+    t->rung[s] = v[s].rung;
+  }
+  return SFA_OK;
+}
+
+// ----------------------------------------------------------------- timing
+
+namespace {
+struct Pending {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<Pending> g_pending;
+std::map<std::string, std::pair<double, int64_t>> g_totals;
+}  // namespace
+
+ProfileScope::ProfileScope(const char* nm, void* st) : name(nm), stream(st), ev0(nullptr) {
+  if (!g_prof_on) return;
+  hipEvent_t e;
+  if (hipEventCreate(&e) == hipSuccess) {
+    hipEventRecord(e, static_cast<hipStream_t>(stream));
+    ev0 = e;
+  }
+}
+
+ProfileScope::~ProfileScope() {
+  if (!ev0) return;
+  hipEvent_t e;
+  if (hipEventCreate(&e) != hipSuccess) {
+    hipEventDestroy(static_cast<hipEvent_t>(ev0));
+    return;
+  }
+  hipEventRecord(e, static_cast<hipStream_t>(stream));
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_pending.push_back({name, static_cast<hipEvent_t>(ev0), e});
+}
+
+static void drain_pending() {
+  for (auto& p : g_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+      auto& t = g_totals[p.name];
+      t.first += ms;
+      t.second += 1;
+    }
+    hipEventDestroy(p.a);
+    hipEventDestroy(p.b);
+  }
+  g_pending.clear();
+}
+
+static int hip_status(int err, const char* what) {
+  if (err != 0)
+    return fail(SFA_ERR_HIP, "%s: %s", what, hipGetErrorString(static_cast<hipError_t>(err)));
+  return SFA_OK;
+}
+
+}  // namespace sfa
+
+using namespace sfa;
+
+extern "C" int sfa_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return SFA_OK;
+}
+
+extern "C" int sfa_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  drain_pending();
+  g_totals.clear();
+  return SFA_OK;
+}
+
+extern "C" int sfa_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel) return fail(SFA_ERR_ARG, "sfa_profile_read: kernel is NULL");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  drain_pending();
+  auto it = g_totals.find(kernel);
+  if (total_ms) *total_ms = it == g_totals.end() ? 0.0 : it->second.first;
+  if (launches) *launches = it == g_totals.end() ? 0 : it->second.second;
+  return SFA_OK;
+}
+
+// ------------------------------------------------------------ entry points
+
+extern "C" int sfa_fwd(const sfa_attn* a, const void* q, const void* k, const void* v, void* o,
+                       float* lse, void* stream) {
+  clear_error();
+  Problem p;
+  int rc = validate_problem(a, &p);
+  if (rc) return rc;
+  if (p.B == 0 || p.n == 0) return SFA_OK;
+  if (!q || !k || !v || !o) return fail(SFA_ERR_ARG, "sfa_fwd: NULL tensor");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return fail(SFA_ERR_ARG, "sfa_fwd: tensors must be 16-byte aligned");
+  SlotTable t;
+  build_slots(a, &t);
+  ProfileScope ps("fwd_offsets", stream);
+  return hip_status(launch_fwd_offsets(p, t, q, k, v, o, lse, stream), "sfa_fwd launch");
+}
+
+extern "C" int sfa_fwd_edges(const sfa_attn* a, const int32_t* edges, const int32_t* count, int width,
+                             const void* q, const void* k, const void* v, void* o, float* lse,
+                             void* stream) {
+  clear_error();
+  Problem p;
+  if (!a) return fail(SFA_ERR_ARG, "problem is NULL");
+  sfa_attn b = *a;
+  b.window = 0;
+  b.n_off = 0;
+  int rc = validate_problem(&b, &p);
+  if (rc) return rc;
+  if (width < 1 || width > SFA_MAX_EDGE_WIDTH)
+    return fail(SFA_ERR_ARG, "sfa_fwd_edges: width must be in [1, %d]", SFA_MAX_EDGE_WIDTH);
+  if (p.B == 0 || p.n == 0) return SFA_OK;
+  if (!q || !k || !v || !o || !edges || !count) return fail(SFA_ERR_ARG, "sfa_fwd_edges: NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)) ||
+      (reinterpret_cast<uintptr_t>(edges) & 3u) || (reinterpret_cast<uintptr_t>(count) & 3u))
+    return fail(SFA_ERR_ARG, "sfa_fwd_edges: misaligned pointer");
+  ProfileScope ps("fwd_edges", stream);
+  return hip_status(launch_fwd_edges(p, edges, count, width, q, k, v, o, lse, stream),
+                    "sfa_fwd_edges launch");
+}
+
+extern "C" size_t sfa_bwd_workspace_bytes(const sfa_attn* a) {
+  clear_error();
+  Problem p;
+  if (validate_problem(a, &p)) return 0;
+  SlotTable t;
+  build_slots(a, &t);
+  BwdWorkspace ws;
+  return bwd_workspace_layout(p, t, nullptr, &ws);
+}
+
+extern "C" int sfa_bwd(const sfa_attn* a, const void* q, const void* k, const void* v,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dd,
+                       const int32_t* base, double alpha, float* dtheta, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  clear_error();
+  Problem p;
+  int rc = validate_problem(a, &p);
+  if (rc) return rc;
+  if (dtheta) {
+    if (p.n_off > 0 && !base) return fail(SFA_ERR_ARG, "sfa_bwd: dtheta needs the base rungs");
+    if (!std::isfinite(alpha)) return fail(SFA_ERR_ARG, "sfa_bwd: alpha must be finite");
+  }
+  SlotTable t;
+  build_slots(a, &t);
+  BwdWorkspace ws;
+  const size_t need = bwd_workspace_layout(p, t, workspace, &ws);
+  float base_f[SFA_MAX_OFFSETS];
+  for (int i = 0; i < p.n_off; ++i) base_f[i] = base ? float(base[i]) : 0.f;
+  if (p.B == 0 || p.n == 0) {
+    // Nothing to sum: the reduce kernel over zero blocks writes zero dd/dtheta.
+    if (!dd && !dtheta) return SFA_OK;
+    ProfileScope ps("bwd_reduce", stream);
+    return hip_status(launch_bwd_reduce(t, ws, base_f, alpha, dd, dtheta, stream), "sfa_bwd reduce launch");
+  }
+  if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv)
+    return fail(SFA_ERR_ARG, "sfa_bwd: NULL tensor");
+  const void* ptrs[] = {q, k, v, lse, dout, dq, dk, dv};
+  for (const void* x : ptrs)
+    if (!aligned16(x)) return fail(SFA_ERR_ARG, "sfa_bwd: tensors must be 16-byte aligned");
+  if (dd && (reinterpret_cast<uintptr_t>(dd) & 3u)) return fail(SFA_ERR_ARG, "sfa_bwd: dd misaligned");
+  if (dtheta && (reinterpret_cast<uintptr_t>(dtheta) & 3u))
+    return fail(SFA_ERR_ARG, "sfa_bwd: dtheta misaligned");
+  if (!workspace || ws_bytes < need || !aligned16(workspace))
+    return fail(SFA_ERR_CAPACITY, "sfa_bwd: workspace needs %zu bytes (16-byte aligned), got %zu", need,
+                ws_bytes);
+  {
+    ProfileScope ps("bwd_query", stream);
+    rc = hip_status(launch_bwd_query(p, t, q, k, v, lse, dout, dq, ws, stream), "sfa_bwd query launch");
+    if (rc) return rc;
+  }
+  {
+    ProfileScope ps("bwd_key", stream);
+    rc = hip_status(launch_bwd_key(p, t, q, k, v, dout, dk, dv, ws, stream), "sfa_bwd key launch");
+    if (rc) return rc;
+  }
+  if (dd || dtheta) {
+    ProfileScope ps("bwd_reduce", stream);
+    rc = hip_status(launch_bwd_reduce(t, ws, base_f, alpha, dd, dtheta, stream), "sfa_bwd reduce launch");
+  }
+  return rc;
+}

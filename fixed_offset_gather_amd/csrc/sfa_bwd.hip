@@ -1,0 +1,489 @@
+// Backward kernels of libsfa (gfx950) for L = <O, dO> of the window plus
+// shared-offset forward ("Depth-Staggered Fibonacci Spacing for Sparse
+// Attention", gather paragraph: the interpolation between the floor and
+// floor-plus-one rows keeps a gradient to the offset distance, hence to
+// alpha and theta through the alpha parameterisation).
+//
+// Three launches on one stream, no atomics, fixed summation order:
+//
+// bwd_query (query-centric, same staging as the forward): recomputes each
+//   logit, p = exp(logit - lse) and dp = dO.v~ in one pass over the slots.
+//   Dvec = rowsum(dO*O) is formed exactly as sum_slots p dp (not from the
+//   rounded forward output), and dq~ = scale sum p (dp - Dvec) k~ is
+//   accumulated as scale (sum p dp k~ - Dvec sum p k~), then rotated back to
+//   dQ.  p, dp and Dvec of every valid (query, slot, head) go to the
+//   workspace.
+// bwd_key (key-centric transpose gather): key j receives from query j+lo
+//   (weight 1-frac) and j+lo+1 (weight frac) of every slot; those queries
+//   form contiguous ranges, so each lane gathers instead of scattering.
+//   dK uses the relative rotation R(j)^T R(i) = R(i-j) with i-j fixed per
+//   (slot, tap), so unrotated Q rows are combined first and rotated once.
+//   It also sums the per-block partials of dL/dd_k.
+// bwd_reduce: sums the dd partials in block order; dalpha = sum f_k dd_k;
+//   dtheta = (alpha - 1/2)(3/2 - alpha) dalpha.
+#include "sfa_device.h"
+#include "sfa_internal.h"
+
+namespace sfa {
+
+namespace {
+
+constexpr int BQ = 64;  // queries (bwd_query) or keys (bwd_key) per workgroup
+constexpr int kCap = 128;
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* P;
+  float* dP;
+  float* Dvec;
+  float* dd_part;
+  const float* rope;
+  int n, hq, hkv, nblk, tiles, S, n_rungs;
+  float scale, scale_log2;
+};
+
+template <int G, int LPQ>
+struct Bc {
+  template <int H = 0>
+  static __device__ __forceinline__ void run(float x, float (&out)[G]) {
+    if constexpr (H < G) {
+      out[H] = group_bcast<LPQ, H>(x);
+      run<H + 1>(x, out);
+    }
+  }
+};
+
+template <int G, int LPQ, int DC>
+__device__ __forceinline__ float own_dot(const float (&a)[G][DC], const float (&b)[DC], int own) {
+  float part[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < DC; ++x) acc = fmaf(a[h][x], b[x], acc);
+    part[h] = group_sum<LPQ>(acc);
+  }
+  float mine = part[0];
+#pragma unroll
+  for (int h = 1; h < G; ++h) mine = (own == h) ? part[h] : mine;
+  return mine;
+}
+
+template <typename T, int D, int G, int LPQ, int CAP>
+__global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable st) {
+  constexpr int DC = D / LPQ;
+  constexpr int KS = D + 4;
+  constexpr int E = 16 / sizeof(T);
+  constexpr int CPR = D / E;
+  constexpr int NT = BQ * LPQ;
+  __shared__ __align__(16) float Ks[CAP * KS];
+  __shared__ __align__(16) float Vs[CAP * KS];
+
+  const int tid = threadIdx.x;
+  const int qq = tid / LPQ;
+  const int c = tid % LPQ;
+  const int own = c % G;
+  const int tile = xcd_tile(blockIdx.x, a.tiles);
+  const int seq = tile / a.nblk;
+  const int blk = a.nblk - 1 - tile % a.nblk;
+  const int b = seq / a.hkv, g = seq % a.hkv;
+  const int n = a.n;
+  const int i0 = blk * BQ;
+  const int i = i0 + qq;
+  const bool active = i < n;
+  const int i_last = min(i0 + BQ, n) - 1;
+
+  const T* __restrict__ Q = static_cast<const T*>(a.q);
+  const T* __restrict__ K = static_cast<const T*>(a.k);
+  const T* __restrict__ V = static_cast<const T*>(a.v);
+  const T* __restrict__ dO = static_cast<const T*>(a.dout);
+
+  // acc_pd = sum p dp k~, acc_p = sum p k~ ; dq~ = scale (acc_pd - Dvec acc_p)
+  float qv[G][DC], dov[G][DC], acc_pd[G][DC], acc_p[G][DC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (active) {
+      const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC;
+      load_vec<DC>(Q + off, qv[h]);
+      if (a.rope) rotate_pairs<DC, 1>(qv[h], a.rope + size_t(i) * D, c * DC);
+      load_vec<DC>(dO + off, dov[h]);
+    } else {
+#pragma unroll
+      for (int x = 0; x < DC; ++x) qv[h][x] = dov[h][x] = 0.f;
+    }
+#pragma unroll
+    for (int x = 0; x < DC; ++x) acc_pd[h][x] = acc_p[h][x] = 0.f;
+  }
+  const float lse2 = active ? a.lse[(size_t(b) * a.hq + size_t(g) * G + own) * n + i] * kLog2e : 0.f;
+  float dvec = 0.f;  // rowsum(dO * O) of the own head, as sum_slots p dp
+
+  const size_t kv_row = size_t(a.hkv) * D;
+  const T* Kseq = K + size_t(b) * n * kv_row + size_t(g) * D;
+  const T* Vseq = V + size_t(b) * n * kv_row + size_t(g) * D;
+  const size_t ws_seq = size_t(seq) * a.S;
+
+  int s = 0;
+  const int S = st.count;
+  while (s < S) {
+    const int lo0 = st.lo[s];
+    if (lo0 > i_last) break;
+    int lomax = lo0 + (st.frac[s] > 0.f ? 1 : 0);
+    int e = s + 1;
+    while (e < S) {
+      const int le = st.lo[e];
+      if (le > i_last) break;
+      const int need = max(lomax, le + (st.frac[e] > 0.f ? 1 : 0));
+      if (need - lo0 + BQ > CAP) break;
+      lomax = need;
+      ++e;
+    }
+    const int r0 = i0 - lomax;
+    const int nrows = lomax - lo0 + BQ;
+
+    __syncthreads();
+    for (int t = tid; t < nrows * CPR; t += NT) {
+      const int row = t / CPR, cc = t % CPR;
+      const int pos = r0 + row;
+      float kf[E], vf[E];
+      if (pos >= 0 && pos < n) {
+        load_vec<E>(Kseq + size_t(pos) * kv_row + cc * E, kf);
+        load_vec<E>(Vseq + size_t(pos) * kv_row + cc * E, vf);
+        if (a.rope) rotate_pairs<E, 1>(kf, a.rope + size_t(pos) * D, cc * E);
+      } else {
+#pragma unroll
+        for (int x = 0; x < E; ++x) kf[x] = vf[x] = 0.f;
+      }
+      store_vec<E>(Ks + row * KS + cc * E, kf);
+      store_vec<E>(Vs + row * KS + cc * E, vf);
+    }
+    __syncthreads();
+
+    for (int sj = s; sj < e; ++sj) {
+      const int lo = st.lo[sj];
+      const float w = st.frac[sj];
+      const int r = i - lo - r0;
+      float kt[DC], vt[DC];
+      load_vec<DC>(Ks + r * KS + c * DC, kt);
+      load_vec<DC>(Vs + r * KS + c * DC, vt);
+      if (w != 0.f) {
+        float kb[DC], vb[DC];
+        load_vec<DC>(Ks + (r - 1) * KS + c * DC, kb);
+        load_vec<DC>(Vs + (r - 1) * KS + c * DC, vb);
+#pragma unroll
+        for (int x = 0; x < DC; ++x) {
+          kt[x] = fmaf(w, kb[x] - kt[x], kt[x]);
+          vt[x] = fmaf(w, vb[x] - vt[x], vt[x]);
+        }
+      }
+      const float sdot = own_dot<G, LPQ, DC>(qv, kt, own);
+      const float dp = own_dot<G, LPQ, DC>(dov, vt, own);
+      const int rel = i - lo;
+      const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f));
+      const float p = valid ? exp2f(sdot * a.scale_log2 - lse2) : 0.f;
+      const float pdp = p * dp;
+      dvec += pdp;
+      if (valid && c < G) {
+        const size_t widx = ((ws_seq + sj) * n + i) * G + c;
+        a.P[widx] = p;
+        a.dP[widx] = dp;
+      }
+      float ph[G], pdh[G];
+      Bc<G, LPQ>::run(p, ph);
+      Bc<G, LPQ>::run(pdp, pdh);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int x = 0; x < DC; ++x) {
+          acc_pd[h][x] = fmaf(pdh[h], kt[x], acc_pd[h][x]);
+          acc_p[h][x] = fmaf(ph[h], kt[x], acc_p[h][x]);
+        }
+    }
+    s = e;
+  }
+
+  if (active && c < G) a.Dvec[(size_t(seq) * n + i) * G + c] = dvec;
+  float dvh[G];
+  Bc<G, LPQ>::run(dvec, dvh);
+  if (active) {
+    T* dQ = static_cast<T*>(a.dq);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float dq[DC];
+#pragma unroll
+      for (int x = 0; x < DC; ++x) dq[x] = a.scale * fmaf(-dvh[h], acc_p[h][x], acc_pd[h][x]);
+      if (a.rope) rotate_pairs<DC, -1>(dq, a.rope + size_t(i) * D, c * DC);
+      store_vec<DC>(dQ + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, dq);
+    }
+  }
+}
+
+// Key-centric pass.  For key j and slot s (row pair i-lo, i-lo-1 of query
+// i): tap 0 is query j+lo (weight 1-frac), tap 1 is query j+lo+1 (weight
+// frac).  dS = scale p (dp - Dvec) is formed here from the stored p, dp and
+// Dvec.  The offset gradient dd_k = sum_i dK~.(Kr[i-lo-1] - Kr[i-lo]) +
+// dV~.(V[i-lo-1] - V[i-lo]) is gathered per key as well: key j meets each
+// rung once as the farther row (tap 1, sign +) and once as the nearer row
+// (tap 0, sign -), both taps taken even when frac = 0.
+template <typename T, int D, int G, int LPQ>
+__global__ __launch_bounds__(BQ* LPQ) void bwd_key_kernel(BwdArgs a, SlotTable st) {
+  constexpr int DC = D / LPQ;
+  constexpr int NT = BQ * LPQ;
+  constexpr int NW = NT / 64;
+  __shared__ float ddl[NW][SFA_MAX_OFFSETS];
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int kk = tid / LPQ;
+  const int c = tid % LPQ;
+  const int tile = xcd_tile(blockIdx.x, a.tiles);
+  const int seq = tile / a.nblk;
+  const int blk = tile % a.nblk;
+  const int b = seq / a.hkv, g = seq % a.hkv;
+  const int n = a.n;
+  const int j0 = blk * BQ;
+  const int j = j0 + kk;
+  const bool activej = j < n;
+
+  for (int t = tid; t < NW * SFA_MAX_OFFSETS; t += NT) (&ddl[0][0])[t] = 0.f;
+  __syncthreads();
+
+  const T* __restrict__ Q = static_cast<const T*>(a.q);
+  const T* __restrict__ dO = static_cast<const T*>(a.dout);
+  const size_t ws_seq = size_t(seq) * a.S;
+  const size_t kv_off = (size_t(b) * n + j) * size_t(a.hkv) * D + size_t(g) * D + c * DC;
+
+  float kj[DC], vj[DC];  // this key's own rows (unrotated K, V), for dd
+  if (activej) {
+    load_vec<DC>(static_cast<const T*>(a.k) + kv_off, kj);
+    load_vec<DC>(static_cast<const T*>(a.v) + kv_off, vj);
+  } else {
+#pragma unroll
+    for (int x = 0; x < DC; ++x) kj[x] = vj[x] = 0.f;
+  }
+
+  float dk[DC], dv[DC];
+#pragma unroll
+  for (int x = 0; x < DC; ++x) dk[x] = dv[x] = 0.f;
+
+  const int S = st.count;
+  for (int sj = 0; sj < S; ++sj) {
+    const int lo = st.lo[sj];
+    if (j0 + lo > n - 1) break;  // no query at this distance for any key of the block
+    const float w = st.frac[sj];
+    const int rung = st.rung[sj];
+    const int taps = (w > 0.f || rung >= 0) ? 2 : 1;
+    for (int tap = 0; tap < taps; ++tap) {
+      const int delta = lo + tap;
+      const float wt = tap ? w : 1.f - w;
+      const int i = j + delta;
+      const bool valid = activej && i < n && (tap == 1 || j > 0 || w == 0.f);
+      float yk[DC], yv[DC];
+#pragma unroll
+      for (int x = 0; x < DC; ++x) yk[x] = yv[x] = 0.f;
+      if (valid) {
+        const size_t widx = ((ws_seq + sj) * n + i) * G;
+        float pg[G], dpg[G], dvg[G];
+        load_vec<G>(a.P + widx, pg);
+        load_vec<G>(a.dP + widx, dpg);
+        load_vec<G>(a.Dvec + (size_t(seq) * n + i) * G, dvg);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float dsh = a.scale * pg[h] * (dpg[h] - dvg[h]);
+          const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC;
+          float qh[DC], oh[DC];
+          load_vec<DC>(Q + off, qh);
+          load_vec<DC>(dO + off, oh);
+#pragma unroll
+          for (int x = 0; x < DC; ++x) {
+            yk[x] = fmaf(dsh, qh[x], yk[x]);
+            yv[x] = fmaf(pg[h], oh[x], yv[x]);
+          }
+        }
+        if (a.rope) rotate_pairs<DC, 1>(yk, a.rope + size_t(delta) * D, c * DC);
+#pragma unroll
+        for (int x = 0; x < DC; ++x) {
+          dk[x] = fmaf(wt, yk[x], dk[x]);
+          dv[x] = fmaf(wt, yv[x], dv[x]);
+        }
+      }
+      if (rung >= 0) {
+        float part = 0.f;
+#pragma unroll
+        for (int x = 0; x < DC; ++x) part = fmaf(yk[x], kj[x], fmaf(yv[x], vj[x], part));
+        const float tot = wave_sum(tap ? part : -part);
+        if ((tid & 63) == 0) ddl[wave][rung] += tot;
+      }
+    }
+  }
+  if (activej) {
+    store_vec<DC>(static_cast<T*>(a.dk) + kv_off, dk);
+    store_vec<DC>(static_cast<T*>(a.dv) + kv_off, dv);
+  }
+  __syncthreads();
+  for (int r = tid; r < a.n_rungs; r += NT) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc += ddl[w][r];
+    a.dd_part[size_t(tile) * a.n_rungs + r] = acc;
+  }
+}
+
+struct ReduceArgs {
+  const float* dd_part;
+  float* dd;
+  float* dtheta;
+  int blocks, n_rungs;
+  double alpha;
+  float base[SFA_MAX_OFFSETS];
+};
+
+__global__ __launch_bounds__(SFA_MAX_OFFSETS) void bwd_reduce_kernel(ReduceArgs a) {
+  __shared__ double sdd[SFA_MAX_OFFSETS];
+  const int k = threadIdx.x;
+  if (k < a.n_rungs) {
+    double acc = 0.0;
+    for (int t = 0; t < a.blocks; ++t) acc += double(a.dd_part[size_t(t) * a.n_rungs + k]);
+    sdd[k] = acc;
+    if (a.dd) a.dd[k] = float(acc);
+  }
+  __syncthreads();
+  if (k == 0 && a.dtheta) {
+    double da = 0.0;
+    for (int r = 0; r < a.n_rungs; ++r) da += double(a.base[r]) * sdd[r];
+    a.dtheta[0] = float((a.alpha - 0.5) * (1.5 - a.alpha) * da);
+  }
+}
+
+// Lanes per query in bwd_query: at least two per head of the group and at
+// most 8 dims per lane (four G x DC register tiles live across the loop),
+// never fewer than 2 dims (rotation pairs) or more than 16 lanes.
+template <int D, int G>
+constexpr int bwd_lpq() {
+  constexpr int a = 2 * G > D / 8 ? 2 * G : D / 8;
+  constexpr int b = a < D / 2 ? a : D / 2;
+  return b < 16 ? b : 16;
+}
+
+// Lanes per key in bwd_key: 16 dims each (the lane sums over all G heads).
+template <int D>
+constexpr int key_lpk() {
+  return D >= 16 ? D / 16 : 1;
+}
+
+BwdArgs make_args(const Problem& p, const SlotTable& t, const BwdWorkspace& ws) {
+  BwdArgs a{};
+  a.P = ws.p;
+  a.dP = ws.dp;
+  a.Dvec = ws.dvec;
+  a.dd_part = ws.dd_part;
+  a.rope = p.rope;
+  a.n = p.n;
+  a.hq = p.hq;
+  a.hkv = p.hkv;
+  a.nblk = (p.n + BQ - 1) / BQ;
+  a.tiles = a.nblk * p.B * p.hkv;
+  a.S = t.count;
+  a.n_rungs = t.n_rungs;
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * kLog2e;
+  return a;
+}
+
+template <typename T, int D, int G>
+int launch_query_t(const BwdArgs& a, const SlotTable& t, hipStream_t st) {
+  constexpr int LPQ = bwd_lpq<D, G>();
+  hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, kCap>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+  return int(hipGetLastError());
+}
+
+template <typename T, int D, int G>
+int launch_key_t(const BwdArgs& a, const SlotTable& t, hipStream_t st) {
+  constexpr int LPQ = key_lpk<D>();
+  hipLaunchKernelGGL((bwd_key_kernel<T, D, G, LPQ>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+  return int(hipGetLastError());
+}
+
+#define SFA_DISPATCH_G(T, D_, FN, g_, ...)         \
+  do {                                             \
+    if (g_ == 1) return FN<T, D_, 1>(__VA_ARGS__); \
+    if (g_ == 2) return FN<T, D_, 2>(__VA_ARGS__); \
+    if (g_ == 4) return FN<T, D_, 4>(__VA_ARGS__); \
+    return FN<T, D_, 8>(__VA_ARGS__);              \
+  } while (0)
+#define SFA_DISPATCH_D(T, FN, d_, g_, ...)                       \
+  do {                                                           \
+    if (d_ == 64) SFA_DISPATCH_G(T, 64, FN, g_, __VA_ARGS__);    \
+    else if (d_ == 32) SFA_DISPATCH_G(T, 32, FN, g_, __VA_ARGS__); \
+    else SFA_DISPATCH_G(T, 16, FN, g_, __VA_ARGS__);             \
+  } while (0)
+#define SFA_DISPATCH(FN, P, ...)                                 \
+  do {                                                           \
+    if ((P).dtype == SFA_BF16) SFA_DISPATCH_D(bf16_t, FN, (P).D, (P).G, __VA_ARGS__); \
+    else SFA_DISPATCH_D(float, FN, (P).D, (P).G, __VA_ARGS__);   \
+  } while (0)
+
+}  // namespace
+
+size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, BwdWorkspace* ws) {
+  const int nblk = (p.n + BQ - 1) / BQ;
+  auto al = [](size_t e) { return (e + 63) & ~size_t(63); };  // 256-byte aligned sections
+  const size_t pe = al(size_t(p.B) * p.hkv * t.count * size_t(p.n) * p.G);  // floats per array
+  const size_t de = al(size_t(p.B) * p.hkv * size_t(p.n) * p.G);
+  ws->blocks = nblk * p.B * p.hkv;
+  const size_t dd_e = size_t(ws->blocks) * (t.n_rungs > 0 ? t.n_rungs : 1);
+  float* f = static_cast<float*>(base);
+  ws->p = f;
+  ws->dp = f ? f + pe : nullptr;
+  ws->dvec = f ? f + 2 * pe : nullptr;
+  ws->dd_part = f ? f + 2 * pe + de : nullptr;
+  ws->bytes = (2 * pe + de + dd_e) * sizeof(float);
+  return ws->bytes;
+}
+
+int launch_bwd_query(const Problem& p, const SlotTable& t, const void* q, const void* k, const void* v,
+                     const float* lse, const void* dout, void* dq, const BwdWorkspace& ws, void* stream) {
+  BwdArgs a = make_args(p, t, ws);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  SFA_DISPATCH(launch_query_t, p, a, t, st);
+}
+
+int launch_bwd_key(const Problem& p, const SlotTable& t, const void* q, const void* k, const void* v,
+                   const void* dout, void* dk, void* dv, const BwdWorkspace& ws, void* stream) {
+  BwdArgs a = make_args(p, t, ws);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.dk = dk;
+  a.dv = dv;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  SFA_DISPATCH(launch_key_t, p, a, t, st);
+}
+
+int launch_bwd_reduce(const SlotTable& t, const BwdWorkspace& ws, const float* base_f, double alpha, float* dd,
+                      float* dtheta, void* stream) {
+  ReduceArgs a{};
+  a.dd_part = ws.dd_part;
+  a.dd = dd;
+  a.dtheta = dtheta;
+  a.blocks = ws.blocks;
+  a.n_rungs = t.n_rungs;
+  a.alpha = alpha;
+  for (int k = 0; k < t.n_rungs; ++k) a.base[k] = base_f[k];
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(1), dim3(SFA_MAX_OFFSETS), 0, static_cast<hipStream_t>(stream), a);
+  return int(hipGetLastError());
+}
+
+}  // namespace sfa

@@ -1,0 +1,210 @@
+// Device-side helpers for the gfx950 kernels of libsfa: bf16 conversion,
+// vector loads/stores into float registers, cross-lane group reductions on
+// 64-wide wavefronts (DPP where the group fits in a 16-lane row), rotary
+// rotation of interleaved pairs and the XCD-aware tile order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace sfa {
+
+typedef uint16_t bf16_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNumXcd = 8;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+// bfloat16 is the upper half of an IEEE float.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bfloat16 bits, round to nearest even, NaN kept quiet.
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ---------------------------------------------------------------- loads
+
+// N consecutive elements of T at p (N * sizeof(T) bytes, naturally aligned
+// to the widest vector used) widened to float.
+template <int N>
+__device__ __forceinline__ void load_vec(const float* __restrict__ p, float (&out)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(p + x);
+      out[x] = t.x; out[x + 1] = t.y; out[x + 2] = t.z; out[x + 3] = t.w;
+    }
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 2) {
+      const float2 t = *reinterpret_cast<const float2*>(p + x);
+      out[x] = t.x; out[x + 1] = t.y;
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < N; ++x) out[x] = p[x];
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void load_vec(const bf16_t* __restrict__ p, float (&out)[N]) {
+  if constexpr (N % 8 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 8) {
+      const uint4 t = *reinterpret_cast<const uint4*>(p + x);
+      out[x] = bf16_lo(t.x); out[x + 1] = bf16_hi(t.x);
+      out[x + 2] = bf16_lo(t.y); out[x + 3] = bf16_hi(t.y);
+      out[x + 4] = bf16_lo(t.z); out[x + 5] = bf16_hi(t.z);
+      out[x + 6] = bf16_lo(t.w); out[x + 7] = bf16_hi(t.w);
+    }
+  } else if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 4) {
+      const uint2 t = *reinterpret_cast<const uint2*>(p + x);
+      out[x] = bf16_lo(t.x); out[x + 1] = bf16_hi(t.x);
+      out[x + 2] = bf16_lo(t.y); out[x + 3] = bf16_hi(t.y);
+    }
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 2) {
+      const uint32_t t = *reinterpret_cast<const uint32_t*>(p + x);
+      out[x] = bf16_lo(t); out[x + 1] = bf16_hi(t);
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < N; ++x) out[x] = __uint_as_float(uint32_t(p[x]) << 16);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void store_vec(float* __restrict__ p, const float (&in)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 4)
+      *reinterpret_cast<float4*>(p + x) = make_float4(in[x], in[x + 1], in[x + 2], in[x + 3]);
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 2) *reinterpret_cast<float2*>(p + x) = make_float2(in[x], in[x + 1]);
+  } else {
+#pragma unroll
+    for (int x = 0; x < N; ++x) p[x] = in[x];
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void store_vec(bf16_t* __restrict__ p, const float (&in)[N]) {
+  if constexpr (N % 8 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 8) {
+      uint4 t;
+      t.x = f2bf(in[x]) | (f2bf(in[x + 1]) << 16);
+      t.y = f2bf(in[x + 2]) | (f2bf(in[x + 3]) << 16);
+      t.z = f2bf(in[x + 4]) | (f2bf(in[x + 5]) << 16);
+      t.w = f2bf(in[x + 6]) | (f2bf(in[x + 7]) << 16);
+      *reinterpret_cast<uint4*>(p + x) = t;
+    }
+  } else if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 4) {
+      uint2 t;
+      t.x = f2bf(in[x]) | (f2bf(in[x + 1]) << 16);
+      t.y = f2bf(in[x + 2]) | (f2bf(in[x + 3]) << 16);
+      *reinterpret_cast<uint2*>(p + x) = t;
+    }
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 2)
+      *reinterpret_cast<uint32_t*>(p + x) = f2bf(in[x]) | (f2bf(in[x + 1]) << 16);
+  } else {
+#pragma unroll
+    for (int x = 0; x < N; ++x) p[x] = bf16_t(f2bf(in[x]));
+  }
+}
+
+// ------------------------------------------------------------- rotation
+
+// Rotate the interleaved pairs of x (dims d0 .. d0+N-1 of a head, d0 even)
+// by the angles of table row `row` ([pos][D/2][cos, sin]).  sign = +1
+// rotates forward (R), -1 applies the transpose (R^T).
+template <int N, int SIGN>
+__device__ __forceinline__ void rotate_pairs(float (&x)[N], const float* __restrict__ row, int d0) {
+  static_assert(N % 2 == 0, "pairs");
+  const float* t = row + d0;  // pair p = d0/2 + j sits at floats d0 + 2j
+  float cs[N];
+  load_vec<N>(t, cs);
+#pragma unroll
+  for (int j = 0; j < N; j += 2) {
+    const float c = cs[j], s = SIGN > 0 ? cs[j + 1] : -cs[j + 1];
+    const float a = x[j], b = x[j + 1];
+    x[j] = a * c - b * s;
+    x[j + 1] = a * s + b * c;
+  }
+}
+
+// ------------------------------------------------------- lane exchange
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+
+// Sum over aligned groups of L lanes; every lane of the group gets the sum.
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (L >= 2) x += dpp<quad_perm(1, 0, 3, 2)>(x);
+  if constexpr (L >= 4) x += dpp<quad_perm(2, 3, 0, 1)>(x);
+  if constexpr (L >= 8) x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (L >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (L >= 32) x += __shfl_xor(x, 16);
+  if constexpr (L >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Value of lane H of the caller's aligned group of L lanes.
+template <int L, int H>
+__device__ __forceinline__ float group_bcast(float x) {
+  static_assert(H < L, "lane in group");
+  if constexpr (L == 1) {
+    return x;
+  } else if constexpr (L == 2) {
+    return dpp<quad_perm(H, H, 2 + H, 2 + H)>(x);
+  } else if constexpr (L == 4) {
+    return dpp<quad_perm(H, H, H, H)>(x);
+  } else {
+    const int lane = __lane_id();
+    return __shfl(x, (lane & ~(L - 1)) + H);
+  }
+}
+
+// Sum over the whole 64-lane wavefront (result valid in every lane).
+__device__ __forceinline__ float wave_sum(float x) {
+  x = group_sum<16>(x);
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// ------------------------------------------------------------ tile order
+
+// Workgroups are dispatched round-robin over the XCDs.  Give each XCD a
+// contiguous range of tiles so that the query blocks of one sequence (which
+// read the same K/V rows) share one L2.
+__device__ __forceinline__ int xcd_tile(int id, int total) {
+  if (total % kNumXcd) return id;
+  const int per = total / kNumXcd;
+  return (id % kNumXcd) * per + id / kNumXcd;
+}
+
+}  // namespace sfa

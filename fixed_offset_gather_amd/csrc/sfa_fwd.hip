@@ -1,0 +1,484 @@
+// Forward kernels of libsfa (gfx950).
+//
+// fwd_offsets: causal attention over the window 0..W plus offsets shared by
+// every query ("Depth-Staggered Fibonacci Spacing for Sparse Attention",
+// key-set definition and gather paragraph; "Christoffel-Balanced Sparse
+// Attention", pseudocode, with offsets as backward distances).  Because the
+// offsets are shared, slot s of the BQ consecutive queries [i0, i0+BQ) reads
+// the contiguous rows [i0-lo_s-1, i0+BQ-1-lo_s].  Slots are sorted by lo and
+// grouped into stages whose row ranges fit CAP rows; each stage is staged
+// once into LDS (K rotated to fp32 at its true position, V widened to fp32)
+// with coalesced 16-byte loads and then serves every slot of the stage for
+// all query heads of the KV group.
+//
+// Work split: one workgroup per (sequence, kv head, query block); LPQ lanes
+// per query, each holding DC = D/LPQ dims of all G query heads of the group,
+// so one LDS read of a key/value element feeds G FMAs.  Logits are reduced
+// across the LPQ lanes with DPP; lane c owns the softmax state of head
+// c % G; probabilities and rescale factors are broadcast back with DPP.
+// Online softmax in the log2 domain over chunks of SC slots.
+//
+// fwd_edges: attention over per-query edge lists ("Critical power-law
+// sparse attention", item 2): rows are arbitrary, so keys are read straight
+// from global memory (L2-resident) with the same lane layout.
+#include "sfa_device.h"
+#include "sfa_internal.h"
+
+namespace sfa {
+
+constexpr int BQ = 64;   // queries per workgroup
+constexpr int SC = 8;    // slots per online-softmax chunk
+constexpr int ESC = 4;   // edges per chunk (keys come from global memory)
+
+template <int D>
+struct RowPad {
+  static constexpr int value = D + 4;  // floats per LDS row (16-byte pad)
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* rope;
+  int n, hq, hkv, nblk, tiles;
+  float scale_log2;  // scale * log2(e)
+};
+
+// Logit of lane's own head for one key chunk; `own` selects head c % G.
+template <int G, int LPQ, int DC>
+__device__ __forceinline__ float own_logit(const float (&qv)[G][DC], const float (&kt)[DC], int own) {
+  float part[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < DC; ++x) acc = fmaf(qv[h][x], kt[x], acc);
+    part[h] = group_sum<LPQ>(acc);
+  }
+  float mine = part[0];
+#pragma unroll
+  for (int h = 1; h < G; ++h) mine = (own == h) ? part[h] : mine;
+  return mine;
+}
+
+template <int G, int LPQ>
+struct Bcast {
+  template <int H = 0>
+  static __device__ __forceinline__ void run(float x, float (&out)[G]) {
+    if constexpr (H < G) {
+      out[H] = group_bcast<LPQ, H>(x);
+      run<H + 1>(x, out);
+    }
+  }
+};
+
+template <typename T, int D, int G, int LPQ, int CAP>
+__global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTable st) {
+  constexpr int DC = D / LPQ;
+  constexpr int KS = RowPad<D>::value;
+  constexpr int E = 16 / sizeof(T);       // elements per 16-byte global chunk
+  constexpr int CPR = D / E;              // chunks per row
+  constexpr int NT = BQ * LPQ;
+  static_assert(DC >= 2 && DC % 2 == 0, "lane chunk");
+  __shared__ __align__(16) float Ks[CAP * KS];
+  __shared__ __align__(16) float Vs[CAP * KS];
+
+  const int tid = threadIdx.x;
+  const int qq = tid / LPQ;
+  const int c = tid % LPQ;
+  const int own = c % G;
+  const int tile = xcd_tile(blockIdx.x, a.tiles);
+  const int seq = tile / a.nblk;
+  const int blk = a.nblk - 1 - tile % a.nblk;  // longest blocks first
+  const int b = seq / a.hkv, g = seq % a.hkv;
+  const int n = a.n;
+  const int i0 = blk * BQ;
+  const int i = i0 + qq;
+  const bool active = i < n;
+  const int i_last = min(i0 + BQ, n) - 1;
+
+  const T* __restrict__ Q = static_cast<const T*>(a.q);
+  const T* __restrict__ K = static_cast<const T*>(a.k);
+  const T* __restrict__ V = static_cast<const T*>(a.v);
+
+  // Rotated query chunk of every head in the group.
+  float qv[G][DC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (active) {
+      const T* src = Q + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC;
+      load_vec<DC>(src, qv[h]);
+      if (a.rope) rotate_pairs<DC, 1>(qv[h], a.rope + size_t(i) * D, c * DC);
+    } else {
+#pragma unroll
+      for (int x = 0; x < DC; ++x) qv[h][x] = 0.f;
+    }
+  }
+
+  float o[G][DC];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int x = 0; x < DC; ++x) o[h][x] = 0.f;
+  float m = neg_inf(), l = 0.f;
+
+  const size_t kv_row = size_t(a.hkv) * D;                  // elements between rows
+  const T* Kseq = K + size_t(b) * n * kv_row + size_t(g) * D;
+  const T* Vseq = V + size_t(b) * n * kv_row + size_t(g) * D;
+
+  int s = 0;
+  const int S = st.count;
+  while (s < S) {
+    const int lo0 = st.lo[s];
+    if (lo0 > i_last) break;  // this slot and all later ones are masked for the block
+    int lomax = lo0 + (st.frac[s] > 0.f ? 1 : 0);
+    int e = s + 1;
+    while (e < S) {
+      const int le = st.lo[e];
+      if (le > i_last) break;
+      const int need = max(lomax, le + (st.frac[e] > 0.f ? 1 : 0));
+      if (need - lo0 + BQ > CAP) break;
+      lomax = need;
+      ++e;
+    }
+    const int r0 = i0 - lomax;          // absolute position of LDS row 0
+    const int nrows = lomax - lo0 + BQ;
+
+    __syncthreads();  // the previous stage is fully consumed
+    for (int t = tid; t < nrows * CPR; t += NT) {
+      const int row = t / CPR, cc = t % CPR;
+      const int pos = r0 + row;
+      float kf[E], vf[E];
+      if (pos >= 0 && pos < n) {
+        load_vec<E>(Kseq + size_t(pos) * kv_row + cc * E, kf);
+        load_vec<E>(Vseq + size_t(pos) * kv_row + cc * E, vf);
+        if (a.rope) rotate_pairs<E, 1>(kf, a.rope + size_t(pos) * D, cc * E);
+      } else {
+#pragma unroll
+        for (int x = 0; x < E; ++x) kf[x] = vf[x] = 0.f;
+      }
+      store_vec<E>(Ks + row * KS + cc * E, kf);
+      store_vec<E>(Vs + row * KS + cc * E, vf);
+    }
+    __syncthreads();
+
+    for (int s0 = s; s0 < e; s0 += SC) {
+      float sl[SC];
+#pragma unroll
+      for (int j = 0; j < SC; ++j) {
+        sl[j] = neg_inf();
+        const int sj = s0 + j;
+        if (sj < e) {
+          const int lo = st.lo[sj];
+          const float w = st.frac[sj];
+          const int r = i - lo - r0;  // in [0, nrows) for every lane of the block
+          float kt[DC];
+          load_vec<DC>(Ks + r * KS + c * DC, kt);
+          if (w != 0.f) {
+            float kb[DC];
+            load_vec<DC>(Ks + (r - 1) * KS + c * DC, kb);
+#pragma unroll
+            for (int x = 0; x < DC; ++x) kt[x] = fmaf(w, kb[x] - kt[x], kt[x]);
+          }
+          const float mine = own_logit<G, LPQ, DC>(qv, kt, own);
+          const int rel = i - lo;
+          const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f));
+          sl[j] = valid ? mine * a.scale_log2 : neg_inf();
+        }
+      }
+      float mx = m;
+#pragma unroll
+      for (int j = 0; j < SC; ++j) mx = fmaxf(mx, sl[j]);
+      const float mref = (mx == neg_inf()) ? 0.f : mx;
+      const float corr = exp2f(m - mref);
+      float p[SC];
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < SC; ++j) {
+        p[j] = exp2f(sl[j] - mref);
+        ps += p[j];
+      }
+      l = l * corr + ps;
+      m = mx;
+      float ch[G];
+      Bcast<G, LPQ>::run(corr, ch);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int x = 0; x < DC; ++x) o[h][x] *= ch[h];
+#pragma unroll
+      for (int j = 0; j < SC; ++j) {
+        const int sj = s0 + j;
+        if (sj < e) {
+          const int lo = st.lo[sj];
+          const float w = st.frac[sj];
+          const int r = i - lo - r0;
+          float vt[DC];
+          load_vec<DC>(Vs + r * KS + c * DC, vt);
+          if (w != 0.f) {
+            float vb[DC];
+            load_vec<DC>(Vs + (r - 1) * KS + c * DC, vb);
+#pragma unroll
+            for (int x = 0; x < DC; ++x) vt[x] = fmaf(w, vb[x] - vt[x], vt[x]);
+          }
+          float ph[G];
+          Bcast<G, LPQ>::run(p[j], ph);
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int x = 0; x < DC; ++x) o[h][x] = fmaf(ph[h], vt[x], o[h][x]);
+        }
+      }
+    }
+    s = e;
+  }
+
+  float lh[G];
+  Bcast<G, LPQ>::run(l, lh);
+  if (active) {
+    T* O = static_cast<T*>(a.o);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float inv = 1.f / lh[h];
+      float out[DC];
+#pragma unroll
+      for (int x = 0; x < DC; ++x) out[x] = o[h][x] * inv;
+      store_vec<DC>(O + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, out);
+    }
+    if (a.lse && c < G) a.lse[(size_t(b) * a.hq + size_t(g) * G + c) * n + i] = (m + log2f(l)) * kLn2;
+  }
+}
+
+// ------------------------------------------------------------ edge lists
+
+struct EdgeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const float* rope;
+  const int32_t* edges;
+  const int32_t* count;
+  int n, hq, hkv, nblk, tiles, width;
+  float scale_log2;
+};
+
+template <typename T, int D, int G, int LPQ>
+__global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
+  constexpr int DC = D / LPQ;
+  const int tid = threadIdx.x;
+  const int qq = tid / LPQ;
+  const int c = tid % LPQ;
+  const int own = c % G;
+  const int tile = xcd_tile(blockIdx.x, a.tiles);
+  const int seq = tile / a.nblk;
+  const int blk = tile % a.nblk;
+  const int b = seq / a.hkv, g = seq % a.hkv;
+  const int n = a.n;
+  const int i = blk * BQ + qq;
+  const bool active = i < n;
+
+  const T* __restrict__ Q = static_cast<const T*>(a.q);
+  const T* __restrict__ K = static_cast<const T*>(a.k);
+  const T* __restrict__ V = static_cast<const T*>(a.v);
+  const size_t kv_row = size_t(a.hkv) * D;
+  const T* Kseq = K + size_t(b) * n * kv_row + size_t(g) * D + c * DC;
+  const T* Vseq = V + size_t(b) * n * kv_row + size_t(g) * D + c * DC;
+
+  float qv[G][DC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (active) {
+      load_vec<DC>(Q + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, qv[h]);
+      if (a.rope) rotate_pairs<DC, 1>(qv[h], a.rope + size_t(i) * D, c * DC);
+    } else {
+#pragma unroll
+      for (int x = 0; x < DC; ++x) qv[h][x] = 0.f;
+    }
+  }
+  const int cnt = active ? min(a.count[i], a.width) : 0;
+  // Wave-uniform trip count: the largest list in the wavefront.
+  int cmax = cnt;
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) cmax = max(cmax, __shfl_xor(cmax, msk));
+  const int32_t* erow = a.edges + size_t(active ? i : 0) * a.width;
+
+  float o[G][DC];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int x = 0; x < DC; ++x) o[h][x] = 0.f;
+  float m = neg_inf(), l = 0.f;
+
+  for (int t0 = 0; t0 < cmax; t0 += ESC) {
+    float sl[ESC];
+    int jj[ESC];
+#pragma unroll
+    for (int j = 0; j < ESC; ++j) {
+      const int t = t0 + j;
+      int key = (t < cnt) ? erow[t] : -1;
+      const bool valid = key >= 0 && key < n;
+      jj[j] = valid ? key : -1;
+      float kt[DC];
+      if (valid) {
+        load_vec<DC>(Kseq + size_t(key) * kv_row, kt);
+        if (a.rope) rotate_pairs<DC, 1>(kt, a.rope + size_t(key) * D, c * DC);
+      } else {
+#pragma unroll
+        for (int x = 0; x < DC; ++x) kt[x] = 0.f;
+      }
+      const float mine = own_logit<G, LPQ, DC>(qv, kt, own);
+      sl[j] = valid ? mine * a.scale_log2 : neg_inf();
+    }
+    float mx = m;
+#pragma unroll
+    for (int j = 0; j < ESC; ++j) mx = fmaxf(mx, sl[j]);
+    const float mref = (mx == neg_inf()) ? 0.f : mx;
+    const float corr = exp2f(m - mref);
+    float p[ESC];
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < ESC; ++j) {
+      p[j] = exp2f(sl[j] - mref);
+      ps += p[j];
+    }
+    l = l * corr + ps;
+    m = mx;
+    float ch[G];
+    Bcast<G, LPQ>::run(corr, ch);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int x = 0; x < DC; ++x) o[h][x] *= ch[h];
+#pragma unroll
+    for (int j = 0; j < ESC; ++j) {
+      float vt[DC];
+      if (jj[j] >= 0) {
+        load_vec<DC>(Vseq + size_t(jj[j]) * kv_row, vt);
+      } else {
+#pragma unroll
+        for (int x = 0; x < DC; ++x) vt[x] = 0.f;
+      }
+      float ph[G];
+      Bcast<G, LPQ>::run(p[j], ph);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int x = 0; x < DC; ++x) o[h][x] = fmaf(ph[h], vt[x], o[h][x]);
+    }
+  }
+
+  float lh[G];
+  Bcast<G, LPQ>::run(l, lh);
+  if (active) {
+    T* O = static_cast<T*>(a.o);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float inv = lh[h] > 0.f ? 1.f / lh[h] : 0.f;
+      float out[DC];
+#pragma unroll
+      for (int x = 0; x < DC; ++x) out[x] = o[h][x] * inv;
+      store_vec<DC>(O + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, out);
+    }
+    if (a.lse && c < G)
+      a.lse[(size_t(b) * a.hq + size_t(g) * G + c) * n + i] = l > 0.f ? (m + log2f(l)) * kLn2 : neg_inf();
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+namespace {
+
+constexpr int kCap = 128;  // staged rows per stage (BQ + 64)
+
+template <int D, int G>
+constexpr int fwd_lpq() {
+  // At least one lane per head of the group and at most 16 dims per lane.
+  return G > D / 16 ? G : D / 16;
+}
+
+template <typename T, int D, int G>
+int launch_fwd_offsets_t(const Problem& p, const SlotTable& t, const FwdArgs& a, hipStream_t st) {
+  constexpr int LPQ = fwd_lpq<D, G>();
+  hipLaunchKernelGGL((fwd_offsets_kernel<T, D, G, LPQ, kCap>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+  return int(hipGetLastError());
+}
+
+template <typename T, int D, int G>
+int launch_fwd_edges_t(const EdgeArgs& a, hipStream_t st) {
+  constexpr int LPQ = fwd_lpq<D, G>();
+  hipLaunchKernelGGL((fwd_edges_kernel<T, D, G, LPQ>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a);
+  return int(hipGetLastError());
+}
+
+// Calls F<T, D, G>(args...) for the runtime (dtype, D, G).
+#define SFA_DISPATCH(FN, P, ...)                                                      \
+  do {                                                                                \
+    const int d_ = (P).D, g_ = (P).G;                                                 \
+    if ((P).dtype == SFA_BF16) {                                                      \
+      SFA_DISPATCH_D(bf16_t, FN, d_, g_, __VA_ARGS__);                                \
+    } else {                                                                          \
+      SFA_DISPATCH_D(float, FN, d_, g_, __VA_ARGS__);                                 \
+    }                                                                                 \
+  } while (0)
+#define SFA_DISPATCH_D(T, FN, d_, g_, ...)                                            \
+  do {                                                                                \
+    if (d_ == 64) SFA_DISPATCH_G(T, 64, FN, g_, __VA_ARGS__);                         \
+    else if (d_ == 32) SFA_DISPATCH_G(T, 32, FN, g_, __VA_ARGS__);                    \
+    else SFA_DISPATCH_G(T, 16, FN, g_, __VA_ARGS__);                                  \
+  } while (0)
+#define SFA_DISPATCH_G(T, D_, FN, g_, ...)                                            \
+  do {                                                                                \
+    if (g_ == 1) return FN<T, D_, 1>(__VA_ARGS__);                                    \
+    if (g_ == 2) return FN<T, D_, 2>(__VA_ARGS__);                                    \
+    if (g_ == 4) return FN<T, D_, 4>(__VA_ARGS__);                                    \
+    return FN<T, D_, 8>(__VA_ARGS__);                                                 \
+  } while (0)
+
+}  // namespace
+
+int launch_fwd_offsets(const Problem& p, const SlotTable& t, const void* q, const void* k, const void* v,
+                       void* o, float* lse, void* stream) {
+  FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.rope = p.rope;
+  a.n = p.n;
+  a.hq = p.hq;
+  a.hkv = p.hkv;
+  a.nblk = (p.n + BQ - 1) / BQ;
+  a.tiles = a.nblk * p.B * p.hkv;
+  a.scale_log2 = p.scale * kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  SFA_DISPATCH(launch_fwd_offsets_t, p, p, t, a, st);
+}
+
+int launch_fwd_edges(const Problem& p, const int32_t* edges, const int32_t* count, int width, const void* q,
+                     const void* k, const void* v, void* o, float* lse, void* stream) {
+  EdgeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.rope = p.rope;
+  a.edges = edges;
+  a.count = count;
+  a.n = p.n;
+  a.hq = p.hq;
+  a.hkv = p.hkv;
+  a.nblk = (p.n + BQ - 1) / BQ;
+  a.tiles = a.nblk * p.B * p.hkv;
+  a.width = width;
+  a.scale_log2 = p.scale * kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  SFA_DISPATCH(launch_fwd_edges_t, p, a, st);
+}
+
+}  // namespace sfa

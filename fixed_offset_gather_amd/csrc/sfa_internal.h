@@ -1,0 +1,77 @@
+// Internal declarations shared by the host translation units of libsfa.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "sfa.h"
+
+namespace sfa {
+
+// Thread-local error message; returns `code` so callers can `return fail(...)`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Slot table handed to the shared-offset kernels by value.  Slots are the
+// window distances 0..W and the offsets, sorted by ascending lo (stable, the
+// window first on ties); rung[s] is the caller's offset index or -1.
+struct SlotTable {
+  int32_t count;
+  int32_t n_rungs;
+  int32_t lo[SFA_MAX_SLOTS];
+  float frac[SFA_MAX_SLOTS];
+  int16_t rung[SFA_MAX_SLOTS];
+};
+
+// Kernel launch parameters derived from sfa_attn after validation.
+struct Problem {
+  int B, n, hq, hkv, D, G, dtype, window, n_off;
+  float scale;
+  const float* rope;
+};
+
+int validate_problem(const sfa_attn* a, Problem* p);
+int build_slots(const sfa_attn* a, SlotTable* t);
+
+// Launchers (defined in the .hip translation units).  They return hipError_t
+// as int (0 = success) and never validate: callers have done that.
+int launch_fwd_offsets(const Problem& p, const SlotTable& t, const void* q,
+                       const void* k, const void* v, void* o, float* lse,
+                       void* stream);
+int launch_fwd_edges(const Problem& p, const int32_t* edges,
+                     const int32_t* count, int width, const void* q,
+                     const void* k, const void* v, void* o, float* lse,
+                     void* stream);
+
+struct BwdWorkspace {
+  float* p;        // [B][Hkv][S][n][G] softmax probabilities of valid slots
+  float* dp;       // [B][Hkv][S][n][G] dO . v~ of valid slots
+  float* dvec;     // [B][Hkv][n][G] rowsum(dO * O) = sum_slots p dp
+  float* dd_part;  // [blocks][n_rungs] per-block partial sums of dL/dd_k
+  size_t bytes;
+  int blocks;
+};
+size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base,
+                            BwdWorkspace* ws);
+
+int launch_bwd_query(const Problem& p, const SlotTable& t, const void* q,
+                     const void* k, const void* v, const float* lse,
+                     const void* dout, void* dq, const BwdWorkspace& ws,
+                     void* stream);
+int launch_bwd_key(const Problem& p, const SlotTable& t, const void* q,
+                   const void* k, const void* v, const void* dout, void* dk,
+                   void* dv, const BwdWorkspace& ws, void* stream);
+int launch_bwd_reduce(const SlotTable& t, const BwdWorkspace& ws,
+                      const float* base_f, double alpha, float* dd,
+                      float* dtheta, void* stream);
+
+// Event-pair bracketing for sfa_profile_*; no-ops while profiling is off.
+struct ProfileScope {
+  ProfileScope(const char* name, void* stream);
+  ~ProfileScope();
+  const char* name;
+  void* stream;
+  void* ev0;
+};
+
+}  // namespace sfa
