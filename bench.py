@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse fixed-offset attention hot path on one MI355X.
+
+One step = one training pass of a page-1 attention layer with a learned
+alpha: the rung offsets for alpha (host producer), the forward over the
+window plus the 15 interpolated Fibonacci rungs (with LSE), and the backward
+(dQ, dK, dV, dd and dtheta).  Shape: 32 sequences x 1024 tokens (32,768
+tokens per batch), 8 query heads over 2 key/value heads, head dim 64, window
+10, RoPE 1e4, bf16 tensors with fp32 arithmetic.  Inputs are seeded N(0,1)
+and rotate over four resident sets (336 MB, more than the 256 MB Infinity
+Cache) so HBM, not the cache, serves them.
+
+Prints ONE JSON line: queries/s of the whole step (value), the step's
+algorithmic HBM GB/s, a roofline object for the dominant kernel (timed with
+HIP events on its launch stream over the timed region), the forward alone on
+the fixed-alpha page-1 layer (window 8, integer rungs), and the fp64 CPU
+oracle timed on a bounded sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("sparse-attn fwd(+bwd) queries/sec and achieved HBM GB/s (% of peak), "
+          "1024-ctx GQA")
+HBM_PEAK_GBS = 8000.0
+NSETS = 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(B, n, hq, hkv, D, esize):
+    """Bytes each kernel must move by definition (every tensor once)."""
+    q = B * n * hq * D * esize
+    kv = B * n * hkv * D * esize
+    lse = B * n * hq * 4
+    return {
+        # read Q, K, V; write O and LSE
+        "fwd_offsets": q + 2 * kv + q + lse,
+        # read Q, K, V, dO, LSE; write dQ
+        "bwd_query": q + 2 * kv + q + lse + q,
+        # read Q, dO, K, V; write dK, dV
+        "bwd_key": 2 * q + 2 * kv + 2 * kv,
+        "bwd_reduce": 0,
+        # the step: forward + backward, each tensor once per pass
+        "step": (q + 2 * kv + q + lse) + (q + 2 * kv + q + lse + q + 2 * kv),
+        # forward without LSE
+        "fwd_only": q + 2 * kv + q,
+    }
+
+
+def cpu_baseline(w, alpha, seqs):
+    """The fp64 oracle on `seqs` sequences of the same step, one thread."""
+    from threadpoolctl import threadpool_limits
+
+    import synth_inputs as si
+    from oracle import attention as ref
+    from oracle import offsets as ref_off
+
+    q, k, v = si.qkv(seqs, w["seqlen"], w["hq"], w["hkv"], w["head_dim"], w["dtype"])
+    do = si.upstream(seqs, w["seqlen"], w["hq"], w["head_dim"], w["dtype"])
+    f = [si.to_f64(t) for t in (q, k, v, do)]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        lo, frac = ref_off.rung_offsets(alpha)
+        ref.forward(f[0], f[1], f[2], w["window"], lo, frac, w["rope_theta"])
+        g = ref.backward(*f, w["window"], lo, frac, w["rope_theta"])
+        ref.dtheta_from_dd(g["dd"], ref_off.FIB_BASE, alpha)
+        dt = time.perf_counter() - t0
+    return {
+        "value": seqs * w["seqlen"] / dt,
+        "unit": "queries/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d of %d sequences of the same step (forward + backward, fp64 numpy, one thread), %.1f s"
+                  % (seqs, w["batch"], dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=16)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fixed_offset_gather_amd as sfa
+    import synth_inputs as si
+
+    dev = torch.device("cuda:0")
+    w = si.WORKLOADS["page1_learned_step"]
+    B, n, hq, hkv, D = w["batch"], w["seqlen"], w["hq"], w["hkv"], w["head_dim"]
+    W = w["window"]
+    alpha = si.learned_alpha()
+    base = sfa.base_fib()
+    rope = sfa.rope_table_device(n, D, w["rope_theta"], dev)
+
+    sets = []
+    for s in range(NSETS):
+        q, k, v = si.qkv(B, n, hq, hkv, D, w["dtype"], seed=si.SEED + 10 * s)
+        do = si.upstream(B, n, hq, D, w["dtype"], seed=si.SEED + 10 * s)
+        sets.append(tuple(t.to(dev) for t in (q, k, v, do)))
+    lo, frac = sfa.offsets_fib(alpha)
+    o_buf = torch.empty_like(sets[0][0])
+    lse_buf = torch.empty((B, hq, n), dtype=torch.float32, device=dev)
+    ws = torch.empty(sfa.bwd_workspace_bytes(sets[0][0], sets[0][1], W, lo, frac, rope),
+                     dtype=torch.uint8, device=dev)
+
+    def step(t):
+        q, k, v, do = sets[t % NSETS]
+        lo_, frac_ = sfa.offsets_fib(alpha)
+        o, lse = sfa.fwd(q, k, v, W, lo_, frac_, rope, out=o_buf, lse=lse_buf)
+        return sfa.bwd(q, k, v, lse, do, W, lo_, frac_, rope, base=base, alpha=alpha, workspace=ws)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    sfa.profile_reset()
+    sfa.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        step(t)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sfa.profile_enable(False)
+    kern = {}
+    for name in ("fwd_offsets", "bwd_query", "bwd_key", "bwd_reduce"):
+        ms, cnt = sfa.profile_read(name)
+        if cnt:
+            kern[name] = {"avg_us": 1e3 * ms / cnt, "launches": cnt}
+    ms_per_step = 1e3 * wall / args.steps
+    esize = 2
+    ab = algorithmic_bytes(B, n, hq, hkv, D, esize)
+    step_gbs = ab["step"] / (ms_per_step * 1e-3) / 1e9
+    log("kernel avg us:", {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
+        "step ms %.4f" % ms_per_step)
+
+    dom = max(kern, key=lambda k_: kern[k_]["avg_us"] * kern[k_]["launches"])
+    dom_gbs = ab[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9
+    roofline = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": round(dom_gbs, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
+        "traffic": None,
+        "algorithmic_bytes_per_launch": ab[dom],
+        "avg_launch_us": round(kern[dom]["avg_us"], 3),
+    }
+
+    # Forward alone on the fixed-alpha page-1 layer (window 8, integer rungs).
+    wf = si.WORKLOADS["page1_fixed"]
+    lo1, frac1 = sfa.offsets_fib(wf["alpha"])
+    for t in range(args.warmup):
+        q, k, v, _ = sets[t % NSETS]
+        sfa.fwd(q, k, v, wf["window"], lo1, frac1, rope, out=o_buf)
+    torch.cuda.synchronize()
+    sfa.profile_reset()
+    sfa.profile_enable(True)
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        q, k, v, _ = sets[t % NSETS]
+        sfa.fwd(q, k, v, wf["window"], lo1, frac1, rope, out=o_buf)
+    torch.cuda.synchronize()
+    fwall = time.perf_counter() - t0
+    sfa.profile_enable(False)
+    fms, fcnt = sfa.profile_read("fwd_offsets")
+    f_us = 1e3 * fms / max(fcnt, 1)
+    fwd_only = {
+        "workload": "page1_fixed",
+        "queries_per_s": round(B * n / (f_us * 1e-6), 1),
+        "avg_launch_us": round(f_us, 3),
+        "wall_ms_per_call": round(1e3 * fwall / args.steps, 4),
+        "algorithmic_GBs": round(ab["fwd_only"] / (f_us * 1e-6) / 1e9, 1),
+        "frac_of_hbm_peak": round(ab["fwd_only"] / (f_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+    out = {
+        "metric": METRIC,
+        "value": round(B * n / (ms_per_step * 1e-3), 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "page1_learned_step",
+            "batch": B, "seqlen": n, "hq": hq, "hkv": hkv, "head_dim": D, "window": W,
+            "rungs": "fibonacci x alpha (interpolated)", "alpha": alpha, "rope_theta": w["rope_theta"],
+            "io_dtype": "bf16", "global_batch_tokens": B * n, "parallelism": "single-gpu",
+        },
+        "step_algorithmic_GBs": round(step_gbs, 1),
+        "step_frac_of_hbm_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+        "kernels_avg_us": {k_: round(v_["avg_us"], 3) for k_, v_ in kern.items()},
+        "roofline": roofline,
+        "fwd_only": fwd_only,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, alpha, args.cpu_seqs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

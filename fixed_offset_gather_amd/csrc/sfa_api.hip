@@ -90,27 +90,37 @@ struct Pending {
 std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_free;  // recycled events: no creation per launch
 std::map<std::string, std::pair<double, int64_t>> g_totals;
+
+hipEvent_t take_event() {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_free.empty()) {
+    hipEvent_t e = g_free.back();
+    g_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
 }  // namespace
 
 ProfileScope::ProfileScope(const char* nm, void* st) : name(nm), stream(st), ev0(nullptr) {
   if (!g_prof_on) return;
-  hipEvent_t e;
-  if (hipEventCreate(&e) == hipSuccess) {
-    hipEventRecord(e, static_cast<hipStream_t>(stream));
-    ev0 = e;
-  }
+  hipEvent_t e = take_event();
+  if (e && hipEventRecord(e, static_cast<hipStream_t>(stream)) == hipSuccess) ev0 = e;
 }
 
 ProfileScope::~ProfileScope() {
   if (!ev0) return;
-  hipEvent_t e;
-  if (hipEventCreate(&e) != hipSuccess) {
-    hipEventDestroy(static_cast<hipEvent_t>(ev0));
+  hipEvent_t e = take_event();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!e || hipEventRecord(e, static_cast<hipStream_t>(stream)) != hipSuccess) {
+    g_free.push_back(static_cast<hipEvent_t>(ev0));
+    if (e) g_free.push_back(e);
     return;
   }
-  hipEventRecord(e, static_cast<hipStream_t>(stream));
-  std::lock_guard<std::mutex> lk(g_prof_mu);
   g_pending.push_back({name, static_cast<hipEvent_t>(ev0), e});
 }
 
@@ -122,8 +132,8 @@ static void drain_pending() {
       t.first += ms;
       t.second += 1;
     }
-    hipEventDestroy(p.a);
-    hipEventDestroy(p.b);
+    g_free.push_back(p.a);
+    g_free.push_back(p.b);
   }
   g_pending.clear();
 }

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
       const float dp = own_dot<G, LPQ, DC>(dov, vt, own);
       const int rel = i - lo;
       const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f));
-      const float p = valid ? exp2f(sdot * a.scale_log2 - lse2) : 0.f;
+      const float p = valid ? __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2) : 0.f;
       const float pdp = p * dp;
       dvec += pdp;
       if (valid && c < G) {
@@ -343,17 +343,31 @@ struct ReduceArgs {
   float base[SFA_MAX_OFFSETS];
 };
 
-__global__ __launch_bounds__(SFA_MAX_OFFSETS) void bwd_reduce_kernel(ReduceArgs a) {
+// One workgroup of 256 threads.  Thread t sums blocks t, t+256, ... of every
+// rung in block order, then the 256 partial sums of each rung are added in
+// a fixed tree order: the result does not depend on timing.
+constexpr int kReduceThreads = 256;
+
+__global__ __launch_bounds__(kReduceThreads) void bwd_reduce_kernel(ReduceArgs a) {
+  __shared__ double part[kReduceThreads];
   __shared__ double sdd[SFA_MAX_OFFSETS];
-  const int k = threadIdx.x;
-  if (k < a.n_rungs) {
+  const int t = threadIdx.x;
+  for (int r = 0; r < a.n_rungs; ++r) {
     double acc = 0.0;
-    for (int t = 0; t < a.blocks; ++t) acc += double(a.dd_part[size_t(t) * a.n_rungs + k]);
-    sdd[k] = acc;
-    if (a.dd) a.dd[k] = float(acc);
+    for (int blk = t; blk < a.blocks; blk += kReduceThreads) acc += double(a.dd_part[size_t(blk) * a.n_rungs + r]);
+    part[t] = acc;
+    __syncthreads();
+    for (int s = kReduceThreads / 2; s > 0; s >>= 1) {
+      if (t < s) part[t] += part[t + s];
+      __syncthreads();
+    }
+    if (t == 0) {
+      sdd[r] = part[0];
+      if (a.dd) a.dd[r] = float(part[0]);
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (k == 0 && a.dtheta) {
+  if (t == 0 && a.dtheta) {
     double da = 0.0;
     for (int r = 0; r < a.n_rungs; ++r) da += double(a.base[r]) * sdd[r];
     a.dtheta[0] = float((a.alpha - 0.5) * (1.5 - a.alpha) * da);
@@ -482,7 +496,7 @@ int launch_bwd_reduce(const SlotTable& t, const BwdWorkspace& ws, const float* b
   a.n_rungs = t.n_rungs;
   a.alpha = alpha;
   for (int k = 0; k < t.n_rungs; ++k) a.base[k] = base_f[k];
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(1), dim3(SFA_MAX_OFFSETS), 0, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, static_cast<hipStream_t>(stream), a);
   return int(hipGetLastError());
 }
 

@@ -192,12 +192,12 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
 #pragma unroll
       for (int j = 0; j < SC; ++j) mx = fmaxf(mx, sl[j]);
       const float mref = (mx == neg_inf()) ? 0.f : mx;
-      const float corr = exp2f(m - mref);
+      const float corr = __builtin_amdgcn_exp2f(m - mref);
       float p[SC];
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < SC; ++j) {
-        p[j] = exp2f(sl[j] - mref);
+        p[j] = __builtin_amdgcn_exp2f(sl[j] - mref);
         ps += p[j];
       }
       l = l * corr + ps;
@@ -337,12 +337,12 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
 #pragma unroll
     for (int j = 0; j < ESC; ++j) mx = fmaxf(mx, sl[j]);
     const float mref = (mx == neg_inf()) ? 0.f : mx;
-    const float corr = exp2f(m - mref);
+    const float corr = __builtin_amdgcn_exp2f(m - mref);
     float p[ESC];
     float ps = 0.f;
 #pragma unroll
     for (int j = 0; j < ESC; ++j) {
-      p[j] = exp2f(sl[j] - mref);
+      p[j] = __builtin_amdgcn_exp2f(sl[j] - mref);
       ps += p[j];
     }
     l = l * corr + ps;
