@@ -58,7 +58,7 @@ int validate_problem(const sfa_attn* a, Problem* p) {
   return SFA_OK;
 }
 
-int build_slots(const sfa_attn* a, SlotTable* t) {
+int build_slots(const sfa_attn* a, SlotTable* t, bool merge) {
   struct S {
     int32_t lo;
     float frac;
@@ -70,13 +70,21 @@ int build_slots(const sfa_attn* a, SlotTable* t) {
   for (int k = 0; k < a->n_off; ++k) v.push_back({a->off_lo[k], a->off_frac[k], int16_t(k)});
   std::stable_sort(v.begin(), v.end(), [](const S& x, const S& y) { return x.lo < y.lo; });
   std::memset(t, 0, sizeof(*t));
-  t->count = int32_t(v.size());
   t->n_rungs = a->n_off;
+  int c = 0;
   for (size_t s = 0; s < v.size(); ++s) {
-    t->lo[s] = v[s].lo;
-    t->frac[s] = v[s].frac;
-    t->rung[s] = v[s].rung;
+    if (merge && c > 0 && t->lo[c - 1] == v[s].lo && t->frac[c - 1] == v[s].frac) {
+      t->mult[c - 1] += 1.f;
+      t->rung[c - 1] = -1;
+      continue;
+    }
+    t->lo[c] = v[s].lo;
+    t->frac[c] = v[s].frac;
+    t->mult[c] = 1.f;
+    t->rung[c] = v[s].rung;
+    ++c;
   }
+  t->count = c;
   return SFA_OK;
 }
 
@@ -184,7 +192,7 @@ extern "C" int sfa_fwd(const sfa_attn* a, const void* q, const void* k, const vo
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return fail(SFA_ERR_ARG, "sfa_fwd: tensors must be 16-byte aligned");
   SlotTable t;
-  build_slots(a, &t);
+  build_slots(a, &t, /*merge=*/true);
   ProfileScope ps("fwd_offsets", stream);
   return hip_status(launch_fwd_offsets(p, t, q, k, v, o, lse, stream), "sfa_fwd launch");
 }

@@ -54,7 +54,7 @@ struct Bc {
   template <int H = 0>
   static __device__ __forceinline__ void run(float x, float (&out)[G]) {
     if constexpr (H < G) {
-      out[H] = group_bcast<LPQ, H>(x);
+      out[H] = owner_bcast<G, LPQ, H>(x);
       run<H + 1>(x, out);
     }
   }
@@ -231,83 +231,159 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
 // dV~.(V[i-lo-1] - V[i-lo]) is gathered per key as well: key j meets each
 // rung once as the farther row (tap 1, sign +) and once as the nearer row
 // (tap 0, sign -), both taps taken even when frac = 0.
-template <typename T, int D, int G, int LPQ>
-__global__ __launch_bounds__(BQ* LPQ) void bwd_key_kernel(BwdArgs a, SlotTable st) {
-  constexpr int DC = D / LPQ;
-  constexpr int NT = BQ * LPQ;
-  constexpr int NW = NT / 64;
+//
+// One workgroup per (sequence, block of KB keys, chunk of KC dims); one key
+// per lane.  The query rows a stage of slots needs, [j0 + lo_first,
+// j0 + KB - 1 + lo_last + 1], are staged once into LDS as raw Q and dO
+// elements of the chunk for all G heads, so each row read from L2 serves
+// every (slot, tap) of the stage.  p, dp and Dvec of the next (slot, tap)
+// are loaded one step ahead.
+constexpr int key_chunk(int D) { return D >= 16 ? 16 : D; }
+
+// Keys per workgroup: 128 (two waves) when a staged row (Q and dO of the
+// chunk for all heads) is at most 256 bytes, else 64; a stage holds the
+// block plus 48 rows of slot spread.
+constexpr int key_block(int esize, int G, int D) {
+  return 2 * G * key_chunk(D) * esize <= 256 ? 128 : 64;
+}
+constexpr int key_cap(int kb) { return kb + 48; }
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(BwdArgs a, SlotTable st) {
+  constexpr int KB = key_block(sizeof(T), G, D);
+  constexpr int KCAP = key_cap(KB);
+  constexpr int KC = key_chunk(D);
+  constexpr int NCH = D / KC;
+  constexpr int HW = KC * int(sizeof(T)) / 4;  // 32-bit words per head chunk
+  constexpr int RW = 2 * G * HW + 4;           // words per staged row (Q, dO, pad)
+  constexpr int CH16 = KC * int(sizeof(T)) / 16;  // 16-byte pieces per head chunk
+  constexpr int PPR = 2 * G * CH16;               // 16-byte pieces per row
+  constexpr int NW = KB / 64;
+  static_assert(KC * sizeof(T) % 16 == 0, "16-byte pieces");
+  __shared__ __align__(16) uint32_t Ws[KCAP * RW];
   __shared__ float ddl[NW][SFA_MAX_OFFSETS];
+
   const int tid = threadIdx.x;
   const int wave = tid / 64;
-  const int kk = tid / LPQ;
-  const int c = tid % LPQ;
   const int tile = xcd_tile(blockIdx.x, a.tiles);
-  const int seq = tile / a.nblk;
-  const int blk = tile % a.nblk;
+  const int c = tile % NCH;
+  const int rest = tile / NCH;
+  const int seq = rest / a.nblk;
+  const int blk = rest % a.nblk;
   const int b = seq / a.hkv, g = seq % a.hkv;
   const int n = a.n;
-  const int j0 = blk * BQ;
-  const int j = j0 + kk;
+  const int j0 = blk * KB;
+  const int j = j0 + tid;
   const bool activej = j < n;
 
-  for (int t = tid; t < NW * SFA_MAX_OFFSETS; t += NT) (&ddl[0][0])[t] = 0.f;
-  __syncthreads();
+  for (int t = tid; t < NW * SFA_MAX_OFFSETS; t += KB) (&ddl[0][0])[t] = 0.f;
 
   const T* __restrict__ Q = static_cast<const T*>(a.q);
   const T* __restrict__ dO = static_cast<const T*>(a.dout);
   const size_t ws_seq = size_t(seq) * a.S;
-  const size_t kv_off = (size_t(b) * n + j) * size_t(a.hkv) * D + size_t(g) * D + c * DC;
+  const size_t kv_off = (size_t(b) * n + j) * size_t(a.hkv) * D + size_t(g) * D + c * KC;
 
-  float kj[DC], vj[DC];  // this key's own rows (unrotated K, V), for dd
+  float kj[KC], vj[KC];  // this key's own rows (unrotated K, V), for dd
   if (activej) {
-    load_vec<DC>(static_cast<const T*>(a.k) + kv_off, kj);
-    load_vec<DC>(static_cast<const T*>(a.v) + kv_off, vj);
+    load_vec<KC>(static_cast<const T*>(a.k) + kv_off, kj);
+    load_vec<KC>(static_cast<const T*>(a.v) + kv_off, vj);
   } else {
 #pragma unroll
-    for (int x = 0; x < DC; ++x) kj[x] = vj[x] = 0.f;
+    for (int x = 0; x < KC; ++x) kj[x] = vj[x] = 0.f;
   }
-
-  float dk[DC], dv[DC];
+  float dk[KC], dv[KC];
 #pragma unroll
-  for (int x = 0; x < DC; ++x) dk[x] = dv[x] = 0.f;
+  for (int x = 0; x < KC; ++x) dk[x] = dv[x] = 0.f;
 
   const int S = st.count;
-  for (int sj = 0; sj < S; ++sj) {
-    const int lo = st.lo[sj];
-    if (j0 + lo > n - 1) break;  // no query at this distance for any key of the block
-    const float w = st.frac[sj];
-    const int rung = st.rung[sj];
-    const int taps = (w > 0.f || rung >= 0) ? 2 : 1;
-    for (int tap = 0; tap < taps; ++tap) {
-      const int delta = lo + tap;
-      const float wt = tap ? w : 1.f - w;
-      const int i = j + delta;
-      const bool valid = activej && i < n && (tap == 1 || j > 0 || w == 0.f);
-      float yk[DC], yv[DC];
-#pragma unroll
-      for (int x = 0; x < DC; ++x) yk[x] = yv[x] = 0.f;
-      if (valid) {
+  const int last_key = min(j0 + KB, n) - 1;
+  int s = 0;
+  while (s < S) {
+    const int lo0 = st.lo[s];
+    if (j0 + lo0 > n - 1) break;  // no query at this distance for any key of the block
+    int lomax = lo0;
+    int e = s;
+    while (e < S) {
+      const int le = st.lo[e];
+      if (j0 + le > n - 1 || le - lo0 + KB + 1 > KCAP) break;
+      lomax = le;
+      ++e;
+    }
+    const int r0 = j0 + lo0;                              // query row of LDS row 0
+    const int nrows = min(lomax - lo0 + KB + 1, n - r0);  // rows past n are never read
+
+    __syncthreads();
+    for (int t = tid; t < nrows * PPR; t += KB) {
+      const int row = t / PPR, piece = t % PPR;
+      const int which = piece / (G * CH16);  // 0: Q, 1: dO
+      const int h = (piece / CH16) % G;
+      const int part = piece % CH16;
+      const T* src = (which ? dO : Q) + ((size_t(b) * n + r0 + row) * a.hq + size_t(g) * G + h) * D + c * KC +
+                     part * (16 / int(sizeof(T)));
+      *reinterpret_cast<uint4*>(Ws + row * RW + (which * G + h) * HW + part * 4) =
+          *reinterpret_cast<const uint4*>(src);
+    }
+    __syncthreads();
+
+    // (slot, tap) steps of this stage, with the workspace loads of the next
+    // step issued before the current one is consumed.
+    auto step_valid = [&](int sj, int tap) {
+      const float w = st.frac[sj];
+      const int i = j + st.lo[sj] + tap;
+      return activej && i < n && (tap == 1 || j > 0 || w == 0.f);
+    };
+    auto load_step = [&](int sj, int tap, float (&pg)[G], float (&dpg)[G], float (&dvg)[G]) {
+      if (step_valid(sj, tap)) {
+        const int i = j + st.lo[sj] + tap;
         const size_t widx = ((ws_seq + sj) * n + i) * G;
-        float pg[G], dpg[G], dvg[G];
         load_vec<G>(a.P + widx, pg);
         load_vec<G>(a.dP + widx, dpg);
         load_vec<G>(a.Dvec + (size_t(seq) * n + i) * G, dvg);
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) pg[h] = dpg[h] = dvg[h] = 0.f;
+      }
+    };
+    auto taps_of = [&](int sj) { return (st.frac[sj] > 0.f || st.rung[sj] >= 0) ? 2 : 1; };
+
+    float pg[G], dpg[G], dvg[G];
+    load_step(s, 0, pg, dpg, dvg);
+    int sj = s, tap = 0;
+    while (sj < e) {
+      int nsj = sj, ntap = tap + 1;
+      if (ntap >= taps_of(sj)) {
+        ++nsj;
+        ntap = 0;
+      }
+      float pn[G], dpn[G], dvn[G];
+      if (nsj < e) load_step(nsj, ntap, pn, dpn, dvn);
+
+      const int lo = st.lo[sj];
+      const float w = st.frac[sj];
+      const int rung = st.rung[sj];
+      const int delta = lo + tap;
+      const float wt = tap ? w : 1.f - w;
+      const bool valid = step_valid(sj, tap);
+      float yk[KC], yv[KC];
+#pragma unroll
+      for (int x = 0; x < KC; ++x) yk[x] = yv[x] = 0.f;
+      if (valid) {
+        const uint32_t* rowp = Ws + (j + delta - r0) * RW;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const float dsh = a.scale * pg[h] * (dpg[h] - dvg[h]);
-          const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC;
-          float qh[DC], oh[DC];
-          load_vec<DC>(Q + off, qh);
-          load_vec<DC>(dO + off, oh);
+          float qh[KC], oh[KC];
+          load_vec<KC>(reinterpret_cast<const T*>(rowp + h * HW), qh);
+          load_vec<KC>(reinterpret_cast<const T*>(rowp + (G + h) * HW), oh);
 #pragma unroll
-          for (int x = 0; x < DC; ++x) {
+          for (int x = 0; x < KC; ++x) {
             yk[x] = fmaf(dsh, qh[x], yk[x]);
             yv[x] = fmaf(pg[h], oh[x], yv[x]);
           }
         }
-        if (a.rope) rotate_pairs<DC, 1>(yk, a.rope + size_t(delta) * D, c * DC);
+        if (a.rope) rotate_pairs<KC, 1>(yk, a.rope + size_t(delta) * D, c * KC);
 #pragma unroll
-        for (int x = 0; x < DC; ++x) {
+        for (int x = 0; x < KC; ++x) {
           dk[x] = fmaf(wt, yk[x], dk[x]);
           dv[x] = fmaf(wt, yv[x], dv[x]);
         }
@@ -315,18 +391,30 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_key_kernel(BwdArgs a, SlotTable s
       if (rung >= 0) {
         float part = 0.f;
 #pragma unroll
-        for (int x = 0; x < DC; ++x) part = fmaf(yk[x], kj[x], fmaf(yv[x], vj[x], part));
+        for (int x = 0; x < KC; ++x) part = fmaf(yk[x], kj[x], fmaf(yv[x], vj[x], part));
         const float tot = wave_sum(tap ? part : -part);
         if ((tid & 63) == 0) ddl[wave][rung] += tot;
       }
+      if (nsj < e) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          pg[h] = pn[h];
+          dpg[h] = dpn[h];
+          dvg[h] = dvn[h];
+        }
+      }
+      sj = nsj;
+      tap = ntap;
     }
+    s = e;
+    (void)last_key;
   }
   if (activej) {
-    store_vec<DC>(static_cast<T*>(a.dk) + kv_off, dk);
-    store_vec<DC>(static_cast<T*>(a.dv) + kv_off, dv);
+    store_vec<KC>(static_cast<T*>(a.dk) + kv_off, dk);
+    store_vec<KC>(static_cast<T*>(a.dv) + kv_off, dv);
   }
   __syncthreads();
-  for (int r = tid; r < a.n_rungs; r += NT) {
+  for (int r = tid; r < a.n_rungs; r += KB) {
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) acc += ddl[w][r];
@@ -384,11 +472,7 @@ constexpr int bwd_lpq() {
   return b < 16 ? b : 16;
 }
 
-// Lanes per key in bwd_key: 16 dims each (the lane sums over all G heads).
-template <int D>
-constexpr int key_lpk() {
-  return D >= 16 ? D / 16 : 1;
-}
+
 
 BwdArgs make_args(const Problem& p, const SlotTable& t, const BwdWorkspace& ws) {
   BwdArgs a{};
@@ -417,9 +501,12 @@ int launch_query_t(const BwdArgs& a, const SlotTable& t, hipStream_t st) {
 }
 
 template <typename T, int D, int G>
-int launch_key_t(const BwdArgs& a, const SlotTable& t, hipStream_t st) {
-  constexpr int LPQ = key_lpk<D>();
-  hipLaunchKernelGGL((bwd_key_kernel<T, D, G, LPQ>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
+  constexpr int KB = key_block(sizeof(T), G, D);
+  BwdArgs a = a0;
+  a.nblk = (a.n + KB - 1) / KB;
+  a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk(D));
+  hipLaunchKernelGGL((bwd_key_kernel<T, D, G>), dim3(a.tiles), dim3(KB), 0, st, a, t);
   return int(hipGetLastError());
 }
 
@@ -449,7 +536,9 @@ size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, Bw
   auto al = [](size_t e) { return (e + 63) & ~size_t(63); };  // 256-byte aligned sections
   const size_t pe = al(size_t(p.B) * p.hkv * t.count * size_t(p.n) * p.G);  // floats per array
   const size_t de = al(size_t(p.B) * p.hkv * size_t(p.n) * p.G);
-  ws->blocks = nblk * p.B * p.hkv;
+  const int kb = key_block(p.dtype == SFA_BF16 ? 2 : 4, p.G, p.D);
+  ws->blocks = ((p.n + kb - 1) / kb) * p.B * p.hkv * (p.D / key_chunk(p.D));  // bwd_key tiles
+  (void)nblk;
   const size_t dd_e = size_t(ws->blocks) * (t.n_rungs > 0 ? t.n_rungs : 1);
   float* f = static_cast<float*>(base);
   ws->p = f;

@@ -129,6 +129,53 @@ __device__ __forceinline__ void store_vec(bf16_t* __restrict__ p, const float (&
   }
 }
 
+// ------------------------------------------------------- packed f16
+
+// Two f16 values in one 32-bit register (low half = even element).
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  const half2_t h = {(_Float16)lo, (_Float16)hi};  // round to nearest even
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t w) { return __builtin_bit_cast(half2_t, w); }
+
+// a.lo*b.lo + a.hi*b.hi + c with f16 products accumulated in fp32.
+__device__ __forceinline__ float dot2_h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
+}
+
+// a + w (b - a) on both halves (packed f16 arithmetic).
+__device__ __forceinline__ uint32_t lerp_h2(uint32_t a, uint32_t b, half2_t w) {
+  const half2_t x = as_h2(a), y = as_h2(b);
+  return __builtin_bit_cast(uint32_t, x + w * (y - x));
+}
+
+// fp32 c + p * (f16 element): one mixed-precision FMA, no unpacking.
+__device__ __forceinline__ float fma_lo(float p, uint32_t w, float c) { return fmaf(p, (float)as_h2(w).x, c); }
+__device__ __forceinline__ float fma_hi(float p, uint32_t w, float c) { return fmaf(p, (float)as_h2(w).y, c); }
+
+template <int N>
+__device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint32_t (&out)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 4) {
+      const uint4 t = *reinterpret_cast<const uint4*>(p + x);
+      out[x] = t.x; out[x + 1] = t.y; out[x + 2] = t.z; out[x + 3] = t.w;
+    }
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 2) {
+      const uint2 t = *reinterpret_cast<const uint2*>(p + x);
+      out[x] = t.x; out[x + 1] = t.y;
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < N; ++x) out[x] = p[x];
+  }
+}
+
 // ------------------------------------------------------------- rotation
 
 // Rotate the interleaved pairs of x (dims d0 .. d0+N-1 of a head, d0 even)
@@ -151,9 +198,12 @@ __device__ __forceinline__ void rotate_pairs(float (&x)[N], const float* __restr
 
 // ------------------------------------------------------- lane exchange
 
+// Lane permutation within rows of 16 lanes.  Every control used here reads
+// a valid lane of the same row, so no fill value is needed (bound_ctrl set)
+// and the move can fold into the consuming add as a DPP operand.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 constexpr int quad_perm(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
@@ -185,6 +235,30 @@ __device__ __forceinline__ float group_bcast(float x) {
   } else {
     const int lane = __lane_id();
     return __shfl(x, (lane & ~(L - 1)) + H);
+  }
+}
+
+// Value held by the lanes that own head H, where lane c of a query's
+// aligned group of L lanes owns head c % G (L a multiple of G, so the owners
+// repeat every G lanes and all owners of one head hold the same value).
+// L <= 2: the group is part of a quad.  L >= 4 and G <= 4: one DPP move
+// inside the lane's quad, which lies in the lane's own group.  G == 8: the
+// quad holding head H is the lane's own quad or its mirror in the 8-lane
+// half row, both inside the group.
+template <int G, int L, int H>
+__device__ __forceinline__ float owner_bcast(float x) {
+  static_assert(H < G && L % G == 0, "head in group");
+  if constexpr (G == 1) {
+    return x;
+  } else if constexpr (L == 2) {
+    return dpp<quad_perm(H, H, 2 + H, 2 + H)>(x);
+  } else if constexpr (G <= 4) {
+    return dpp<quad_perm(H, H, H, H)>(x);
+  } else {
+    static_assert(G == 8, "group size");
+    const float v = dpp<quad_perm(H & 3, H & 3, H & 3, H & 3)>(x);
+    const float w = dpp<kDppRowHalfMirror>(v);
+    return ((__lane_id() >> 2) & 1) == (H >> 2) ? v : w;
   }
 }
 

@@ -26,6 +26,24 @@
 
 namespace sfa {
 
+// Tuning knobs (compile-time): rows per LDS stage of the f16 kernel, whether
+// a stage's global loads are all issued before conversion, and the waves
+// per SIMD the register allocation must allow (0 = compiler's choice).
+#ifndef SFA_FWD_CAP
+#define SFA_FWD_CAP 128
+#endif
+#ifndef SFA_FWD_HOIST
+#define SFA_FWD_HOIST 0
+#endif
+#ifndef SFA_FWD_MINWAVES
+#define SFA_FWD_MINWAVES 0
+#endif
+// bf16 tensors: 0 = fp32 kernel, 1 = f16 keys and values, 2 = f16 keys and
+// fp32 values.
+#ifndef SFA_FWD_BF16_PATH
+#define SFA_FWD_BF16_PATH 1
+#endif
+
 constexpr int BQ = 64;   // queries per workgroup
 constexpr int SC = 8;    // slots per online-softmax chunk
 constexpr int ESC = 4;   // edges per chunk (keys come from global memory)
@@ -68,7 +86,7 @@ struct Bcast {
   template <int H = 0>
   static __device__ __forceinline__ void run(float x, float (&out)[G]) {
     if constexpr (H < G) {
-      out[H] = group_bcast<LPQ, H>(x);
+      out[H] = owner_bcast<G, LPQ, H>(x);
       run<H + 1>(x, out);
     }
   }
@@ -98,6 +116,18 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
   const int i = i0 + qq;
   const bool active = i < n;
   const int i_last = min(i0 + BQ, n) - 1;
+
+  // Slot table copied to LDS once: the hot loops read it with uniform
+  // addresses instead of scalar loads from the kernel arguments.
+  __shared__ int s_lo[SFA_MAX_SLOTS];
+  __shared__ float s_w[SFA_MAX_SLOTS];
+  __shared__ float s_mult[SFA_MAX_SLOTS];
+  for (int t = threadIdx.x; t < st.count; t += blockDim.x) {
+    s_lo[t] = st.lo[t];
+    s_w[t] = st.frac[t];
+    s_mult[t] = st.mult[t];
+  }
+  __syncthreads();
 
   const T* __restrict__ Q = static_cast<const T*>(a.q);
   const T* __restrict__ K = static_cast<const T*>(a.k);
@@ -171,8 +201,8 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
         sl[j] = neg_inf();
         const int sj = s0 + j;
         if (sj < e) {
-          const int lo = st.lo[sj];
-          const float w = st.frac[sj];
+          const int lo = __builtin_amdgcn_readfirstlane(s_lo[sj]);
+          const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_w[sj])));
           const int r = i - lo - r0;  // in [0, nrows) for every lane of the block
           float kt[DC];
           load_vec<DC>(Ks + r * KS + c * DC, kt);
@@ -198,6 +228,7 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
 #pragma unroll
       for (int j = 0; j < SC; ++j) {
         p[j] = __builtin_amdgcn_exp2f(sl[j] - mref);
+        if (s0 + j < e) p[j] *= s_mult[s0 + j];
         ps += p[j];
       }
       l = l * corr + ps;
@@ -212,8 +243,8 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
       for (int j = 0; j < SC; ++j) {
         const int sj = s0 + j;
         if (sj < e) {
-          const int lo = st.lo[sj];
-          const float w = st.frac[sj];
+          const int lo = __builtin_amdgcn_readfirstlane(s_lo[sj]);
+          const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_w[sj])));
           const int r = i - lo - r0;
           float vt[DC];
           load_vec<DC>(Vs + r * KS + c * DC, vt);
@@ -239,6 +270,303 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
   Bcast<G, LPQ>::run(l, lh);
   if (active) {
     T* O = static_cast<T*>(a.o);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float inv = 1.f / lh[h];
+      float out[DC];
+#pragma unroll
+      for (int x = 0; x < DC; ++x) out[x] = o[h][x] * inv;
+      store_vec<DC>(O + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, out);
+    }
+    if (a.lse && c < G) a.lse[(size_t(b) * a.hq + size_t(g) * G + c) * n + i] = (m + log2f(l)) * kLn2;
+  }
+}
+
+// bf16 tensors: the same algorithm with f16 operands.  LDS holds K rotated
+// at its true position and V, both as packed f16 (half the footprint of
+// fp32 rows, so more workgroups fit on a CU); the query is rotated, scaled
+// by scale*log2(e) and packed to f16 once.  Logits use v_dot2c_f32_f16 (two
+// f16 products per instruction, fp32 accumulation), interpolation is packed
+// f16 arithmetic, and the value sum is a mixed-precision FMA into fp32
+// accumulators.  The softmax and the output accumulation stay in fp32.
+#if SFA_FWD_MINWAVES > 0
+#define SFA_FWD_BOUNDS(T) __launch_bounds__(T, SFA_FWD_MINWAVES)
+#else
+#define SFA_FWD_BOUNDS(T) __launch_bounds__(T)
+#endif
+
+template <int D, int G, int LPQ, int CAP, bool VF32>
+__global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTable st) {
+  constexpr int DC = D / LPQ;  // dims per lane
+  constexpr int DW = DC / 2;   // f16 pairs per lane
+  constexpr int RW = D / 2 + 4;  // 32-bit words per LDS row (16-byte pad)
+  constexpr int VRW = VF32 ? D + 4 : RW;  // words per value row
+  constexpr int CPR = D / 8;     // 16-byte global chunks (8 bf16) per row
+  constexpr int NT = BQ * LPQ;
+  static_assert(DC >= 2 && DC % 2 == 0, "lane chunk");
+  __shared__ __align__(16) uint32_t Ks[CAP * RW];
+  __shared__ __align__(16) uint32_t Vs[CAP * VRW];
+
+  const int tid = threadIdx.x;
+  const int qq = tid / LPQ;
+  const int c = tid % LPQ;
+  const int own = c % G;
+  const int tile = xcd_tile(blockIdx.x, a.tiles);
+  const int seq = tile / a.nblk;
+  const int blk = a.nblk - 1 - tile % a.nblk;  // longest blocks first
+  const int b = seq / a.hkv, g = seq % a.hkv;
+  const int n = a.n;
+  const int i0 = blk * BQ;
+  const int i = i0 + qq;
+  const bool active = i < n;
+  const int i_last = min(i0 + BQ, n) - 1;
+
+  // Slot table copied to LDS once: the hot loops read it with uniform
+  // addresses instead of scalar loads from the kernel arguments.
+  __shared__ int s_lo[SFA_MAX_SLOTS];
+  __shared__ float s_w[SFA_MAX_SLOTS];
+  __shared__ float s_mult[SFA_MAX_SLOTS];
+  for (int t = threadIdx.x; t < st.count; t += blockDim.x) {
+    s_lo[t] = st.lo[t];
+    s_w[t] = st.frac[t];
+    s_mult[t] = st.mult[t];
+  }
+  __syncthreads();
+
+  const bf16_t* __restrict__ Q = static_cast<const bf16_t*>(a.q);
+  const bf16_t* __restrict__ K = static_cast<const bf16_t*>(a.k);
+  const bf16_t* __restrict__ V = static_cast<const bf16_t*>(a.v);
+
+  uint32_t qh[G][DW];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float qf[DC];
+    if (active) {
+      load_vec<DC>(Q + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, qf);
+      if (a.rope) rotate_pairs<DC, 1>(qf, a.rope + size_t(i) * D, c * DC);
+    } else {
+#pragma unroll
+      for (int x = 0; x < DC; ++x) qf[x] = 0.f;
+    }
+#pragma unroll
+    for (int x = 0; x < DW; ++x) qh[h][x] = pack_h2(qf[2 * x] * a.scale_log2, qf[2 * x + 1] * a.scale_log2);
+  }
+
+  float o[G][DC];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int x = 0; x < DC; ++x) o[h][x] = 0.f;
+  float m = neg_inf(), l = 0.f;
+
+  const size_t kv_row = size_t(a.hkv) * D;
+  const bf16_t* Kseq = K + size_t(b) * n * kv_row + size_t(g) * D;
+  const bf16_t* Vseq = V + size_t(b) * n * kv_row + size_t(g) * D;
+
+  int s = 0;
+  const int S = st.count;
+  while (s < S) {
+    const int lo0 = st.lo[s];
+    if (lo0 > i_last) break;
+    int lomax = lo0 + (st.frac[s] > 0.f ? 1 : 0);
+    int e = s + 1;
+    while (e < S) {
+      const int le = st.lo[e];
+      if (le > i_last) break;
+      const int need = max(lomax, le + (st.frac[e] > 0.f ? 1 : 0));
+      if (need - lo0 + BQ > CAP) break;
+      lomax = need;
+      ++e;
+    }
+    const int r0 = i0 - lomax;
+    const int nrows = lomax - lo0 + BQ;
+
+    __syncthreads();
+#if SFA_FWD_HOIST
+    {
+      // Issue every global load of this thread's chunks first (they overlap
+      // in flight), then rotate, convert and store.
+      constexpr int PER = (CAP * CPR + NT - 1) / NT;
+      uint4 kr[PER], vr[PER];
+      float4 cs0[PER], cs1[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int t = tid + u * NT;
+        const int row = t / CPR, cc = t % CPR;
+        const int pos = r0 + row;
+        kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
+        cs0[u] = cs1[u] = make_float4(1.f, 0.f, 1.f, 0.f);
+        if (t < nrows * CPR && pos >= 0 && pos < n) {
+          kr[u] = *reinterpret_cast<const uint4*>(Kseq + size_t(pos) * kv_row + cc * 8);
+          vr[u] = *reinterpret_cast<const uint4*>(Vseq + size_t(pos) * kv_row + cc * 8);
+          if (a.rope) {
+            const float4* rp = reinterpret_cast<const float4*>(a.rope + size_t(pos) * D + cc * 8);
+            cs0[u] = rp[0];
+            cs1[u] = rp[1];
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int t = tid + u * NT;
+        if (t < nrows * CPR) {
+          const int row = t / CPR, cc = t % CPR;
+          const uint32_t kw4[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
+          const float cs[8] = {cs0[u].x, cs0[u].y, cs0[u].z, cs0[u].w, cs1[u].x, cs1[u].y, cs1[u].z, cs1[u].w};
+          uint32_t ko[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const float e0 = bf16_lo(kw4[x]), e1 = bf16_hi(kw4[x]);
+            const float c_ = cs[2 * x], s_ = cs[2 * x + 1];
+            ko[x] = pack_h2(e0 * c_ - e1 * s_, e0 * s_ + e1 * c_);
+          }
+          *reinterpret_cast<uint4*>(Ks + row * RW + cc * 4) = make_uint4(ko[0], ko[1], ko[2], ko[3]);
+          if constexpr (VF32) {
+            float* vrow = reinterpret_cast<float*>(Vs + row * VRW) + cc * 8;
+            *reinterpret_cast<float4*>(vrow) =
+                make_float4(bf16_lo(vr[u].x), bf16_hi(vr[u].x), bf16_lo(vr[u].y), bf16_hi(vr[u].y));
+            *reinterpret_cast<float4*>(vrow + 4) =
+                make_float4(bf16_lo(vr[u].z), bf16_hi(vr[u].z), bf16_lo(vr[u].w), bf16_hi(vr[u].w));
+          } else {
+            *reinterpret_cast<uint4*>(Vs + row * VRW + cc * 4) =
+                make_uint4(pack_h2(bf16_lo(vr[u].x), bf16_hi(vr[u].x)), pack_h2(bf16_lo(vr[u].y), bf16_hi(vr[u].y)),
+                           pack_h2(bf16_lo(vr[u].z), bf16_hi(vr[u].z)), pack_h2(bf16_lo(vr[u].w), bf16_hi(vr[u].w)));
+          }
+        }
+      }
+    }
+#else
+    for (int t = tid; t < nrows * CPR; t += NT) {
+      const int row = t / CPR, cc = t % CPR;
+      const int pos = r0 + row;
+      float kf[8], vf[8];
+      if (pos >= 0 && pos < n) {
+        load_vec<8>(Kseq + size_t(pos) * kv_row + cc * 8, kf);
+        load_vec<8>(Vseq + size_t(pos) * kv_row + cc * 8, vf);
+        if (a.rope) rotate_pairs<8, 1>(kf, a.rope + size_t(pos) * D, cc * 8);
+      } else {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) kf[x] = vf[x] = 0.f;
+      }
+      *reinterpret_cast<uint4*>(Ks + row * RW + cc * 4) =
+          make_uint4(pack_h2(kf[0], kf[1]), pack_h2(kf[2], kf[3]), pack_h2(kf[4], kf[5]), pack_h2(kf[6], kf[7]));
+      if constexpr (VF32) {
+        store_vec<8>(reinterpret_cast<float*>(Vs + row * VRW) + cc * 8, vf);
+      } else {
+        *reinterpret_cast<uint4*>(Vs + row * VRW + cc * 4) =
+            make_uint4(pack_h2(vf[0], vf[1]), pack_h2(vf[2], vf[3]), pack_h2(vf[4], vf[5]), pack_h2(vf[6], vf[7]));
+      }
+    }
+#endif
+    __syncthreads();
+
+    for (int s0 = s; s0 < e; s0 += SC) {
+      float sl[SC];
+#pragma unroll
+      for (int j = 0; j < SC; ++j) {
+        sl[j] = neg_inf();
+        const int sj = s0 + j;
+        if (sj < e) {
+          const int lo = __builtin_amdgcn_readfirstlane(s_lo[sj]);
+          const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_w[sj])));
+          const int r = i - lo - r0;
+          uint32_t kw[DW];
+          load_words<DW>(Ks + r * RW + c * DW, kw);
+          if (w != 0.f) {
+            uint32_t kb[DW];
+            load_words<DW>(Ks + (r - 1) * RW + c * DW, kb);
+            const half2_t w2 = {(_Float16)w, (_Float16)w};
+#pragma unroll
+            for (int x = 0; x < DW; ++x) kw[x] = lerp_h2(kw[x], kb[x], w2);
+          }
+          float part[G];
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            float acc = 0.f;
+#pragma unroll
+            for (int x = 0; x < DW; ++x) acc = dot2_h(qh[h][x], kw[x], acc);
+            part[h] = group_sum<LPQ>(acc);
+          }
+          float mine = part[0];
+#pragma unroll
+          for (int h = 1; h < G; ++h) mine = (own == h) ? part[h] : mine;
+          const int rel = i - lo;
+          const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f));
+          sl[j] = valid ? mine : neg_inf();
+        }
+      }
+      float mx = m;
+#pragma unroll
+      for (int j = 0; j < SC; ++j) mx = fmaxf(mx, sl[j]);
+      const float mref = (mx == neg_inf()) ? 0.f : mx;
+      const float corr = __builtin_amdgcn_exp2f(m - mref);
+      float p[SC];
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < SC; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(sl[j] - mref);
+        if (s0 + j < e) p[j] *= s_mult[s0 + j];
+        ps += p[j];
+      }
+      l = l * corr + ps;
+      m = mx;
+      float ch[G];
+      Bcast<G, LPQ>::run(corr, ch);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int x = 0; x < DC; ++x) o[h][x] *= ch[h];
+#pragma unroll
+      for (int j = 0; j < SC; ++j) {
+        const int sj = s0 + j;
+        if (sj < e) {
+          const int lo = __builtin_amdgcn_readfirstlane(s_lo[sj]);
+          const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_w[sj])));
+          const int r = i - lo - r0;
+          float ph[G];
+          Bcast<G, LPQ>::run(p[j], ph);
+          if constexpr (VF32) {
+            const float* vrow = reinterpret_cast<const float*>(Vs + r * VRW) + c * DC;
+            float vt[DC];
+            load_vec<DC>(vrow, vt);
+            if (w != 0.f) {
+              float vb[DC];
+              load_vec<DC>(vrow - VRW, vb);
+#pragma unroll
+              for (int x = 0; x < DC; ++x) vt[x] = fmaf(w, vb[x] - vt[x], vt[x]);
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+              for (int x = 0; x < DC; ++x) o[h][x] = fmaf(ph[h], vt[x], o[h][x]);
+          } else {
+            uint32_t vw[DW];
+            load_words<DW>(Vs + r * VRW + c * DW, vw);
+            if (w != 0.f) {
+              uint32_t vb[DW];
+              load_words<DW>(Vs + (r - 1) * VRW + c * DW, vb);
+              const half2_t w2 = {(_Float16)w, (_Float16)w};
+#pragma unroll
+              for (int x = 0; x < DW; ++x) vw[x] = lerp_h2(vw[x], vb[x], w2);
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+              for (int x = 0; x < DW; ++x) {
+                o[h][2 * x] = fma_lo(ph[h], vw[x], o[h][2 * x]);
+                o[h][2 * x + 1] = fma_hi(ph[h], vw[x], o[h][2 * x + 1]);
+              }
+          }
+        }
+      }
+    }
+    s = e;
+  }
+
+  float lh[G];
+  Bcast<G, LPQ>::run(l, lh);
+  if (active) {
+    bf16_t* O = static_cast<bf16_t*>(a.o);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float inv = 1.f / lh[h];
@@ -403,7 +731,12 @@ constexpr int fwd_lpq() {
 template <typename T, int D, int G>
 int launch_fwd_offsets_t(const Problem& p, const SlotTable& t, const FwdArgs& a, hipStream_t st) {
   constexpr int LPQ = fwd_lpq<D, G>();
-  hipLaunchKernelGGL((fwd_offsets_kernel<T, D, G, LPQ, kCap>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+  if constexpr (sizeof(T) == 2 && SFA_FWD_BF16_PATH > 0) {
+    hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, SFA_FWD_CAP, SFA_FWD_BF16_PATH == 2>), dim3(a.tiles),
+                       dim3(BQ * LPQ), 0, st, a, t);
+  } else {
+    hipLaunchKernelGGL((fwd_offsets_kernel<T, D, G, LPQ, kCap>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+  }
   return int(hipGetLastError());
 }
 

@@ -14,12 +14,16 @@ void clear_error();
 
 // Slot table handed to the shared-offset kernels by value.  Slots are the
 // window distances 0..W and the offsets, sorted by ascending lo (stable, the
-// window first on ties); rung[s] is the caller's offset index or -1.
+// window first on ties); rung[s] is the caller's offset index or -1.  With
+// merging (forward only), slots naming the same (lo, frac) become one entry
+// of multiplicity mult[s]: its softmax weight is mult * exp(logit), exactly
+// the sum of the identical slots.
 struct SlotTable {
   int32_t count;
   int32_t n_rungs;
   int32_t lo[SFA_MAX_SLOTS];
   float frac[SFA_MAX_SLOTS];
+  float mult[SFA_MAX_SLOTS];
   int16_t rung[SFA_MAX_SLOTS];
 };
 
@@ -31,7 +35,7 @@ struct Problem {
 };
 
 int validate_problem(const sfa_attn* a, Problem* p);
-int build_slots(const sfa_attn* a, SlotTable* t);
+int build_slots(const sfa_attn* a, SlotTable* t, bool merge = false);
 
 // Launchers (defined in the .hip translation units).  They return hipError_t
 // as int (0 = success) and never validate: callers have done that.
