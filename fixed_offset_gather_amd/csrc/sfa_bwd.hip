@@ -431,33 +431,31 @@ struct ReduceArgs {
   float base[SFA_MAX_OFFSETS];
 };
 
-// One workgroup of 256 threads.  Thread t sums blocks t, t+256, ... of every
-// rung in block order, then the 256 partial sums of each rung are added in
-// a fixed tree order: the result does not depend on timing.
-constexpr int kReduceThreads = 256;
+// One workgroup of 16 waves.  Wave w reduces rungs w, w+16, ...: lane l adds
+// the partial sums of blocks l, l+64, ... in block order, then the wave adds
+// its 64 lanes in a fixed DPP/shuffle tree.  The result does not depend on
+// timing.
+constexpr int kReduceThreads = 1024;
 
 __global__ __launch_bounds__(kReduceThreads) void bwd_reduce_kernel(ReduceArgs a) {
-  __shared__ double part[kReduceThreads];
-  __shared__ double sdd[SFA_MAX_OFFSETS];
-  const int t = threadIdx.x;
-  for (int r = 0; r < a.n_rungs; ++r) {
-    double acc = 0.0;
-    for (int blk = t; blk < a.blocks; blk += kReduceThreads) acc += double(a.dd_part[size_t(blk) * a.n_rungs + r]);
-    part[t] = acc;
-    __syncthreads();
-    for (int s = kReduceThreads / 2; s > 0; s >>= 1) {
-      if (t < s) part[t] += part[t + s];
-      __syncthreads();
+  __shared__ float sdd[SFA_MAX_OFFSETS];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int r = wave; r < a.n_rungs; r += kReduceThreads / 64) {
+    float acc = 0.f;
+    int blk = lane;
+#pragma unroll 4
+    for (; blk < a.blocks; blk += 64) acc += a.dd_part[size_t(blk) * a.n_rungs + r];
+    const float tot = wave_sum(acc);
+    if (lane == 0) {
+      sdd[r] = tot;
+      if (a.dd) a.dd[r] = tot;
     }
-    if (t == 0) {
-      sdd[r] = part[0];
-      if (a.dd) a.dd[r] = float(part[0]);
-    }
-    __syncthreads();
   }
-  if (t == 0 && a.dtheta) {
+  __syncthreads();
+  if (threadIdx.x == 0 && a.dtheta) {
     double da = 0.0;
-    for (int r = 0; r < a.n_rungs; ++r) da += double(a.base[r]) * sdd[r];
+    for (int r = 0; r < a.n_rungs; ++r) da += double(a.base[r]) * double(sdd[r]);
     a.dtheta[0] = float((a.alpha - 0.5) * (1.5 - a.alpha) * da);
   }
 }
