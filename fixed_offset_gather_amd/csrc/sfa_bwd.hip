@@ -11,8 +11,8 @@
 //   Dvec = rowsum(dO*O) is formed exactly as sum_slots p dp (not from the
 //   rounded forward output), and dq~ = scale sum p (dp - Dvec) k~ is
 //   accumulated as scale (sum p dp k~ - Dvec sum p k~), then rotated back to
-//   dQ.  p, dp and Dvec of every valid (query, slot, head) go to the
-//   workspace.
+//   dQ.  p (0 where the slot has no row), dp and Dvec of every (query,
+//   slot, head) go to the workspace.
 // bwd_key (key-centric transpose gather): key j receives from query j+lo
 //   (weight 1-frac) and j+lo+1 (weight frac) of every slot; those queries
 //   form contiguous ranges, so each lane gathers instead of scattering.
@@ -46,6 +46,7 @@ struct BwdArgs {
   float* dd_part;
   const float* rope;
   int n, hq, hkv, nblk, tiles, S, n_rungs;
+  int kcap;  // bwd_key: rows one stage may hold (dynamic LDS)
   float scale, scale_log2;
 };
 
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
       const float p = valid ? __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2) : 0.f;
       const float pdp = p * dp;
       dvec += pdp;
-      if (valid && c < G) {
+      if (active && c < G) {  // p = 0 where the slot has no row for query i
         const size_t widx = ((ws_seq + sj) * n + i) * G + c;
         a.P[widx] = p;
         a.dP[widx] = dp;
@@ -247,6 +248,23 @@ constexpr int key_block(int esize, int G, int D) {
   return 2 * G * key_chunk(D) * esize <= 256 ? 128 : 64;
 }
 constexpr int key_cap(int kb) { return kb + 48; }
+
+// bf16 key pass: words per staged row (Q and dO of the chunk as f16 head
+// pairs, plus a 4-word pad against bank conflicts).
+constexpr int key_row_words(int G, int D) { return 2 * key_chunk(D) * ((G + 1) / 2) + 4; }
+
+// Rows per stage of the bf16 key pass.  As many as let 8 waves per CU share
+// the 160 KiB of LDS (a stage then spans about 20 rows of slot offsets for
+// the page-1 shapes), but at least the block plus 12 rows (a window of 10
+// and the interpolation tap in one stage) and at most the block plus 64.
+inline int key_h16_cap(int kb, int G, int D, int n_rungs) {
+  const int nw = kb / 64;
+  const int budget = 163840 * nw / 8 - nw * n_rungs * 4;
+  int cap = budget / (4 * key_row_words(G, D));
+  if (cap < kb + 12) cap = kb + 12;
+  if (cap > kb + 64) cap = kb + 64;
+  return cap;
+}
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(BwdArgs a, SlotTable st) {
@@ -422,6 +440,287 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
   }
 }
 
+// bf16 tensors: the same key pass with f16 operands.  The staged query rows
+// hold Q and dO of the chunk as f16 with the heads interleaved in pairs
+// (word [hp][x] = (head 2hp, head 2hp+1) of dim x), so the head sums
+// yk[x] = sum_h dS_h q_h[x] and yv[x] = sum_h p_h dO_h[x] are one
+// v_dot2c_f32_f16 per head pair and dim, accumulated in fp32; dS and p enter
+// as f16 pairs.  Rotation, the dK/dV accumulation and dd stay in fp32.
+template <int D, int G>
+__global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs a, SlotTable st) {
+  constexpr int KB = key_block(2, G, D);
+  constexpr int KC = key_chunk(D);
+  constexpr int NCH = D / KC;
+  constexpr int GW = (G + 1) / 2;  // head pairs
+  constexpr int PW = KC * GW;      // words per Q (or dO) part of a staged row
+  constexpr int RW = key_row_words(G, D);
+  constexpr int XH = KC / 8;       // 8-dim pieces per head chunk
+  constexpr int PPR = 2 * GW * XH; // staging pieces per row
+  constexpr int NW = KB / 64;
+  static_assert(KC % 8 == 0, "8-dim pieces");
+  // Dynamic LDS: a.kcap staged rows of RW words, then NW x n_rungs dd sums.
+  extern __shared__ __align__(16) uint32_t key_smem[];
+  uint32_t* Ws = key_smem;
+  float* ddl = reinterpret_cast<float*>(key_smem + size_t(a.kcap) * RW);
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int tile = xcd_tile(blockIdx.x, a.tiles);
+  const int c = tile % NCH;
+  const int rest = tile / NCH;
+  const int seq = rest / a.nblk;
+  const int blk = rest % a.nblk;
+  const int b = seq / a.hkv, g = seq % a.hkv;
+  const int n = a.n;
+  const int j0 = blk * KB;
+  const int j = j0 + tid;
+  const bool activej = j < n;
+
+  for (int t = tid; t < NW * a.n_rungs; t += KB) ddl[t] = 0.f;
+
+  const bf16_t* __restrict__ Q = static_cast<const bf16_t*>(a.q);
+  const bf16_t* __restrict__ dO = static_cast<const bf16_t*>(a.dout);
+  const size_t kv_off = (size_t(b) * n + j) * size_t(a.hkv) * D + size_t(g) * D + c * KC;
+
+  float kj[KC], vj[KC];
+  if (activej) {
+    load_vec<KC>(static_cast<const bf16_t*>(a.k) + kv_off, kj);
+    load_vec<KC>(static_cast<const bf16_t*>(a.v) + kv_off, vj);
+  } else {
+#pragma unroll
+    for (int x = 0; x < KC; ++x) kj[x] = vj[x] = 0.f;
+  }
+  float dk[KC], dv[KC];
+#pragma unroll
+  for (int x = 0; x < KC; ++x) dk[x] = dv[x] = 0.f;
+
+  const int S = st.count;
+  auto taps_of = [&](int sj) { return (st.frac[sj] > 0.f || st.rung[sj] >= 0) ? 2 : 1; };
+  // p, dp and Dvec of one (slot, tap) step, loaded without a branch: the row
+  // is clamped to n - 1, and every clamped row is one the query pass wrote
+  // (a slot is only reached while j0 + lo <= n - 1).  Steps past the end or
+  // with query j + lo + tap >= n are masked where they are used.
+  const float* __restrict__ Pseq = a.P + size_t(seq) * a.S * n * G;
+  const float* __restrict__ dPseq = a.dP + size_t(seq) * a.S * n * G;
+  const float* __restrict__ Dseq = a.Dvec + size_t(seq) * n * G;
+  auto load_step = [&](int sj, int tap, float (&pg)[G], float (&dpg)[G], float (&dvg)[G]) {
+    const int sc = sj < S ? sj : S - 1;
+    const int i = min(j + min(st.lo[sc], n) + tap, n - 1);
+    const size_t widx = (size_t(sc) * n + i) * G;
+    load_vec<G>(Pseq + widx, pg);
+    load_vec<G>(dPseq + widx, dpg);
+    load_vec<G>(Dseq + size_t(i) * G, dvg);
+  };
+  auto next_step = [&](int& sj, int& tap) {
+    if (sj >= S) return;
+    if (tap + 1 < taps_of(sj)) {
+      ++tap;
+    } else {
+      ++sj;
+      tap = 0;
+    }
+  };
+
+  // Two-deep prefetch along the (slot, tap) sequence, straight across stage
+  // boundaries.
+  float pA[G], dpA[G], dvA[G], pB[G], dpB[G], dvB[G];
+  int fs = 0, ft = 0;  // the step the B buffers will be loaded for
+  if (S > 0) {
+    load_step(0, 0, pA, dpA, dvA);
+    next_step(fs, ft);
+    load_step(fs, ft, pB, dpB, dvB);
+    next_step(fs, ft);
+  }
+  const int kcap = a.kcap;
+  int s = 0;
+  while (s < S) {
+    const int lo0 = st.lo[s];
+    if (j0 + lo0 > n - 1) break;
+    int lomax = lo0;
+    int e = s;
+    while (e < S) {
+      const int le = st.lo[e];
+      if (j0 + le > n - 1 || le - lo0 + KB + 1 > kcap) break;
+      lomax = le;
+      ++e;
+    }
+    const int r0 = j0 + lo0;
+    const int nrows = min(lomax - lo0 + KB + 1, n - r0);
+
+    __syncthreads();
+
+    // Batches of SB pieces per thread: all their global loads are issued
+    // before the first conversion.
+    constexpr int SB = 4;
+    const int total = nrows * PPR;
+    for (int t0 = tid; t0 < total; t0 += SB * KB) {
+      uint4 u0[SB], u1[SB];
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int t = t0 + u * KB;
+        u0[u] = u1[u] = make_uint4(0, 0, 0, 0);
+        if (t < total) {
+          const int row = t / PPR, pc = t % PPR;
+          const int which = pc / (GW * XH);
+          const int hp = (pc / XH) % GW;
+          const int xh = pc % XH;
+          const bf16_t* src = (which ? dO : Q) +
+                              ((size_t(b) * n + r0 + row) * a.hq + size_t(g) * G + 2 * hp) * D + c * KC + xh * 8;
+          u0[u] = *reinterpret_cast<const uint4*>(src);
+          if (2 * hp + 1 < G) u1[u] = *reinterpret_cast<const uint4*>(src + D);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const int t = t0 + u * KB;
+        if (t < total) {
+          const int row = t / PPR, pc = t % PPR;
+          const int which = pc / (GW * XH);
+          const int hp = (pc / XH) % GW;
+          const int xh = pc % XH;
+          const uint32_t e0[4] = {u0[u].x, u0[u].y, u0[u].z, u0[u].w};
+          const uint32_t e1[4] = {u1[u].x, u1[u].y, u1[u].z, u1[u].w};
+          uint32_t wv[8];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            wv[2 * x] = pack_h2(bf16_lo(e0[x]), bf16_lo(e1[x]));
+            wv[2 * x + 1] = pack_h2(bf16_hi(e0[x]), bf16_hi(e1[x]));
+          }
+          uint32_t* dst = Ws + row * RW + which * PW + hp * KC + xh * 8;
+          *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+          *reinterpret_cast<uint4*>(dst + 4) = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+        }
+      }
+    }
+    __syncthreads();
+
+    for (int sj = s; sj < e; ++sj) {
+      const int lo = st.lo[sj];
+      const float w = st.frac[sj];
+      const int rung = st.rung[sj];
+      const int ntaps = taps_of(sj);
+      float ddacc = 0.f;
+      for (int tap = 0; tap < ntaps; ++tap) {
+        float pg[G], dpg[G], dvg[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          pg[h] = pA[h];
+          dpg[h] = dpA[h];
+          dvg[h] = dvA[h];
+          pA[h] = pB[h];
+          dpA[h] = dpB[h];
+          dvA[h] = dvB[h];
+        }
+        load_step(fs, ft, pB, dpB, dvB);  // two steps ahead
+        next_step(fs, ft);
+
+        const int delta = lo + tap;
+        const float wt = tap ? w : 1.f - w;
+        // Query j + delta; the query pass stored p = 0 where the slot has no
+        // row for it.  Masked steps read staged row 0 with zero weights.
+        const bool valid = j + delta < n;
+        const int lrow = valid ? j + delta - r0 : 0;
+        uint32_t dsp[GW], pp[GW];
+#pragma unroll
+        for (int hp = 0; hp < GW; ++hp) {
+          const int h0 = 2 * hp, h1 = 2 * hp + 1 < G ? 2 * hp + 1 : 2 * hp;
+          const float m1 = 2 * hp + 1 < G ? pg[h1] : 0.f;
+          const uint32_t ds_ = pack_h2(a.scale * pg[h0] * (dpg[h0] - dvg[h0]), a.scale * m1 * (dpg[h1] - dvg[h1]));
+          const uint32_t p_ = pack_h2(pg[h0], m1);
+          dsp[hp] = valid ? ds_ : 0u;
+          pp[hp] = valid ? p_ : 0u;
+        }
+        const uint32_t* rowp = Ws + lrow * RW;
+        // yk[x] = sum_h dS_h q_h[x] (unrotated frame of query i)
+        float yk[KC];
+        {
+          uint32_t qw[KC];
+          load_words<KC>(rowp, qw);
+#pragma unroll
+          for (int x = 0; x < KC; ++x) yk[x] = dot2_h(dsp[0], qw[x], 0.f);
+#pragma unroll
+          for (int hp = 1; hp < GW; ++hp) {
+            load_words<KC>(rowp + hp * KC, qw);
+#pragma unroll
+            for (int x = 0; x < KC; ++x) yk[x] = dot2_h(dsp[hp], qw[x], yk[x]);
+          }
+        }
+        // dK gathers R(delta) yk (relative rotation into key j's frame)
+        float cs[KC];
+        if (a.rope) {
+          load_vec<KC>(a.rope + size_t(valid ? delta : 0) * D + c * KC, cs);
+        } else {
+#pragma unroll
+          for (int x = 0; x < KC; x += 2) {
+            cs[x] = 1.f;
+            cs[x + 1] = 0.f;
+          }
+        }
+        if (rung < 0) {
+          // window slot: weight 1, no offset gradient; rotation fused into
+          // the dK update and the dV head sums chained into dV.
+#pragma unroll
+          for (int x = 0; x < KC; x += 2) {
+            const float c_ = cs[x], s_ = cs[x + 1];
+            dk[x] = fmaf(yk[x], c_, fmaf(-yk[x + 1], s_, dk[x]));
+            dk[x + 1] = fmaf(yk[x], s_, fmaf(yk[x + 1], c_, dk[x + 1]));
+          }
+#pragma unroll
+          for (int hp = 0; hp < GW; ++hp) {
+            uint32_t ow[KC];
+            load_words<KC>(rowp + PW + hp * KC, ow);
+#pragma unroll
+            for (int x = 0; x < KC; ++x) dv[x] = dot2_h(pp[hp], ow[x], dv[x]);
+          }
+        } else {
+          float yv[KC];
+          {
+            uint32_t ow[KC];
+            load_words<KC>(rowp + PW, ow);
+#pragma unroll
+            for (int x = 0; x < KC; ++x) yv[x] = dot2_h(pp[0], ow[x], 0.f);
+#pragma unroll
+            for (int hp = 1; hp < GW; ++hp) {
+              load_words<KC>(rowp + PW + hp * KC, ow);
+#pragma unroll
+              for (int x = 0; x < KC; ++x) yv[x] = dot2_h(pp[hp], ow[x], yv[x]);
+            }
+          }
+          float part = 0.f;
+#pragma unroll
+          for (int x = 0; x < KC; x += 2) {
+            const float c_ = cs[x], s_ = cs[x + 1];
+            const float r0_ = yk[x] * c_ - yk[x + 1] * s_;
+            const float r1_ = yk[x] * s_ + yk[x + 1] * c_;
+            dk[x] = fmaf(wt, r0_, dk[x]);
+            dk[x + 1] = fmaf(wt, r1_, dk[x + 1]);
+            dv[x] = fmaf(wt, yv[x], dv[x]);
+            dv[x + 1] = fmaf(wt, yv[x + 1], dv[x + 1]);
+            part = fmaf(r0_, kj[x], fmaf(r1_, kj[x + 1], fmaf(yv[x], vj[x], fmaf(yv[x + 1], vj[x + 1], part))));
+          }
+          ddacc += tap ? part : -part;
+        }
+      }
+      if (rung >= 0) {
+        const float tot = wave_sum(ddacc);
+        if ((tid & 63) == 0) ddl[wave * a.n_rungs + rung] += tot;
+      }
+    }
+    s = e;
+  }
+  if (activej) {
+    store_vec<KC>(static_cast<bf16_t*>(a.dk) + kv_off, dk);
+    store_vec<KC>(static_cast<bf16_t*>(a.dv) + kv_off, dv);
+  }
+  __syncthreads();
+  for (int r = tid; r < a.n_rungs; r += KB) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) acc += ddl[w * a.n_rungs + r];
+    a.dd_part[size_t(tile) * a.n_rungs + r] = acc;
+  }
+}
+
 struct ReduceArgs {
   const float* dd_part;
   float* dd;
@@ -504,7 +803,13 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
   BwdArgs a = a0;
   a.nblk = (a.n + KB - 1) / KB;
   a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk(D));
-  hipLaunchKernelGGL((bwd_key_kernel<T, D, G>), dim3(a.tiles), dim3(KB), 0, st, a, t);
+  if constexpr (sizeof(T) == 2) {
+    a.kcap = key_h16_cap(KB, G, D, t.n_rungs);
+    const size_t lds = (size_t(a.kcap) * key_row_words(G, D) + size_t(KB / 64) * t.n_rungs) * 4;
+    hipLaunchKernelGGL((bwd_key_h16_kernel<D, G>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+  } else {
+    hipLaunchKernelGGL((bwd_key_kernel<T, D, G>), dim3(a.tiles), dim3(KB), 0, st, a, t);
+  }
   return int(hipGetLastError());
 }
 
