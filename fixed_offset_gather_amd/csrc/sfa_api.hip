@@ -62,12 +62,12 @@ int build_slots(const sfa_attn* a, SlotTable* t, bool merge) {
   struct S {
     int32_t lo;
     float frac;
-    int16_t rung;
+    int32_t rung;
   };
   std::vector<S> v;
   v.reserve(size_t(a->window) + 1 + size_t(a->n_off));
   for (int s = 0; s <= a->window; ++s) v.push_back({s, 0.f, -1});
-  for (int k = 0; k < a->n_off; ++k) v.push_back({a->off_lo[k], a->off_frac[k], int16_t(k)});
+  for (int k = 0; k < a->n_off; ++k) v.push_back({a->off_lo[k], a->off_frac[k], int32_t(k)});
   std::stable_sort(v.begin(), v.end(), [](const S& x, const S& y) { return x.lo < y.lo; });
   std::memset(t, 0, sizeof(*t));
   t->n_rungs = a->n_off;

@@ -436,7 +436,7 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) acc += ddl[w][r];
-    a.dd_part[size_t(tile) * a.n_rungs + r] = acc;
+    a.dd_part[size_t(r) * a.tiles + tile] = acc;
   }
 }
 
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
 // yk[x] = sum_h dS_h q_h[x] and yv[x] = sum_h p_h dO_h[x] are one
 // v_dot2c_f32_f16 per head pair and dim, accumulated in fp32; dS and p enter
 // as f16 pairs.  Rotation, the dK/dV accumulation and dd stay in fp32.
-template <int D, int G>
+template <int D, int G, bool ROPE>
 __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs a, SlotTable st) {
   constexpr int KB = key_block(2, G, D);
   constexpr int KC = key_chunk(D);
@@ -511,25 +511,42 @@ __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs
     load_vec<G>(dPseq + widx, dpg);
     load_vec<G>(Dseq + size_t(i) * G, dvg);
   };
-  auto next_step = [&](int& sj, int& tap) {
-    if (sj >= S) return;
-    if (tap + 1 < taps_of(sj)) {
-      ++tap;
-    } else {
-      ++sj;
-      tap = 0;
+  // f16 weights of a step from its p, dp and Dvec: dS pairs, then p pairs;
+  // zero for a masked step (query j + lo + tap beyond the sequence).
+  auto convert = [&](int sj, int tap, const float (&pg)[G], const float (&dpg)[G], const float (&dvg)[G],
+                     uint32_t (&wts)[2 * GW]) {
+    const bool valid = sj < S && j + min(st.lo[sj < S ? sj : 0], n) + tap < n;
+#pragma unroll
+    for (int hp = 0; hp < GW; ++hp) {
+      const int h0 = 2 * hp, h1 = 2 * hp + 1 < G ? 2 * hp + 1 : 2 * hp;
+      const float m1 = 2 * hp + 1 < G ? pg[h1] : 0.f;
+      const uint32_t ds_ = pack_h2(a.scale * pg[h0] * (dpg[h0] - dvg[h0]), a.scale * m1 * (dpg[h1] - dvg[h1]));
+      const uint32_t p_ = pack_h2(pg[h0], m1);
+      wts[hp] = valid ? ds_ : 0u;
+      wts[GW + hp] = valid ? p_ : 0u;
     }
   };
+  auto next_step = [&](int& sj, int& tap) {
+    const int nt = sj < S ? taps_of(sj < S ? sj : 0) : 0;
+    const bool adv = tap + 1 >= nt;
+    sj = adv ? min(sj + 1, S) : sj;
+    tap = adv ? 0 : tap + 1;
+  };
 
-  // Two-deep prefetch along the (slot, tap) sequence, straight across stage
-  // boundaries.
-  float pA[G], dpA[G], dvA[G], pB[G], dpB[G], dvB[G];
-  int fs = 0, ft = 0;  // the step the B buffers will be loaded for
+  // Software pipeline along the (slot, tap) sequence, straight across stage
+  // boundaries: wts holds the f16 weights of the step being computed and
+  // rp/rdp/rdv the raw loads of the step after it (fs, ft).  The end of each
+  // step converts those into the next weights and only then reuses the
+  // registers for the loads of the step after that, so every load has a
+  // whole step to arrive.
+  uint32_t wts[2 * GW] = {};
+  float rp[G], rdp[G], rdv[G];
+  int fs = 0, ft = 0;
   if (S > 0) {
-    load_step(0, 0, pA, dpA, dvA);
+    load_step(0, 0, rp, rdp, rdv);
+    convert(0, 0, rp, rdp, rdv, wts);
     next_step(fs, ft);
-    load_step(fs, ft, pB, dpB, dvB);
-    next_step(fs, ft);
+    load_step(fs, ft, rp, rdp, rdv);
   }
   const int kcap = a.kcap;
   int s = 0;
@@ -549,46 +566,49 @@ __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs
 
     __syncthreads();
 
-    // Batches of SB pieces per thread: all their global loads are issued
-    // before the first conversion.
-    constexpr int SB = 4;
-    const int total = nrows * PPR;
-    for (int t0 = tid; t0 < total; t0 += SB * KB) {
-      uint4 u0[SB], u1[SB];
+    // Thread t always stages piece t % PPR of a row (KB is a multiple of
+    // PPR), rows t / PPR, t / PPR + KB / PPR, ...  Batches of SB pieces: all
+    // their global loads are issued before the first conversion.
+    {
+      static_assert(KB % PPR == 0, "pieces per row divide the block");
+      constexpr int SB = 4;
+      constexpr int RSTEP = KB / PPR;
+      const int pc = tid % PPR;
+      const int which = pc / (GW * XH);
+      const int hp = (pc / XH) % GW;
+      const int xh = pc % XH;
+      const bool pair = 2 * hp + 1 < G;
+      const size_t rstride = size_t(a.hq) * D;
+      const bf16_t* src0 = (which ? dO : Q) + (size_t(b) * n + r0) * rstride + (size_t(g) * G + 2 * hp) * D + c * KC + xh * 8;
+      uint32_t* dst0 = Ws + which * PW + hp * KC + xh * 8;
+      for (int row0 = tid / PPR; row0 < nrows; row0 += SB * RSTEP) {
+        uint4 u0[SB], u1[SB];
 #pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        const int t = t0 + u * KB;
-        u0[u] = u1[u] = make_uint4(0, 0, 0, 0);
-        if (t < total) {
-          const int row = t / PPR, pc = t % PPR;
-          const int which = pc / (GW * XH);
-          const int hp = (pc / XH) % GW;
-          const int xh = pc % XH;
-          const bf16_t* src = (which ? dO : Q) +
-                              ((size_t(b) * n + r0 + row) * a.hq + size_t(g) * G + 2 * hp) * D + c * KC + xh * 8;
-          u0[u] = *reinterpret_cast<const uint4*>(src);
-          if (2 * hp + 1 < G) u1[u] = *reinterpret_cast<const uint4*>(src + D);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        const int t = t0 + u * KB;
-        if (t < total) {
-          const int row = t / PPR, pc = t % PPR;
-          const int which = pc / (GW * XH);
-          const int hp = (pc / XH) % GW;
-          const int xh = pc % XH;
-          const uint32_t e0[4] = {u0[u].x, u0[u].y, u0[u].z, u0[u].w};
-          const uint32_t e1[4] = {u1[u].x, u1[u].y, u1[u].z, u1[u].w};
-          uint32_t wv[8];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            wv[2 * x] = pack_h2(bf16_lo(e0[x]), bf16_lo(e1[x]));
-            wv[2 * x + 1] = pack_h2(bf16_hi(e0[x]), bf16_hi(e1[x]));
+        for (int u = 0; u < SB; ++u) {
+          const int row = row0 + u * RSTEP;
+          u0[u] = u1[u] = make_uint4(0, 0, 0, 0);
+          if (row < nrows) {
+            const bf16_t* src = src0 + size_t(row) * rstride;
+            u0[u] = *reinterpret_cast<const uint4*>(src);
+            if (pair) u1[u] = *reinterpret_cast<const uint4*>(src + D);
           }
-          uint32_t* dst = Ws + row * RW + which * PW + hp * KC + xh * 8;
-          *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-          *reinterpret_cast<uint4*>(dst + 4) = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const int row = row0 + u * RSTEP;
+          if (row < nrows) {
+            const uint32_t e0[4] = {u0[u].x, u0[u].y, u0[u].z, u0[u].w};
+            const uint32_t e1[4] = {u1[u].x, u1[u].y, u1[u].z, u1[u].w};
+            uint32_t wv[8];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              wv[2 * x] = pack_h2(bf16_lo(e0[x]), bf16_lo(e1[x]));
+              wv[2 * x + 1] = pack_h2(bf16_hi(e0[x]), bf16_hi(e1[x]));
+            }
+            uint32_t* dst = dst0 + row * RW;
+            *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            *reinterpret_cast<uint4*>(dst + 4) = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+          }
         }
       }
     }
@@ -601,35 +621,14 @@ __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs
       const int ntaps = taps_of(sj);
       float ddacc = 0.f;
       for (int tap = 0; tap < ntaps; ++tap) {
-        float pg[G], dpg[G], dvg[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          pg[h] = pA[h];
-          dpg[h] = dpA[h];
-          dvg[h] = dvA[h];
-          pA[h] = pB[h];
-          dpA[h] = dpB[h];
-          dvA[h] = dvB[h];
-        }
-        load_step(fs, ft, pB, dpB, dvB);  // two steps ahead
-        next_step(fs, ft);
-
         const int delta = lo + tap;
         const float wt = tap ? w : 1.f - w;
         // Query j + delta; the query pass stored p = 0 where the slot has no
         // row for it.  Masked steps read staged row 0 with zero weights.
         const bool valid = j + delta < n;
         const int lrow = valid ? j + delta - r0 : 0;
-        uint32_t dsp[GW], pp[GW];
-#pragma unroll
-        for (int hp = 0; hp < GW; ++hp) {
-          const int h0 = 2 * hp, h1 = 2 * hp + 1 < G ? 2 * hp + 1 : 2 * hp;
-          const float m1 = 2 * hp + 1 < G ? pg[h1] : 0.f;
-          const uint32_t ds_ = pack_h2(a.scale * pg[h0] * (dpg[h0] - dvg[h0]), a.scale * m1 * (dpg[h1] - dvg[h1]));
-          const uint32_t p_ = pack_h2(pg[h0], m1);
-          dsp[hp] = valid ? ds_ : 0u;
-          pp[hp] = valid ? p_ : 0u;
-        }
+        const uint32_t* dsp = wts;
+        const uint32_t* pp = wts + GW;
         const uint32_t* rowp = Ws + lrow * RW;
         // yk[x] = sum_h dS_h q_h[x] (unrotated frame of query i)
         float yk[KC];
@@ -647,8 +646,13 @@ __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs
         }
         // dK gathers R(delta) yk (relative rotation into key j's frame)
         float cs[KC];
-        if (a.rope) {
-          load_vec<KC>(a.rope + size_t(valid ? delta : 0) * D + c * KC, cs);
+        if constexpr (ROPE) {
+          // One row for the whole wave (masked lanes carry zero weights),
+          // read through the constant address space as a scalar load.
+          using crow_t = const __attribute__((address_space(4))) float*;
+          const crow_t rr = (crow_t)(a.rope + size_t(min(delta, n - 1)) * D + c * KC);
+#pragma unroll
+          for (int x = 0; x < KC; ++x) cs[x] = rr[x];
         } else {
 #pragma unroll
           for (int x = 0; x < KC; x += 2) {
@@ -656,50 +660,40 @@ __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs
             cs[x + 1] = 0.f;
           }
         }
-        if (rung < 0) {
-          // window slot: weight 1, no offset gradient; rotation fused into
-          // the dK update and the dV head sums chained into dV.
+        // Window slots run the same arithmetic with weight 1; their dd sum
+        // is never stored.  One straight-line body keeps the registers put.
+        float yv[KC];
+        {
+          uint32_t ow[KC];
+          load_words<KC>(rowp + PW, ow);
 #pragma unroll
-          for (int x = 0; x < KC; x += 2) {
-            const float c_ = cs[x], s_ = cs[x + 1];
-            dk[x] = fmaf(yk[x], c_, fmaf(-yk[x + 1], s_, dk[x]));
-            dk[x + 1] = fmaf(yk[x], s_, fmaf(yk[x + 1], c_, dk[x + 1]));
-          }
+          for (int x = 0; x < KC; ++x) yv[x] = dot2_h(pp[0], ow[x], 0.f);
 #pragma unroll
-          for (int hp = 0; hp < GW; ++hp) {
-            uint32_t ow[KC];
+          for (int hp = 1; hp < GW; ++hp) {
             load_words<KC>(rowp + PW + hp * KC, ow);
 #pragma unroll
-            for (int x = 0; x < KC; ++x) dv[x] = dot2_h(pp[hp], ow[x], dv[x]);
+            for (int x = 0; x < KC; ++x) yv[x] = dot2_h(pp[hp], ow[x], yv[x]);
           }
-        } else {
-          float yv[KC];
-          {
-            uint32_t ow[KC];
-            load_words<KC>(rowp + PW, ow);
-#pragma unroll
-            for (int x = 0; x < KC; ++x) yv[x] = dot2_h(pp[0], ow[x], 0.f);
-#pragma unroll
-            for (int hp = 1; hp < GW; ++hp) {
-              load_words<KC>(rowp + PW + hp * KC, ow);
-#pragma unroll
-              for (int x = 0; x < KC; ++x) yv[x] = dot2_h(pp[hp], ow[x], yv[x]);
-            }
-          }
-          float part = 0.f;
-#pragma unroll
-          for (int x = 0; x < KC; x += 2) {
-            const float c_ = cs[x], s_ = cs[x + 1];
-            const float r0_ = yk[x] * c_ - yk[x + 1] * s_;
-            const float r1_ = yk[x] * s_ + yk[x + 1] * c_;
-            dk[x] = fmaf(wt, r0_, dk[x]);
-            dk[x + 1] = fmaf(wt, r1_, dk[x + 1]);
-            dv[x] = fmaf(wt, yv[x], dv[x]);
-            dv[x + 1] = fmaf(wt, yv[x + 1], dv[x + 1]);
-            part = fmaf(r0_, kj[x], fmaf(r1_, kj[x + 1], fmaf(yv[x], vj[x], fmaf(yv[x + 1], vj[x + 1], part))));
-          }
-          ddacc += tap ? part : -part;
         }
+        float part = 0.f;
+#pragma unroll
+        for (int x = 0; x < KC; x += 2) {
+          const float c_ = cs[x], s_ = cs[x + 1];
+          const float r0_ = yk[x] * c_ - yk[x + 1] * s_;
+          const float r1_ = yk[x] * s_ + yk[x + 1] * c_;
+          dk[x] = fmaf(wt, r0_, dk[x]);
+          dk[x + 1] = fmaf(wt, r1_, dk[x + 1]);
+          dv[x] = fmaf(wt, yv[x], dv[x]);
+          dv[x + 1] = fmaf(wt, yv[x + 1], dv[x + 1]);
+          part = fmaf(r0_, kj[x], fmaf(r1_, kj[x + 1], fmaf(yv[x], vj[x], fmaf(yv[x + 1], vj[x + 1], part))));
+        }
+        ddacc += tap ? part : -part;
+
+        // weights of the next step, then the loads of the one after it
+        convert(fs, ft, rp, rdp, rdv, wts);
+        __builtin_amdgcn_sched_barrier(0);
+        next_step(fs, ft);
+        load_step(fs, ft, rp, rdp, rdv);
       }
       if (rung >= 0) {
         const float tot = wave_sum(ddacc);
@@ -717,7 +711,7 @@ __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) acc += ddl[w * a.n_rungs + r];
-    a.dd_part[size_t(tile) * a.n_rungs + r] = acc;
+    a.dd_part[size_t(r) * a.tiles + tile] = acc;
   }
 }
 
@@ -730,10 +724,11 @@ struct ReduceArgs {
   float base[SFA_MAX_OFFSETS];
 };
 
-// One workgroup of 16 waves.  Wave w reduces rungs w, w+16, ...: lane l adds
-// the partial sums of blocks l, l+64, ... in block order, then the wave adds
-// its 64 lanes in a fixed DPP/shuffle tree.  The result does not depend on
-// timing.
+// One workgroup of 16 waves.  The partials are stored rung-major
+// ([rung][block]), so wave w reduces rungs w, w+16, ... with coalesced
+// loads: lane l adds the partials of blocks l, l+64, ... in block order,
+// then the wave adds its 64 lanes in a fixed DPP/shuffle tree.  The result
+// does not depend on timing.
 constexpr int kReduceThreads = 1024;
 
 __global__ __launch_bounds__(kReduceThreads) void bwd_reduce_kernel(ReduceArgs a) {
@@ -742,9 +737,16 @@ __global__ __launch_bounds__(kReduceThreads) void bwd_reduce_kernel(ReduceArgs a
   const int wave = threadIdx.x >> 6;
   for (int r = wave; r < a.n_rungs; r += kReduceThreads / 64) {
     float acc = 0.f;
+    const float* row = a.dd_part + size_t(r) * a.blocks;
     int blk = lane;
-#pragma unroll 4
-    for (; blk < a.blocks; blk += 64) acc += a.dd_part[size_t(blk) * a.n_rungs + r];
+    for (; blk + 7 * 64 < a.blocks; blk += 8 * 64) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = row[blk + u * 64];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += x[u];
+    }
+    for (; blk < a.blocks; blk += 64) acc += row[blk];
     const float tot = wave_sum(acc);
     if (lane == 0) {
       sdd[r] = tot;
@@ -806,7 +808,10 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
     a.kcap = key_h16_cap(KB, G, D, t.n_rungs);
     const size_t lds = (size_t(a.kcap) * key_row_words(G, D) + size_t(KB / 64) * t.n_rungs) * 4;
-    hipLaunchKernelGGL((bwd_key_h16_kernel<D, G>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+    if (a.rope)
+      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, true>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+    else
+      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, false>), dim3(a.tiles), dim3(KB), lds, st, a, t);
   } else {
     hipLaunchKernelGGL((bwd_key_kernel<T, D, G>), dim3(a.tiles), dim3(KB), 0, st, a, t);
   }

@@ -24,7 +24,7 @@ struct SlotTable {
   int32_t lo[SFA_MAX_SLOTS];
   float frac[SFA_MAX_SLOTS];
   float mult[SFA_MAX_SLOTS];
-  int16_t rung[SFA_MAX_SLOTS];
+  int32_t rung[SFA_MAX_SLOTS];  // 32-bit: kernels read it with scalar loads
 };
 
 // Kernel launch parameters derived from sfa_attn after validation.
@@ -48,10 +48,10 @@ int launch_fwd_edges(const Problem& p, const int32_t* edges,
                      void* stream);
 
 struct BwdWorkspace {
-  float* p;        // [B][Hkv][S][n][G] softmax probabilities of valid slots
-  float* dp;       // [B][Hkv][S][n][G] dO . v~ of valid slots
+  float* p;        // [B][Hkv][S][n][G] softmax probabilities (0 where a slot has no row)
+  float* dp;       // [B][Hkv][S][n][G] dO . v~
   float* dvec;     // [B][Hkv][n][G] rowsum(dO * O) = sum_slots p dp
-  float* dd_part;  // [blocks][n_rungs] per-block partial sums of dL/dd_k
+  float* dd_part;  // [n_rungs][blocks] per-block partial sums of dL/dd_k
   size_t bytes;
   int blocks;
 };
