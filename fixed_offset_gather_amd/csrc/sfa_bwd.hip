@@ -249,18 +249,20 @@ constexpr int key_block(int esize, int G, int D) {
 }
 constexpr int key_cap(int kb) { return kb + 48; }
 
-// bf16 key pass: words per staged row (Q and dO of the chunk as f16 head
-// pairs, plus a 4-word pad against bank conflicts).
-constexpr int key_row_words(int G, int D) { return 2 * key_chunk(D) * ((G + 1) / 2) + 4; }
+// bf16 key pass: two kernels of 128 keys per workgroup, one for dK (staging
+// Q) and one for dV (staging dO).  Words per staged row: the chunk of every
+// head as f16 head pairs, plus a 4-word pad against bank conflicts.
+constexpr int kKeyBlockH16 = 128;
+constexpr int key_half_row_words(int G, int D) { return key_chunk(D) * ((G + 1) / 2) + 4; }
 
-// Rows per stage of the bf16 key pass.  As many as let 8 waves per CU share
-// the 160 KiB of LDS (a stage then spans about 20 rows of slot offsets for
-// the page-1 shapes), but at least the block plus 12 rows (a window of 10
-// and the interpolation tap in one stage) and at most the block plus 64.
-inline int key_h16_cap(int kb, int G, int D, int n_rungs) {
-  const int nw = kb / 64;
-  const int budget = 163840 * nw / 8 - nw * n_rungs * 4;
-  int cap = budget / (4 * key_row_words(G, D));
+// Rows per stage of a bf16 key-pass half.  As many as let 16 waves per CU
+// share the 160 KiB of LDS, but at least the block plus 12 rows (a window
+// of 10 and the interpolation tap in one stage) and at most the block plus
+// 64.
+inline int key_half_cap(int G, int D, int n_rungs) {
+  constexpr int kb = kKeyBlockH16, nw = kb / 64;
+  const int budget = 163840 * nw / 16 - nw * n_rungs * 4;
+  int cap = budget / (4 * key_half_row_words(G, D));
   if (cap < kb + 12) cap = kb + 12;
   if (cap > kb + 64) cap = kb + 64;
   return cap;
@@ -440,24 +442,31 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
   }
 }
 
-// bf16 tensors: the same key pass with f16 operands.  The staged query rows
-// hold Q and dO of the chunk as f16 with the heads interleaved in pairs
-// (word [hp][x] = (head 2hp, head 2hp+1) of dim x), so the head sums
-// yk[x] = sum_h dS_h q_h[x] and yv[x] = sum_h p_h dO_h[x] are one
-// v_dot2c_f32_f16 per head pair and dim, accumulated in fp32; dS and p enter
-// as f16 pairs.  Rotation, the dK/dV accumulation and dd stay in fp32.
-template <int D, int G, bool ROPE>
-__global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs a, SlotTable st) {
-  constexpr int KB = key_block(2, G, D);
+// bf16 tensors: the key pass with f16 operands, split into two kernels that
+// each stage half of a query row.  PART 0 (dK) stages q~ = R(i) q of the
+// chunk (rotated while staging) and gathers yk~ = sum_h dS_h q~_h; dK~ =
+// sum w yk~ is rotated back once, dK = R(j)^T dK~, and the key term of dd_k
+// is yk~ . k~_j with k~_j = R(j) k_j (the relative rotation R(i - j) =
+// R(j)^T R(i) never has to be formed per step).  PART 1 (dV) stages dO and
+// gathers yv = sum_h p_h dO_h: dV += w yv, and the value term of dd_k is
+// yv . v_j.  A staged row holds the chunk of every head as f16 with the
+// heads interleaved in pairs (word [hp][x] = (head 2hp, head 2hp+1) of dim
+// x), so each head sum is one v_dot2c_f32_f16 per head pair and dim,
+// accumulated in fp32; dS and p enter as f16 pairs.  Half a row per kernel
+// halves the LDS and registers per wave, so four waves share a SIMD.
+// SMALL: at most 64 slots (one VGPR per slot-table column).
+template <int D, int G, int PART, bool SMALL>
+__global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, SlotTable st) {
+  constexpr int KB = kKeyBlockH16;
   constexpr int KC = key_chunk(D);
   constexpr int NCH = D / KC;
   constexpr int GW = (G + 1) / 2;  // head pairs
-  constexpr int PW = KC * GW;      // words per Q (or dO) part of a staged row
-  constexpr int RW = key_row_words(G, D);
+  constexpr int RW = key_half_row_words(G, D);
   constexpr int XH = KC / 8;       // 8-dim pieces per head chunk
-  constexpr int PPR = 2 * GW * XH; // staging pieces per row
+  constexpr int PPR = GW * XH;     // staging pieces per row
   constexpr int NW = KB / 64;
-  static_assert(KC % 8 == 0, "8-dim pieces");
+  constexpr int NQ = SMALL ? 1 : 3;  // VGPRs per slot-table column
+  static_assert(KC % 8 == 0 && KB % PPR == 0, "8-dim pieces, whole rows per pass");
   // Dynamic LDS: a.kcap staged rows of RW words, then NW x n_rungs dd sums.
   extern __shared__ __align__(16) uint32_t key_smem[];
   uint32_t* Ws = key_smem;
@@ -475,88 +484,133 @@ __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs
   const int j0 = blk * KB;
   const int j = j0 + tid;
   const bool activej = j < n;
+  const bool rope = PART == 0 && a.rope != nullptr;
 
   for (int t = tid; t < NW * a.n_rungs; t += KB) ddl[t] = 0.f;
 
-  const bf16_t* __restrict__ Q = static_cast<const bf16_t*>(a.q);
-  const bf16_t* __restrict__ dO = static_cast<const bf16_t*>(a.dout);
+  const bf16_t* __restrict__ X = static_cast<const bf16_t*>(PART == 0 ? a.q : a.dout);
   const size_t kv_off = (size_t(b) * n + j) * size_t(a.hkv) * D + size_t(g) * D + c * KC;
 
-  float kj[KC], vj[KC];
+  // k~_j = R(j) k_j (dK) or v_j (dV): the dd term's partner row
+  float own[KC];
   if (activej) {
-    load_vec<KC>(static_cast<const bf16_t*>(a.k) + kv_off, kj);
-    load_vec<KC>(static_cast<const bf16_t*>(a.v) + kv_off, vj);
+    load_vec<KC>(static_cast<const bf16_t*>(PART == 0 ? a.k : a.v) + kv_off, own);
+    if (rope) rotate_pairs<KC, 1>(own, a.rope + size_t(j) * D, c * KC);
   } else {
 #pragma unroll
-    for (int x = 0; x < KC; ++x) kj[x] = vj[x] = 0.f;
+    for (int x = 0; x < KC; ++x) own[x] = 0.f;
   }
-  float dk[KC], dv[KC];
+  float acc[KC];
 #pragma unroll
-  for (int x = 0; x < KC; ++x) dk[x] = dv[x] = 0.f;
+  for (int x = 0; x < KC; ++x) acc[x] = 0.f;
 
+  // The slot table lives in VGPRs for the loops (lane l holds slot l, then
+  // l + 64 and l + 128) and is read with v_readlane: no scalar memory access
+  // inside the loops, whose waits would also drain the LDS reads (both count
+  // on lgkmcnt, and scalar loads return out of order).
   const int S = st.count;
-  auto taps_of = [&](int sj) { return (st.frac[sj] > 0.f || st.rung[sj] >= 0) ? 2 : 1; };
-  // p, dp and Dvec of one (slot, tap) step, loaded without a branch: the row
-  // is clamped to n - 1, and every clamped row is one the query pass wrote
-  // (a slot is only reached while j0 + lo <= n - 1).  Steps past the end or
-  // with query j + lo + tap >= n are masked where they are used.
+  const int lane = tid & 63;
+  int vlo[NQ], vfr[NQ], vinfo[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int sl = q * 64 + lane;
+    const bool in = sl < S;
+    const int sc = in ? sl : 0;
+    const float fr = in ? st.frac[sc] : 0.f;
+    const int rg = in ? st.rung[sc] : -1;
+    vlo[q] = in ? min(st.lo[sc], n) : n;
+    vfr[q] = __float_as_int(fr);
+    // bits 0-15: rung + 1 (0 for a window slot); bit 16: a second tap
+    vinfo[q] = (rg + 1) | ((in && (fr > 0.f || rg >= 0)) ? 0x10000 : 0);
+  }
+  auto slot_i = [&](const int (&v)[NQ], int sj) {  // sj wave-uniform, < 64 * NQ
+    if constexpr (SMALL) {
+      return __builtin_amdgcn_readlane(v[0], sj);
+    } else {
+      const int l = sj & 63;
+      const int x0 = __builtin_amdgcn_readlane(v[0], l);
+      const int x1 = __builtin_amdgcn_readlane(v[1], l);
+      const int x2 = __builtin_amdgcn_readlane(v[2], l);
+      return sj < 64 ? x0 : (sj < 128 ? x1 : x2);
+    }
+  };
+
+  // p (and for dK dp and Dvec) of one (slot, tap) step, loaded without a
+  // branch: the row is clamped to n - 1, and every clamped row is one the
+  // query pass wrote (a slot is only reached while j0 + lo <= n - 1).  A
+  // step past the end reloads the last slot's rows; masked steps get zero
+  // weights in convert().
+  constexpr int NR = PART == 0 ? 3 : 1;
   const float* __restrict__ Pseq = a.P + size_t(seq) * a.S * n * G;
   const float* __restrict__ dPseq = a.dP + size_t(seq) * a.S * n * G;
   const float* __restrict__ Dseq = a.Dvec + size_t(seq) * n * G;
-  auto load_step = [&](int sj, int tap, float (&pg)[G], float (&dpg)[G], float (&dvg)[G]) {
-    const int sc = sj < S ? sj : S - 1;
-    const int i = min(j + min(st.lo[sc], n) + tap, n - 1);
+  // the prefetch cursor: step (fs, ft) and its slot's min(lo, n) and taps
+  int fs = 0, ft = 0, flo = 0, ftaps = 1;
+  auto load_step = [&](float (&raw)[NR][G]) {
+    const int sc = fs < S ? fs : S - 1;
+    const int i = min(j + flo + ft, n - 1);
     const size_t widx = (size_t(sc) * n + i) * G;
-    load_vec<G>(Pseq + widx, pg);
-    load_vec<G>(dPseq + widx, dpg);
-    load_vec<G>(Dseq + size_t(i) * G, dvg);
+    load_vec<G>(Pseq + widx, raw[0]);
+    if constexpr (PART == 0) {
+      load_vec<G>(dPseq + widx, raw[1]);
+      load_vec<G>(Dseq + size_t(i) * G, raw[2]);
+    }
   };
-  // f16 weights of a step from its p, dp and Dvec: dS pairs, then p pairs;
-  // zero for a masked step (query j + lo + tap beyond the sequence).
-  auto convert = [&](int sj, int tap, const float (&pg)[G], const float (&dpg)[G], const float (&dvg)[G],
-                     uint32_t (&wts)[2 * GW]) {
-    const bool valid = sj < S && j + min(st.lo[sj < S ? sj : 0], n) + tap < n;
+  // f16 weight pairs of the cursor's step: dS = scale p (dp - Dvec) for dK,
+  // p for dV; zero for a masked step.
+  auto convert = [&](const float (&raw)[NR][G], uint32_t (&wts)[GW]) {
+    const bool valid = fs < S && j + flo + ft < n;
 #pragma unroll
     for (int hp = 0; hp < GW; ++hp) {
       const int h0 = 2 * hp, h1 = 2 * hp + 1 < G ? 2 * hp + 1 : 2 * hp;
-      const float m1 = 2 * hp + 1 < G ? pg[h1] : 0.f;
-      const uint32_t ds_ = pack_h2(a.scale * pg[h0] * (dpg[h0] - dvg[h0]), a.scale * m1 * (dpg[h1] - dvg[h1]));
-      const uint32_t p_ = pack_h2(pg[h0], m1);
-      wts[hp] = valid ? ds_ : 0u;
-      wts[GW + hp] = valid ? p_ : 0u;
+      float w0 = raw[0][h0], w1 = 2 * hp + 1 < G ? raw[0][h1] : 0.f;
+      if constexpr (PART == 0) {
+        w0 = a.scale * w0 * (raw[1][h0] - raw[2][h0]);
+        w1 = a.scale * w1 * (raw[1][h1] - raw[2][h1]);
+      }
+      const uint32_t pk = pack_h2(w0, w1);
+      wts[hp] = valid ? pk : 0u;
     }
   };
-  auto next_step = [&](int& sj, int& tap) {
-    const int nt = sj < S ? taps_of(sj < S ? sj : 0) : 0;
-    const bool adv = tap + 1 >= nt;
-    sj = adv ? min(sj + 1, S) : sj;
-    tap = adv ? 0 : tap + 1;
+  // advance the cursor one step; it stays at (S, 0) once past the end
+  auto advance = [&]() {
+    if (ft + 1 < ftaps) {
+      ++ft;
+    } else if (fs < S) {
+      ++fs;
+      ft = 0;
+      if (fs < S) {
+        flo = slot_i(vlo, fs);
+        ftaps = (slot_i(vinfo, fs) >> 16) + 1;
+      }
+    }
   };
 
   // Software pipeline along the (slot, tap) sequence, straight across stage
-  // boundaries: wts holds the f16 weights of the step being computed and
-  // rp/rdp/rdv the raw loads of the step after it (fs, ft).  The end of each
-  // step converts those into the next weights and only then reuses the
-  // registers for the loads of the step after that, so every load has a
-  // whole step to arrive.
-  uint32_t wts[2 * GW] = {};
-  float rp[G], rdp[G], rdv[G];
-  int fs = 0, ft = 0;
+  // boundaries: wts holds the f16 weights of the step being computed and raw
+  // the loads of the cursor's step, the one after it.  The end of each step
+  // converts those into the next weights and only then reuses the registers
+  // for the loads of the step after that, so every load has a whole step to
+  // arrive.
+  uint32_t wts[GW] = {};
+  float raw[NR][G];
   if (S > 0) {
-    load_step(0, 0, rp, rdp, rdv);
-    convert(0, 0, rp, rdp, rdv, wts);
-    next_step(fs, ft);
-    load_step(fs, ft, rp, rdp, rdv);
+    flo = slot_i(vlo, 0);
+    ftaps = (slot_i(vinfo, 0) >> 16) + 1;
+    load_step(raw);
+    convert(raw, wts);
+    advance();
+    load_step(raw);
   }
   const int kcap = a.kcap;
   int s = 0;
   while (s < S) {
-    const int lo0 = st.lo[s];
+    const int lo0 = slot_i(vlo, s);
     if (j0 + lo0 > n - 1) break;
     int lomax = lo0;
     int e = s;
     while (e < S) {
-      const int le = st.lo[e];
+      const int le = slot_i(vlo, e);
       if (j0 + le > n - 1 || le - lo0 + KB + 1 > kcap) break;
       lomax = le;
       ++e;
@@ -566,31 +620,37 @@ __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs
 
     __syncthreads();
 
-    // Thread t always stages piece t % PPR of a row (KB is a multiple of
-    // PPR), rows t / PPR, t / PPR + KB / PPR, ...  Batches of SB pieces: all
-    // their global loads are issued before the first conversion.
+    // Thread t always stages piece t % PPR of a row, rows t / PPR,
+    // t / PPR + KB / PPR, ...  Batches of SB pieces: all their global loads
+    // are issued before the first conversion.  dK rows are rotated by their
+    // own position, R(i) q, on the way.
     {
-      static_assert(KB % PPR == 0, "pieces per row divide the block");
-      constexpr int SB = 4;
+      constexpr int SB = PART == 0 ? 2 : 4;  // dK also holds rotary rows
       constexpr int RSTEP = KB / PPR;
       const int pc = tid % PPR;
-      const int which = pc / (GW * XH);
-      const int hp = (pc / XH) % GW;
+      const int hp = pc / XH;
       const int xh = pc % XH;
       const bool pair = 2 * hp + 1 < G;
       const size_t rstride = size_t(a.hq) * D;
-      const bf16_t* src0 = (which ? dO : Q) + (size_t(b) * n + r0) * rstride + (size_t(g) * G + 2 * hp) * D + c * KC + xh * 8;
-      uint32_t* dst0 = Ws + which * PW + hp * KC + xh * 8;
+      const bf16_t* src0 = X + (size_t(b) * n + r0) * rstride + (size_t(g) * G + 2 * hp) * D + c * KC + xh * 8;
+      const float* rope0 = rope ? a.rope + size_t(r0) * D + c * KC + xh * 8 : nullptr;
+      uint32_t* dst0 = Ws + hp * KC + xh * 8;
       for (int row0 = tid / PPR; row0 < nrows; row0 += SB * RSTEP) {
         uint4 u0[SB], u1[SB];
+        float4 ra[SB], rb[SB];
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
           const int row = row0 + u * RSTEP;
           u0[u] = u1[u] = make_uint4(0, 0, 0, 0);
+          ra[u] = rb[u] = make_float4(1.f, 0.f, 1.f, 0.f);
           if (row < nrows) {
             const bf16_t* src = src0 + size_t(row) * rstride;
             u0[u] = *reinterpret_cast<const uint4*>(src);
             if (pair) u1[u] = *reinterpret_cast<const uint4*>(src + D);
+            if (rope) {
+              ra[u] = *reinterpret_cast<const float4*>(rope0 + size_t(row) * D);
+              rb[u] = *reinterpret_cast<const float4*>(rope0 + size_t(row) * D + 4);
+            }
           }
         }
 #pragma unroll
@@ -599,11 +659,21 @@ __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs
           if (row < nrows) {
             const uint32_t e0[4] = {u0[u].x, u0[u].y, u0[u].z, u0[u].w};
             const uint32_t e1[4] = {u1[u].x, u1[u].y, u1[u].z, u1[u].w};
+            const float cs[8] = {ra[u].x, ra[u].y, ra[u].z, ra[u].w, rb[u].x, rb[u].y, rb[u].z, rb[u].w};
             uint32_t wv[8];
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-              wv[2 * x] = pack_h2(bf16_lo(e0[x]), bf16_lo(e1[x]));
-              wv[2 * x + 1] = pack_h2(bf16_hi(e0[x]), bf16_hi(e1[x]));
+              // dims 2x, 2x + 1 of both heads: one rotation pair each
+              float a0 = bf16_lo(e0[x]), b0 = bf16_hi(e0[x]);
+              float a1 = bf16_lo(e1[x]), b1 = bf16_hi(e1[x]);
+              if (PART == 0) {
+                const float c_ = cs[2 * x], s_ = cs[2 * x + 1];
+                const float ra0 = a0 * c_ - b0 * s_, rb0 = a0 * s_ + b0 * c_;
+                const float ra1 = a1 * c_ - b1 * s_, rb1 = a1 * s_ + b1 * c_;
+                a0 = ra0; b0 = rb0; a1 = ra1; b1 = rb1;
+              }
+              wv[2 * x] = pack_h2(a0, a1);
+              wv[2 * x + 1] = pack_h2(b0, b1);
             }
             uint32_t* dst = dst0 + row * RW;
             *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
@@ -615,85 +685,48 @@ __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs
     __syncthreads();
 
     for (int sj = s; sj < e; ++sj) {
-      const int lo = st.lo[sj];
-      const float w = st.frac[sj];
-      const int rung = st.rung[sj];
-      const int ntaps = taps_of(sj);
+      const int lo = slot_i(vlo, sj);
+      const float w = __int_as_float(slot_i(vfr, sj));
+      const int info = slot_i(vinfo, sj);
+      const int rung = (info & 0xffff) - 1;
+      const int ntaps = (info >> 16) + 1;
       float ddacc = 0.f;
       for (int tap = 0; tap < ntaps; ++tap) {
         const int delta = lo + tap;
         const float wt = tap ? w : 1.f - w;
         // Query j + delta; the query pass stored p = 0 where the slot has no
         // row for it.  Masked steps read staged row 0 with zero weights.
+        // Window slots run the same arithmetic with weight 1; their dd sum is
+        // never stored.  One straight-line body keeps the registers put.
         const bool valid = j + delta < n;
         const int lrow = valid ? j + delta - r0 : 0;
-        const uint32_t* dsp = wts;
-        const uint32_t* pp = wts + GW;
         const uint32_t* rowp = Ws + lrow * RW;
-        // yk[x] = sum_h dS_h q_h[x] (unrotated frame of query i)
-        float yk[KC];
+        float y[KC];
         {
-          uint32_t qw[KC];
-          load_words<KC>(rowp, qw);
+          uint32_t xw[KC];
+          load_words<KC>(rowp, xw);
 #pragma unroll
-          for (int x = 0; x < KC; ++x) yk[x] = dot2_h(dsp[0], qw[x], 0.f);
+          for (int x = 0; x < KC; ++x) y[x] = dot2_h(wts[0], xw[x], 0.f);
 #pragma unroll
           for (int hp = 1; hp < GW; ++hp) {
-            load_words<KC>(rowp + hp * KC, qw);
+            load_words<KC>(rowp + hp * KC, xw);
 #pragma unroll
-            for (int x = 0; x < KC; ++x) yk[x] = dot2_h(dsp[hp], qw[x], yk[x]);
-          }
-        }
-        // dK gathers R(delta) yk (relative rotation into key j's frame)
-        float cs[KC];
-        if constexpr (ROPE) {
-          // One row for the whole wave (masked lanes carry zero weights),
-          // read through the constant address space as a scalar load.
-          using crow_t = const __attribute__((address_space(4))) float*;
-          const crow_t rr = (crow_t)(a.rope + size_t(min(delta, n - 1)) * D + c * KC);
-#pragma unroll
-          for (int x = 0; x < KC; ++x) cs[x] = rr[x];
-        } else {
-#pragma unroll
-          for (int x = 0; x < KC; x += 2) {
-            cs[x] = 1.f;
-            cs[x + 1] = 0.f;
-          }
-        }
-        // Window slots run the same arithmetic with weight 1; their dd sum
-        // is never stored.  One straight-line body keeps the registers put.
-        float yv[KC];
-        {
-          uint32_t ow[KC];
-          load_words<KC>(rowp + PW, ow);
-#pragma unroll
-          for (int x = 0; x < KC; ++x) yv[x] = dot2_h(pp[0], ow[x], 0.f);
-#pragma unroll
-          for (int hp = 1; hp < GW; ++hp) {
-            load_words<KC>(rowp + PW + hp * KC, ow);
-#pragma unroll
-            for (int x = 0; x < KC; ++x) yv[x] = dot2_h(pp[hp], ow[x], yv[x]);
+            for (int x = 0; x < KC; ++x) y[x] = dot2_h(wts[hp], xw[x], y[x]);
           }
         }
         float part = 0.f;
 #pragma unroll
-        for (int x = 0; x < KC; x += 2) {
-          const float c_ = cs[x], s_ = cs[x + 1];
-          const float r0_ = yk[x] * c_ - yk[x + 1] * s_;
-          const float r1_ = yk[x] * s_ + yk[x + 1] * c_;
-          dk[x] = fmaf(wt, r0_, dk[x]);
-          dk[x + 1] = fmaf(wt, r1_, dk[x + 1]);
-          dv[x] = fmaf(wt, yv[x], dv[x]);
-          dv[x + 1] = fmaf(wt, yv[x + 1], dv[x + 1]);
-          part = fmaf(r0_, kj[x], fmaf(r1_, kj[x + 1], fmaf(yv[x], vj[x], fmaf(yv[x + 1], vj[x + 1], part))));
+        for (int x = 0; x < KC; ++x) {
+          acc[x] = fmaf(wt, y[x], acc[x]);
+          part = fmaf(y[x], own[x], part);
         }
         ddacc += tap ? part : -part;
 
         // weights of the next step, then the loads of the one after it
-        convert(fs, ft, rp, rdp, rdv, wts);
+        convert(raw, wts);
         __builtin_amdgcn_sched_barrier(0);
-        next_step(fs, ft);
-        load_step(fs, ft, rp, rdp, rdv);
+        advance();
+        load_step(raw);
       }
       if (rung >= 0) {
         const float tot = wave_sum(ddacc);
@@ -703,15 +736,16 @@ __global__ __launch_bounds__(key_block(2, G, D)) void bwd_key_h16_kernel(BwdArgs
     s = e;
   }
   if (activej) {
-    store_vec<KC>(static_cast<bf16_t*>(a.dk) + kv_off, dk);
-    store_vec<KC>(static_cast<bf16_t*>(a.dv) + kv_off, dv);
+    if (rope) rotate_pairs<KC, -1>(acc, a.rope + size_t(j) * D, c * KC);  // dK = R(j)^T dK~
+    store_vec<KC>(static_cast<bf16_t*>(PART == 0 ? a.dk : a.dv) + kv_off, acc);
   }
   __syncthreads();
+  // dd partials: [rung][2 * tiles], the dK half first
   for (int r = tid; r < a.n_rungs; r += KB) {
-    float acc = 0.f;
+    float t_ = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) acc += ddl[w * a.n_rungs + r];
-    a.dd_part[size_t(r) * a.tiles + tile] = acc;
+    for (int w_ = 0; w_ < NW; ++w_) t_ += ddl[w_ * a.n_rungs + r];
+    a.dd_part[size_t(r) * (2 * a.tiles) + PART * a.tiles + tile] = t_;
   }
 }
 
@@ -801,18 +835,24 @@ int launch_query_t(const BwdArgs& a, const SlotTable& t, hipStream_t st) {
 
 template <typename T, int D, int G>
 int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
-  constexpr int KB = key_block(sizeof(T), G, D);
   BwdArgs a = a0;
-  a.nblk = (a.n + KB - 1) / KB;
-  a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk(D));
   if constexpr (sizeof(T) == 2) {
-    a.kcap = key_h16_cap(KB, G, D, t.n_rungs);
-    const size_t lds = (size_t(a.kcap) * key_row_words(G, D) + size_t(KB / 64) * t.n_rungs) * 4;
-    if (a.rope)
-      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, true>), dim3(a.tiles), dim3(KB), lds, st, a, t);
-    else
-      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, false>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+    constexpr int KB = kKeyBlockH16;
+    a.nblk = (a.n + KB - 1) / KB;
+    a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk(D));
+    a.kcap = key_half_cap(G, D, t.n_rungs);
+    const size_t lds = (size_t(a.kcap) * key_half_row_words(G, D) + size_t(KB / 64) * t.n_rungs) * 4;
+    if (t.count <= 64) {
+      hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 0, true>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+      hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 1, true>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+    } else {
+      hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 0, false>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+      hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 1, false>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+    }
   } else {
+    constexpr int KB = key_block(sizeof(T), G, D);
+    a.nblk = (a.n + KB - 1) / KB;
+    a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk(D));
     hipLaunchKernelGGL((bwd_key_kernel<T, D, G>), dim3(a.tiles), dim3(KB), 0, st, a, t);
   }
   return int(hipGetLastError());
@@ -844,8 +884,11 @@ size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, Bw
   auto al = [](size_t e) { return (e + 63) & ~size_t(63); };  // 256-byte aligned sections
   const size_t pe = al(size_t(p.B) * p.hkv * t.count * size_t(p.n) * p.G);  // floats per array
   const size_t de = al(size_t(p.B) * p.hkv * size_t(p.n) * p.G);
-  const int kb = key_block(p.dtype == SFA_BF16 ? 2 : 4, p.G, p.D);
-  ws->blocks = ((p.n + kb - 1) / kb) * p.B * p.hkv * (p.D / key_chunk(p.D));  // bwd_key tiles
+  // dd partials per rung: one per key-pass workgroup (bf16: the dK and the
+  // dV kernel each have one per tile)
+  const bool h16 = p.dtype == SFA_BF16;
+  const int kb = h16 ? kKeyBlockH16 : key_block(4, p.G, p.D);
+  ws->blocks = ((p.n + kb - 1) / kb) * p.B * p.hkv * (p.D / key_chunk(p.D)) * (h16 ? 2 : 1);
   (void)nblk;
   const size_t dd_e = size_t(ws->blocks) * (t.n_rungs > 0 ? t.n_rungs : 1);
   float* f = static_cast<float*>(base);

@@ -171,7 +171,9 @@ def test_bwd_validation_and_workspace_size():
     al = lambda e: (e + 63) // 64 * 64
     pe = al(2 * 2 * S * 100 * 4)          # p and dp: [B][Hkv][S][n][G]
     de = al(2 * 2 * 100 * 4)              # Dvec: [B][Hkv][n][G]
-    blocks = 1 * 2 * 2 * 4                # key-pass tiles: 128-key blocks x B x Hkv x 16-dim chunks
+    # dd partials: one per key-pass tile (128-key blocks x B x Hkv x 16-dim
+    # chunks) from each of the bf16 dK and dV kernels
+    blocks = 1 * 2 * 2 * 4 * 2
     assert nb == (2 * pe + de + blocks * 15) * 4
     assert lib.sfa_bwd_workspace_bytes(ctypes.byref(_prob(head_dim=48))) == 0
     base = sfa.base_fib()

@@ -7,7 +7,12 @@ on [4, 8)), so bf16 outputs must lie within 1e-2 plus half a bf16 ulp of
 the exact value: the accumulation error, before the final rounding, is what
 the 1e-2 bounds.  dd and dtheta are
 sums over every (query, head) of the batch, so their bound is relative:
-|err| <= tol * max(1, |ref|).  Offsets, edge lists and Christoffel offsets
+|err| <= tol * max(1, |ref|).  The bf16 kernels round dS, p and the rotated
+queries to f16 (11-bit significand) before the products; a dd that is a
+near cancellation of large terms can then be off by more than that, so
+bf16 cases add 4 u L2 per rung (u = 2^-11, L2 the size of the rounded terms,
+from oracle/tolerance.py; about seven standard deviations of the rounding
+error), carried into dtheta through its weights.  Offsets, edge lists and Christoffel offsets
 are produced by the library and were checked bit-exact against the oracle
 by the CPU tests.
 """
@@ -20,6 +25,7 @@ import synth_inputs as si
 from oracle import attention as ref
 from oracle import christoffel as ref_chr
 from oracle import offsets as ref_off
+from oracle import tolerance as ref_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -103,11 +109,21 @@ def _bwd_check(case, W, lo, frac, alpha, base, sel=slice(None), tol=None, grad_t
         assert e <= tol, nm
     if sel == slice(None) and len(lo):
         rdd = g["dd"]
-        edd = np.abs(_np(dd) - rdd) / np.maximum(1.0, np.abs(rdd))
         rth = ref.dtheta_from_dd(rdd, base, alpha)
-        eth = abs(float(dth.item()) - rth) / max(1.0, abs(rth))
-        print("dd rel err %.3g dtheta rel err %.3g (ref %.6g)" % (edd.max(), eth, rth), flush=True)
-        assert edd.max() <= grad_tol and eth <= grad_tol
+        bdd = grad_tol * np.maximum(1.0, np.abs(rdd))
+        bth = grad_tol * max(1.0, abs(rth))
+        if case.dtype == "bf16":
+            # bf16 kernels round dS, p and q~ to f16: add 4 u L2 per rung
+            # (oracle/tolerance.py), carried into dtheta through its weights
+            l2, _ = ref_tol.dd_rounding_scale(*case.f64(), W, lo, frac, case.rope_theta)
+            r16 = 4 * ref_tol.U16 * l2
+            bdd = bdd + r16
+            bth = bth + abs(ref_off.dalpha_dtheta(alpha)) * float(np.sum(np.abs(base) * r16))
+        add = np.abs(_np(dd) - rdd)
+        ath = abs(float(dth.item()) - rth)
+        print("dd abs err / bound %.3g (worst rung %d) dtheta abs err %.3g bound %.3g (ref %.6g)"
+              % (float((add / bdd).max()), int((add / bdd).argmax()), ath, bth, rth), flush=True)
+        assert np.all(add <= bdd) and ath <= bth
     return dq, dk, dv, dd, dth
 
 
