@@ -28,7 +28,10 @@ namespace sfa {
 
 namespace {
 
-constexpr int BQ = 64;  // queries (bwd_query) or keys (bwd_key) per workgroup
+#ifndef SFA_BWD_BQ
+#define SFA_BWD_BQ 32
+#endif
+constexpr int BQ = SFA_BWD_BQ;  // queries per bwd_query workgroup
 constexpr int kCap = 128;
 
 struct BwdArgs {

@@ -44,7 +44,10 @@ namespace sfa {
 #define SFA_FWD_BF16_PATH 1
 #endif
 
-constexpr int BQ = 64;   // queries per workgroup
+#ifndef SFA_FWD_BQ
+#define SFA_FWD_BQ 64
+#endif
+constexpr int BQ = SFA_FWD_BQ;  // queries per workgroup
 constexpr int SC = 8;    // slots per online-softmax chunk
 constexpr int ESC = 4;   // edges per chunk (keys come from global memory)
 
