@@ -49,14 +49,60 @@ def algorithmic_bytes(B, n, hq, hkv, D, esize):
         "fwd_offsets": q + 2 * kv + q + lse,
         # read Q, K, V, dO, LSE; write dQ
         "bwd_query": q + 2 * kv + q + lse + q,
-        # read Q, dO, K, V; write dK, dV
+        # read Q, dO, K, V; write dK, dV (bf16: the dK kernel reads Q and K
+        # and writes dK, the dV kernel reads dO and V and writes dV)
         "bwd_key": 2 * q + 2 * kv + 2 * kv,
+        "bwd_key_dk": q + kv + kv,
+        "bwd_key_dv": q + kv + kv,
         "bwd_reduce": 0,
         # the step: forward + backward, each tensor once per pass
         "step": (q + 2 * kv + q + lse) + (q + 2 * kv + q + lse + q + 2 * kv),
         # forward without LSE
         "fwd_only": q + 2 * kv + q,
     }
+
+
+KERNEL_SOURCES = ("fixed_offset_gather_amd/csrc/sfa_bwd.hip", "fixed_offset_gather_amd/csrc/sfa_fwd.hip",
+                  "fixed_offset_gather_amd/csrc/sfa_device.h", "fixed_offset_gather_amd/csrc/sfa_internal.h")
+
+
+def kernel_source_hash():
+    """sha256 over the kernel sources, to tell whether counters still apply."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known size), or
+    None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "%s__page1_learned_step__traffic.txt" % kernel)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return int(fields["hbm_bytes_per_launch"])
+
+
+def calibration_copy():
+    """One plain device copy of 256 MiB (outside any timed region), so a
+    counter run sees a kernel of known traffic: it reads and writes 256 MiB."""
+    import torch
+    a = torch.empty(128 * 1024 * 1024, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
 
 
 def cpu_baseline(w, alpha, seqs):
@@ -94,6 +140,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=16)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 256 MiB device copy (for counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -131,6 +179,8 @@ def main():
         o, lse = sfa.fwd(q, k, v, W, lo_, frac_, rope, out=o_buf, lse=lse_buf)
         return sfa.bwd(q, k, v, lse, do, W, lo_, frac_, rope, base=base, alpha=alpha, workspace=ws)
 
+    if args.calibrate_copy:
+        calibration_copy()
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
@@ -144,7 +194,7 @@ def main():
     wall = time.perf_counter() - t0
     sfa.profile_enable(False)
     kern = {}
-    for name in ("fwd_offsets", "bwd_query", "bwd_key", "bwd_reduce"):
+    for name in ("fwd_offsets", "bwd_query", "bwd_key_dk", "bwd_key_dv", "bwd_reduce"):
         ms, cnt = sfa.profile_read(name)
         if cnt:
             kern[name] = {"avg_us": 1e3 * ms / cnt, "launches": cnt}
@@ -164,7 +214,7 @@ def main():
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
-        "traffic": None,
+        "traffic": measured_traffic(dom),
         "algorithmic_bytes_per_launch": ab[dom],
         "avg_launch_us": round(kern[dom]["avg_us"], 3),
     }

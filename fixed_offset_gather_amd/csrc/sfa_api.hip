@@ -115,7 +115,7 @@ hipEvent_t take_event() {
 }  // namespace
 
 ProfileScope::ProfileScope(const char* nm, void* st) : name(nm), stream(st), ev0(nullptr) {
-  if (!g_prof_on) return;
+  if (!g_prof_on || !nm) return;  // a null name records nothing
   hipEvent_t e = take_event();
   if (e && hipEventRecord(e, static_cast<hipStream_t>(stream)) == hipSuccess) ev0 = e;
 }
@@ -271,7 +271,8 @@ extern "C" int sfa_bwd(const sfa_attn* a, const void* q, const void* k, const vo
     if (rc) return rc;
   }
   {
-    ProfileScope ps("bwd_key", stream);
+    // bf16: the launcher records its two kernels as bwd_key_dk / bwd_key_dv
+    ProfileScope ps(p.dtype == SFA_BF16 ? nullptr : "bwd_key", stream);
     rc = hip_status(launch_bwd_key(p, t, q, k, v, dout, dk, dv, ws, stream), "sfa_bwd key launch");
     if (rc) return rc;
   }

@@ -845,12 +845,20 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
     a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk(D));
     a.kcap = key_half_cap(G, D, t.n_rungs);
     const size_t lds = (size_t(a.kcap) * key_half_row_words(G, D) + size_t(KB / 64) * t.n_rungs) * 4;
-    if (t.count <= 64) {
-      hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 0, true>), dim3(a.tiles), dim3(KB), lds, st, a, t);
-      hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 1, true>), dim3(a.tiles), dim3(KB), lds, st, a, t);
-    } else {
-      hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 0, false>), dim3(a.tiles), dim3(KB), lds, st, a, t);
-      hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 1, false>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+    const bool small = t.count <= 64;
+    {
+      ProfileScope ps("bwd_key_dk", st);
+      if (small)
+        hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 0, true>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+      else
+        hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 0, false>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+    }
+    {
+      ProfileScope ps("bwd_key_dv", st);
+      if (small)
+        hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 1, true>), dim3(a.tiles), dim3(KB), lds, st, a, t);
+      else
+        hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 1, false>), dim3(a.tiles), dim3(KB), lds, st, a, t);
     }
   } else {
     constexpr int KB = key_block(sizeof(T), G, D);

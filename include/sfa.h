@@ -242,7 +242,9 @@ int sfa_bwd(const sfa_attn* a, const void* q, const void* k, const void* v,
  * on its launch stream.  sfa_profile_read synchronises the recorded events
  * and returns the accumulated milliseconds and launch count of the named
  * kernel ("fwd_offsets", "fwd_edges", "bwd_query", "bwd_key",
- * "bwd_reduce"); sfa_profile_reset drops all records.  Not thread-safe with
+ * "bwd_reduce"; with bf16 tensors the key pass is the two kernels
+ * "bwd_key_dk" and "bwd_key_dv" instead of "bwd_key");
+ * sfa_profile_reset drops all records.  Not thread-safe with
  * concurrent launches.
  */
 int sfa_profile_enable(int on);
