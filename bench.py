@@ -246,6 +246,45 @@ def main():
         "frac_of_hbm_peak": round(ab["fwd_only"] / (f_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
     }
 
+    # Learned interpolated gather against fused integer offsets (the pages'
+    # one speed claim: learned about 5x slower at identical FLOPs), page-1
+    # layer forward on the same inputs.  W = 0: self + 15 rungs on both
+    # sides, no duplicate rows.  W = 8: the page's layer, where integer
+    # rungs 1, 2, 3, 5, 8 coincide with window slots and are merged.
+    def time_fwd(W_, lo_, fr_, interp=False):
+        for t in range(args.warmup):
+            q, k, v, _ = sets[t % NSETS]
+            sfa.fwd(q, k, v, W_, lo_, fr_, rope, out=o_buf, interp_kernel=interp)
+        torch.cuda.synchronize()
+        sfa.profile_reset()
+        sfa.profile_enable(True)
+        for t in range(args.steps):
+            q, k, v, _ = sets[t % NSETS]
+            sfa.fwd(q, k, v, W_, lo_, fr_, rope, out=o_buf, interp_kernel=interp)
+        torch.cuda.synchronize()
+        sfa.profile_enable(False)
+        ms_, c_ = sfa.profile_read("fwd_offsets")
+        return round(1e3 * ms_ / max(c_, 1), 3)
+
+    lo_l, fr_l = sfa.offsets_fib(alpha)
+    rows = {
+        "integer_w0": {"window": 0, "alpha": 1.0, "slots": 16, "avg_us": time_fwd(0, lo1, frac1)},
+        "integer_w0_interp_kernel": {"window": 0, "alpha": 1.0, "slots": 16,
+                                     "avg_us": time_fwd(0, lo1, frac1, interp=True)},
+        "learned_w0": {"window": 0, "alpha": alpha, "slots": 16, "avg_us": time_fwd(0, lo_l, fr_l)},
+        "integer_w8": {"window": 8, "alpha": 1.0, "slots": 24, "distinct_rows": 19,
+                       "avg_us": time_fwd(8, lo1, frac1)},
+        "learned_w8": {"window": 8, "alpha": alpha, "slots": 24, "avg_us": time_fwd(8, lo_l, fr_l)},
+    }
+    integer_vs_learned = {
+        "workload": "page-1 layer forward (32 x 1024, 8/2 heads, D 64, bf16, RoPE 1e4)",
+        "rows": rows,
+        "learned_over_integer_w0": round(rows["learned_w0"]["avg_us"] / rows["integer_w0"]["avg_us"], 3),
+        "learned_over_integer_w8": round(rows["learned_w8"]["avg_us"] / rows["integer_w8"]["avg_us"], 3),
+        "pages_claim": "learned interpolated gather about 5x slower than fused integer offsets, no hardware stated",
+    }
+    log("integer vs learned:", {k_: v_["avg_us"] for k_, v_ in rows.items()})
+
     out = {
         "metric": METRIC,
         "value": round(B * n / (ms_per_step * 1e-3), 1),
@@ -270,6 +309,7 @@ def main():
         "kernels_avg_us": {k_: round(v_["avg_us"], 3) for k_, v_ in kern.items()},
         "roofline": roofline,
         "fwd_only": fwd_only,
+        "integer_vs_learned": integer_vs_learned,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, alpha, args.cpu_seqs)

@@ -39,6 +39,7 @@ SFA_ERR_UNSUPPORTED = -3
 SFA_ERR_HIP = -4
 SFA_F32 = 0
 SFA_BF16 = 1
+SFA_FLAG_INTERP_KERNEL = 1
 MAX_OFFSETS = 128
 MAX_SLOTS = 192
 SCHEDULES = {"fixed": 0, "linear": 1, "coprime": 2}
@@ -56,7 +57,7 @@ class SfaAttn(ctypes.Structure):
         ("hq", ctypes.c_int32), ("hkv", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
         ("window", ctypes.c_int32), ("n_off", ctypes.c_int32),
-        ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("flags", ctypes.c_int32),
         ("off_lo", _i32p), ("off_frac", _f32p), ("rope", _vp),
     ]
 
@@ -237,7 +238,7 @@ def _require(t, name, dtype=None, shape=None):
 class Problem:
     """Holds an ``sfa_attn`` and the host arrays it points to."""
 
-    def __init__(self, q, k, window=0, lo=None, frac=None, rope=None, scale=0.0):
+    def __init__(self, q, k, window=0, lo=None, frac=None, rope=None, scale=0.0, flags=0):
         B, n, hq, d = q.shape
         hkv = k.shape[2]
         self.lo = np.ascontiguousarray(np.zeros(0) if lo is None else lo, dtype=np.int32)
@@ -247,22 +248,27 @@ class Problem:
         if rope is not None:
             _require(rope, "rope", _torch().float32, (n, d // 2, 2))
         self.rope = rope
-        self.c = SfaAttn(B, n, hq, hkv, d, _dtype_code(q), int(window), len(self.lo), float(scale), 0,
+        self.c = SfaAttn(B, n, hq, hkv, d, _dtype_code(q), int(window), len(self.lo), float(scale), int(flags),
                          _ip(self.lo), _fp(self.frac), None if rope is None else rope.data_ptr())
 
     def ref(self):
         return ctypes.byref(self.c)
 
 
-def fwd(q, k, v, window=0, lo=None, frac=None, rope=None, scale=0.0, want_lse=False, out=None, lse=None):
-    """Forward over the window 0..window plus shared offsets (lo, frac)."""
+def fwd(q, k, v, window=0, lo=None, frac=None, rope=None, scale=0.0, want_lse=False, out=None, lse=None,
+        interp_kernel=False):
+    """Forward over the window 0..window plus shared offsets (lo, frac).
+
+    interp_kernel=True runs the interpolating instantiation even when every
+    frac is 0 (SFA_FLAG_INTERP_KERNEL); the result is the same.
+    """
     torch = _torch()
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, nm, q.dtype)
     if k.shape != v.shape:
         raise ValueError("k and v shapes differ")
     B, n, hq, d = q.shape
-    pr = Problem(q, k, window, lo, frac, rope, scale)
+    pr = Problem(q, k, window, lo, frac, rope, scale, SFA_FLAG_INTERP_KERNEL if interp_kernel else 0)
     o = torch.empty_like(q) if out is None else out
     _require(o, "out", q.dtype, q.shape)
     if want_lse and lse is None:

@@ -33,7 +33,7 @@ int validate_problem(const sfa_attn* a, Problem* p) {
     return fail(SFA_ERR_UNSUPPORTED, "n_off %d not in [0, %d]", a->n_off, SFA_MAX_OFFSETS);
   if (int64_t(a->window) + 1 + a->n_off > SFA_MAX_SLOTS)
     return fail(SFA_ERR_UNSUPPORTED, "window + 1 + n_off exceeds %d slots", SFA_MAX_SLOTS);
-  if (a->reserved != 0) return fail(SFA_ERR_ARG, "reserved field must be 0");
+  if (a->flags & ~SFA_FLAG_INTERP_KERNEL) return fail(SFA_ERR_ARG, "unknown flags 0x%x", unsigned(a->flags));
   if (!std::isfinite(a->scale) || a->scale < 0.f) return fail(SFA_ERR_ARG, "scale must be finite and >= 0");
   if (a->n_off > 0 && (!a->off_lo || !a->off_frac)) return fail(SFA_ERR_ARG, "offset arrays are NULL");
   for (int k = 0; k < a->n_off; ++k) {
@@ -53,6 +53,7 @@ int validate_problem(const sfa_attn* a, Problem* p) {
   p->dtype = a->dtype;
   p->window = a->window;
   p->n_off = a->n_off;
+  p->flags = a->flags;
   p->scale = a->scale > 0.f ? a->scale : float(1.0 / std::sqrt(double(a->head_dim)));
   p->rope = a->rope;
   return SFA_OK;

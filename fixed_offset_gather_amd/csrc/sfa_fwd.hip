@@ -95,7 +95,7 @@ struct Bcast {
   }
 };
 
-template <typename T, int D, int G, int LPQ, int CAP>
+template <typename T, int D, int G, int LPQ, int CAP, bool INTERP>
 __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTable st) {
   constexpr int DC = D / LPQ;
   constexpr int KS = RowPad<D>::value;
@@ -166,12 +166,12 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
   while (s < S) {
     const int lo0 = st.lo[s];
     if (lo0 > i_last) break;  // this slot and all later ones are masked for the block
-    int lomax = lo0 + (st.frac[s] > 0.f ? 1 : 0);
+    int lomax = lo0 + ((INTERP && st.frac[s] > 0.f) ? 1 : 0);
     int e = s + 1;
     while (e < S) {
       const int le = st.lo[e];
       if (le > i_last) break;
-      const int need = max(lomax, le + (st.frac[e] > 0.f ? 1 : 0));
+      const int need = max(lomax, le + ((INTERP && st.frac[e] > 0.f) ? 1 : 0));
       if (need - lo0 + BQ > CAP) break;
       lomax = need;
       ++e;
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
           const int r = i - lo - r0;  // in [0, nrows) for every lane of the block
           float kt[DC];
           load_vec<DC>(Ks + r * KS + c * DC, kt);
-          if (w != 0.f) {
+          if (INTERP && w != 0.f) {
             float kb[DC];
             load_vec<DC>(Ks + (r - 1) * KS + c * DC, kb);
 #pragma unroll
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
           const int r = i - lo - r0;
           float vt[DC];
           load_vec<DC>(Vs + r * KS + c * DC, vt);
-          if (w != 0.f) {
+          if (INTERP && w != 0.f) {
             float vb[DC];
             load_vec<DC>(Vs + (r - 1) * KS + c * DC, vb);
 #pragma unroll
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
 #define SFA_FWD_BOUNDS(T) __launch_bounds__(T)
 #endif
 
-template <int D, int G, int LPQ, int CAP, bool VF32>
+template <int D, int G, int LPQ, int CAP, bool VF32, bool INTERP>
 __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTable st) {
   constexpr int DC = D / LPQ;  // dims per lane
   constexpr int DW = DC / 2;   // f16 pairs per lane
@@ -371,12 +371,12 @@ __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTa
   while (s < S) {
     const int lo0 = st.lo[s];
     if (lo0 > i_last) break;
-    int lomax = lo0 + (st.frac[s] > 0.f ? 1 : 0);
+    int lomax = lo0 + ((INTERP && st.frac[s] > 0.f) ? 1 : 0);
     int e = s + 1;
     while (e < S) {
       const int le = st.lo[e];
       if (le > i_last) break;
-      const int need = max(lomax, le + (st.frac[e] > 0.f ? 1 : 0));
+      const int need = max(lomax, le + ((INTERP && st.frac[e] > 0.f) ? 1 : 0));
       if (need - lo0 + BQ > CAP) break;
       lomax = need;
       ++e;
@@ -475,7 +475,7 @@ __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTa
           const int r = i - lo - r0;
           uint32_t kw[DW];
           load_words<DW>(Ks + r * RW + c * DW, kw);
-          if (w != 0.f) {
+          if (INTERP && w != 0.f) {
             uint32_t kb[DW];
             load_words<DW>(Ks + (r - 1) * RW + c * DW, kb);
             const half2_t w2 = {(_Float16)w, (_Float16)w};
@@ -532,7 +532,7 @@ __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTa
             const float* vrow = reinterpret_cast<const float*>(Vs + r * VRW) + c * DC;
             float vt[DC];
             load_vec<DC>(vrow, vt);
-            if (w != 0.f) {
+            if (INTERP && w != 0.f) {
               float vb[DC];
               load_vec<DC>(vrow - VRW, vb);
 #pragma unroll
@@ -545,7 +545,7 @@ __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTa
           } else {
             uint32_t vw[DW];
             load_words<DW>(Vs + r * VRW + c * DW, vw);
-            if (w != 0.f) {
+            if (INTERP && w != 0.f) {
               uint32_t vb[DW];
               load_words<DW>(Vs + (r - 1) * VRW + c * DW, vb);
               const half2_t w2 = {(_Float16)w, (_Float16)w};
@@ -731,15 +731,29 @@ constexpr int fwd_lpq() {
   return G > D / 16 ? G : D / 16;
 }
 
-template <typename T, int D, int G>
-int launch_fwd_offsets_t(const Problem& p, const SlotTable& t, const FwdArgs& a, hipStream_t st) {
+template <typename T, int D, int G, bool INTERP>
+void launch_fwd_offsets_i(const SlotTable& t, const FwdArgs& a, hipStream_t st) {
   constexpr int LPQ = fwd_lpq<D, G>();
   if constexpr (sizeof(T) == 2 && SFA_FWD_BF16_PATH > 0) {
-    hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, SFA_FWD_CAP, SFA_FWD_BF16_PATH == 2>), dim3(a.tiles),
-                       dim3(BQ * LPQ), 0, st, a, t);
+    hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, SFA_FWD_CAP, SFA_FWD_BF16_PATH == 2, INTERP>),
+                       dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
   } else {
-    hipLaunchKernelGGL((fwd_offsets_kernel<T, D, G, LPQ, kCap>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+    hipLaunchKernelGGL((fwd_offsets_kernel<T, D, G, LPQ, kCap, INTERP>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a,
+                       t);
   }
+}
+
+// The integer instantiation (no interpolation code) runs when every slot
+// has frac == 0, unless SFA_FLAG_INTERP_KERNEL asks for the interpolating
+// one; both give the same bits there.
+template <typename T, int D, int G>
+int launch_fwd_offsets_t(const Problem& p, const SlotTable& t, const FwdArgs& a, hipStream_t st) {
+  bool interp = (p.flags & SFA_FLAG_INTERP_KERNEL) != 0;
+  for (int s = 0; s < t.count && !interp; ++s) interp = t.frac[s] > 0.f;
+  if (interp)
+    launch_fwd_offsets_i<T, D, G, true>(t, a, st);
+  else
+    launch_fwd_offsets_i<T, D, G, false>(t, a, st);
   return int(hipGetLastError());
 }
 

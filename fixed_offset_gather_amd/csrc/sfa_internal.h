@@ -29,7 +29,7 @@ struct SlotTable {
 
 // Kernel launch parameters derived from sfa_attn after validation.
 struct Problem {
-  int B, n, hq, hkv, D, G, dtype, window, n_off;
+  int B, n, hq, hkv, D, G, dtype, window, n_off, flags;
   float scale;
   const float* rope;
 };

@@ -159,6 +159,18 @@ int sfa_rope_table(int n, int head_dim, double theta, float* table);
 /* ------------------------------------------------------------------ */
 
 /*
+ * sfa_attn.flags.  SFA_FLAG_INTERP_KERNEL: sfa_fwd runs the interpolating
+ * instantiation of the shared-offset kernel even when every offset is an
+ * integer (frac == 0 everywhere).  By default such a layer runs the integer
+ * instantiation, which has no interpolation code: the pages' fused
+ * integer-offset kernel against their learned interpolated gather
+ * ("Depth-Staggered Fibonacci Spacing for Sparse Attention", results
+ * discussion of the learned variant).  Both give bit-identical results; the
+ * flag exists to measure and test that.
+ */
+#define SFA_FLAG_INTERP_KERNEL 1
+
+/*
  * Problem description (plain data; host arrays are read during the call
  * and not retained).
  */
@@ -172,7 +184,7 @@ typedef struct sfa_attn {
   int32_t window;   /* W >= 0: distances 0..W, self always present ([P1]) */
   int32_t n_off;    /* shared offsets, 0..SFA_MAX_OFFSETS */
   float scale;      /* logit scale; 0 -> 1/sqrt(D) ([P2] item 2, [P3]) */
-  int32_t reserved; /* must be 0 */
+  int32_t flags;    /* SFA_FLAG_* bits, 0 by default */
   const int32_t* off_lo; /* host [n_off]: floor of each offset distance, >= 0 */
   const float* off_frac; /* host [n_off]: interpolation weight in [0, 1) */
   const float* rope;     /* device [n][D/2][2] from sfa_rope_table, or NULL

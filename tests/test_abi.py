@@ -99,7 +99,7 @@ def test_rope_table_matches_oracle_angles():
 
 def _prob(**kw):
     d = dict(batch=1, seqlen=64, hq=8, hkv=2, head_dim=64, dtype=sfa.SFA_BF16, window=8, n_off=0,
-             scale=0.0, reserved=0)
+             scale=0.0, flags=0)
     d.update(kw)
     lo = np.asarray(kw.pop("lo", []), dtype=np.int32)
     fr = np.asarray(kw.pop("frac", []), dtype=np.float32)
@@ -138,7 +138,7 @@ def _fwd(a, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None):
     (dict(lo=[1], frac=[float("nan")]), sfa.SFA_ERR_ARG),
     (dict(scale=float("nan")), sfa.SFA_ERR_ARG),
     (dict(scale=-1.0), sfa.SFA_ERR_ARG),
-    (dict(reserved=3), sfa.SFA_ERR_ARG),
+    (dict(flags=2), sfa.SFA_ERR_ARG),
     (dict(batch=-1), sfa.SFA_ERR_ARG),
 ])
 def test_fwd_rejects_invalid_problem(kw, code):

@@ -180,6 +180,23 @@ def test_integer_offsets_equal_window_slots_bitwise():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("W,base", [(8, "fib"), (0, "fib"), (8, "pow2")])
+def test_integer_instantiation_bitwise_equals_interpolating_kernel(dtype, W, base):
+    # alpha = 1: every rung is an integer distance, so the library runs the
+    # integer instantiation (no interpolation code); the interpolating
+    # instantiation forced on the same layer must give the same bits.
+    sfa = _sfa()
+    case = Case(4, 1024, 8, 2, 64, dtype, seed=13)
+    lo, fr = (sfa.offsets_fib if base == "fib" else sfa.offsets_pow2)(1.0)
+    assert not fr.any()
+    o1, l1 = sfa.fwd(case.qd, case.kd, case.vd, W, lo, fr, case.rope, want_lse=True)
+    o2, l2 = sfa.fwd(case.qd, case.kd, case.vd, W, lo, fr, case.rope, want_lse=True, interp_kernel=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    _fwd_check(case, W, lo, fr, sel=slice(0, 1))
+
+
 def test_integer_alpha_interpolation_path_bitwise():
     # alpha = 1: every rung has frac = 0; the same rungs given as exact
     # integer distances (frac = 0 written explicitly) are bit-identical, and
