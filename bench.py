@@ -251,16 +251,25 @@ def main():
     # layer forward on the same inputs.  W = 0: self + 15 rungs on both
     # sides, no duplicate rows.  W = 8: the page's layer, where integer
     # rungs 1, 2, 3, 5, 8 coincide with window slots and are merged.
-    def time_fwd(W_, lo_, fr_, interp=False):
-        for t in range(args.warmup):
+    def time_fwd(W_, lo_, fr_, interp=False, n_=n, rope_=None):
+        # n_ != n: the same resident tokens as B * n / n_ sequences of n_
+        rope_ = rope if rope_ is None else rope_
+        B_ = B * n // n_
+        shp_q, shp_kv = (B_, n_, hq, D), (B_, n_, hkv, D)
+        ob = o_buf.view(shp_q)
+
+        def call(t):
             q, k, v, _ = sets[t % NSETS]
-            sfa.fwd(q, k, v, W_, lo_, fr_, rope, out=o_buf, interp_kernel=interp)
+            sfa.fwd(q.view(shp_q), k.view(shp_kv), v.view(shp_kv), W_, lo_, fr_, rope_, out=ob,
+                    interp_kernel=interp)
+
+        for t in range(args.warmup):
+            call(t)
         torch.cuda.synchronize()
         sfa.profile_reset()
         sfa.profile_enable(True)
         for t in range(args.steps):
-            q, k, v, _ = sets[t % NSETS]
-            sfa.fwd(q, k, v, W_, lo_, fr_, rope, out=o_buf, interp_kernel=interp)
+            call(t)
         torch.cuda.synchronize()
         sfa.profile_enable(False)
         ms_, c_ = sfa.profile_read("fwd_offsets")
@@ -284,6 +293,21 @@ def main():
         "pages_claim": "learned interpolated gather about 5x slower than fused integer offsets, no hardware stated",
     }
     log("integer vs learned:", {k_: v_["avg_us"] for k_, v_ in rows.items()})
+
+    # Length extrapolation: the page-1 layer forward (W = 8) at longer
+    # contexts with unchanged offsets, 32,768 tokens per batch throughout.
+    lengths = {}
+    for n_ in (1024, 2048, 4096, 8192):
+        rope_ = sfa.rope_table_device(n_, D, w["rope_theta"], dev)
+        row = {"batch": B * n // n_}
+        for label, (lo_, fr_) in (("integer", (lo1, frac1)), ("learned", (lo_l, fr_l))):
+            us = time_fwd(8, lo_, fr_, n_=n_, rope_=rope_)
+            row[label] = {"avg_us": us, "queries_per_s": round(B * n / (us * 1e-6), 1),
+                          "algorithmic_GBs": round(ab["fwd_only"] / (us * 1e-6) / 1e9, 1)}
+        lengths[str(n_)] = row
+        del rope_
+    log("length extrapolation us:", {k_: (v_["integer"]["avg_us"], v_["learned"]["avg_us"])
+                                     for k_, v_ in lengths.items()})
 
     out = {
         "metric": METRIC,
@@ -310,6 +334,7 @@ def main():
         "roofline": roofline,
         "fwd_only": fwd_only,
         "integer_vs_learned": integer_vs_learned,
+        "length_extrapolation": {"workload": "page-1 layer forward, W 8, 32,768 tokens per batch", "by_seqlen": lengths},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, alpha, args.cpu_seqs)

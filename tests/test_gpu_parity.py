@@ -361,6 +361,25 @@ def test_page1_learned_step_full_size():
     _bwd_check(case, w["window"], lo, frac, alpha, sfa.base_fib())
 
 
+@pytest.mark.parametrize("n", [2048, 4096, 8192])
+@pytest.mark.parametrize("alpha", [1.0, 0.7886])
+def test_length_extrapolation_forward(n, alpha):
+    # The page-1 layer at longer contexts with unchanged offsets: 32,768
+    # tokens per batch as 32768 / n sequences; sequence 0 compared in full.
+    sfa = _sfa()
+    case = Case(32768 // n, n, 8, 2, 64, "bf16", seed=21)
+    lo, frac = sfa.offsets_fib(alpha)
+    _fwd_check(case, 8, lo, frac, sel=slice(0, 1))
+
+
+def test_length_extrapolation_backward_4096():
+    sfa = _sfa()
+    case = Case(2, 4096, 8, 2, 64, "bf16", seed=22)
+    alpha = 0.7886
+    lo, frac = sfa.offsets_fib(alpha)
+    _bwd_check(case, 10, lo, frac, alpha, sfa.base_fib())
+
+
 def test_ctx2048_christoffel_full_size():
     sfa = _sfa()
     w = si.WORKLOADS["ctx2048_christoffel"]
