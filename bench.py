@@ -149,6 +149,7 @@ def main():
               "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     import fixed_offset_gather_amd as sfa
@@ -309,6 +310,53 @@ def main():
     log("length extrapolation us:", {k_: (v_["integer"]["avg_us"], v_["learned"]["avg_us"])
                                      for k_, v_ in lengths.items()})
 
+    # Page 3's Christoffel layer trained: forward with LSE + backward (no
+    # offset gradient) at context 2048, 8 x 2048 tokens, 4/4 heads, self +
+    # 128 carry-word offsets, no rotation; views of the resident tensors.
+    wc = si.WORKLOADS["ctx2048_christoffel"]
+    Bc, nc, hc = wc["batch"], wc["seqlen"], wc["hq"]
+    offs = sfa.offsets_christoffel(wc["m"], wc["k"])
+    fr0 = np.zeros(len(offs), dtype=np.float32)
+    ne = Bc * nc * hc * D
+
+    def cview(t):
+        return t.view(-1)[:ne].view(Bc, nc, hc, D)
+
+    lse_c = lse_buf.view(-1)[:Bc * hc * nc].view(Bc, hc, nc)
+    ws_c = torch.empty(sfa.bwd_workspace_bytes(cview(sets[0][0]), cview(sets[0][1]), 0, offs, fr0, None),
+                       dtype=torch.uint8, device=dev)
+
+    def cstep(t):
+        q, k, v, do = (cview(x) for x in sets[t % NSETS])
+        sfa.fwd(q, k, v, 0, offs, fr0, None, out=cview(o_buf), lse=lse_c)
+        sfa.bwd(q, k, v, lse_c, do, 0, offs, fr0, None, workspace=ws_c, want_dd=False)
+
+    for t in range(args.warmup):
+        cstep(t)
+    torch.cuda.synchronize()
+    sfa.profile_reset()
+    sfa.profile_enable(True)
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        cstep(t)
+    torch.cuda.synchronize()
+    cwall = time.perf_counter() - t0
+    sfa.profile_enable(False)
+    ck = {}
+    for name in ("fwd_offsets", "bwd_query", "bwd_key_dk", "bwd_key_dv"):
+        ms_, c_ = sfa.profile_read(name)
+        if c_:
+            ck[name] = round(1e3 * ms_ / c_, 3)
+    christoffel_step = {
+        "workload": "ctx2048_christoffel: 8 x 2048, 4/4 heads, D 64, bf16, W 0 + 128 offsets (129 slots), "
+                    "forward with LSE + backward without dd",
+        "ms_per_step": round(1e3 * cwall / args.steps, 4),
+        "queries_per_s": round(Bc * nc / (cwall / args.steps), 1),
+        "kernels_avg_us": ck,
+    }
+    log("christoffel step:", christoffel_step["ms_per_step"], ck)
+    del ws_c
+
     out = {
         "metric": METRIC,
         "value": round(B * n / (ms_per_step * 1e-3), 1),
@@ -334,6 +382,7 @@ def main():
         "roofline": roofline,
         "fwd_only": fwd_only,
         "integer_vs_learned": integer_vs_learned,
+        "christoffel_step": christoffel_step,
         "length_extrapolation": {"workload": "page-1 layer forward, W 8, 32,768 tokens per batch", "by_seqlen": lengths},
     }
     if not args.no_cpu_baseline:

@@ -49,7 +49,8 @@ struct BwdArgs {
   float* dd_part;
   const float* rope;
   int n, hq, hkv, nblk, tiles, S, n_rungs;
-  int kcap;  // bwd_key: rows one stage may hold (dynamic LDS)
+  int kcap;     // bwd_key: rows one stage may hold (dynamic LDS)
+  int need_dd;  // bwd_key: dd requested, so integer rungs also take their weight-0 second tap
   float scale, scale_log2;
 };
 
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
         for (int h = 0; h < G; ++h) pg[h] = dpg[h] = dvg[h] = 0.f;
       }
     };
-    auto taps_of = [&](int sj) { return (st.frac[sj] > 0.f || st.rung[sj] >= 0) ? 2 : 1; };
+    auto taps_of = [&](int sj) { return (st.frac[sj] > 0.f || (a.need_dd && st.rung[sj] >= 0)) ? 2 : 1; };
 
     float pg[G], dpg[G], dvg[G];
     load_step(s, 0, pg, dpg, dvg);
@@ -523,8 +524,10 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
     const int rg = in ? st.rung[sc] : -1;
     vlo[q] = in ? min(st.lo[sc], n) : n;
     vfr[q] = __float_as_int(fr);
-    // bits 0-15: rung + 1 (0 for a window slot); bit 16: a second tap
-    vinfo[q] = (rg + 1) | ((in && (fr > 0.f || rg >= 0)) ? 0x10000 : 0);
+    // bits 0-15: rung + 1 (0 for a window slot); bit 16: a second tap (an
+    // interpolated rung, or any rung when dd is wanted: the weight-0 tap of
+    // an integer rung still carries its dd term)
+    vinfo[q] = (rg + 1) | ((in && (fr > 0.f || (a.need_dd && rg >= 0))) ? 0x10000 : 0);
   }
   auto slot_i = [&](const int (&v)[NQ], int sj) {  // sj wave-uniform, < 64 * NQ
     if constexpr (SMALL) {
@@ -925,8 +928,9 @@ int launch_bwd_query(const Problem& p, const SlotTable& t, const void* q, const 
 }
 
 int launch_bwd_key(const Problem& p, const SlotTable& t, const void* q, const void* k, const void* v,
-                   const void* dout, void* dk, void* dv, const BwdWorkspace& ws, void* stream) {
+                   const void* dout, void* dk, void* dv, const BwdWorkspace& ws, bool need_dd, void* stream) {
   BwdArgs a = make_args(p, t, ws);
+  a.need_dd = need_dd ? 1 : 0;
   a.q = q;
   a.k = k;
   a.v = v;

@@ -64,7 +64,7 @@ int launch_bwd_query(const Problem& p, const SlotTable& t, const void* q,
                      void* stream);
 int launch_bwd_key(const Problem& p, const SlotTable& t, const void* q,
                    const void* k, const void* v, const void* dout, void* dk,
-                   void* dv, const BwdWorkspace& ws, void* stream);
+                   void* dv, const BwdWorkspace& ws, bool need_dd, void* stream);
 int launch_bwd_reduce(const SlotTable& t, const BwdWorkspace& ws,
                       const float* base_f, double alpha, float* dd,
                       float* dtheta, void* stream);

@@ -92,11 +92,14 @@ def _fwd_check(case, W, lo, frac, sel=slice(None), tol=None):
     return o, lse
 
 
-def _bwd_check(case, W, lo, frac, alpha, base, sel=slice(None), tol=None, grad_tol=None):
+def _bwd_check(case, W, lo, frac, alpha, base, sel=slice(None), tol=None, grad_tol=None, want_dd=True):
     sfa = _sfa()
     o, lse = sfa.fwd(case.qd, case.kd, case.vd, W, lo, frac, case.rope, want_lse=True)
     dq, dk, dv, dd, dth = sfa.bwd(case.qd, case.kd, case.vd, lse, case.dod, W, lo, frac, case.rope,
-                                  base=base, alpha=alpha)
+                                  base=base if want_dd else None, alpha=alpha if want_dd else None,
+                                  want_dd=want_dd)
+    if not want_dd:
+        assert dd is None and dth is None
     torch.cuda.synchronize()
     g = ref.backward(*case.f64(sel), W, lo, frac, case.rope_theta)
     tol = tol or TOL[case.dtype]
@@ -107,7 +110,7 @@ def _bwd_check(case, W, lo, frac, alpha, base, sel=slice(None), tol=None, grad_t
           "raw", {k_: "%.3g" % e for k_, e in raw.items()}, flush=True)
     for nm, e in errs.items():
         assert e <= tol, nm
-    if sel == slice(None) and len(lo):
+    if want_dd and sel == slice(None) and len(lo):
         rdd = g["dd"]
         rth = ref.dtheta_from_dd(rdd, base, alpha)
         bdd = grad_tol * np.maximum(1.0, np.abs(rdd))
@@ -378,6 +381,39 @@ def test_length_extrapolation_backward_4096():
     alpha = 0.7886
     lo, frac = sfa.offsets_fib(alpha)
     _bwd_check(case, 10, lo, frac, alpha, sfa.base_fib())
+
+
+def test_christoffel_backward_full_size():
+    # Page 3's layer trained: self + 128 carry-word offsets (129 slots, the
+    # general slot-table path of the key pass), no rotation, no offset
+    # gradient requested; sequence 0 of 8 compared.
+    sfa = _sfa()
+    w = si.WORKLOADS["ctx2048_christoffel"]
+    case = Case(w["batch"], w["seqlen"], w["hq"], w["hkv"], w["head_dim"], w["dtype"], rope_theta=0.0)
+    offs = sfa.offsets_christoffel(w["m"], w["k"])
+    _bwd_check(case, 0, offs, np.zeros(len(offs), dtype=np.float32), None, None, sel=slice(0, 1), want_dd=False)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_without_dd_integer_rungs(dtype):
+    # alpha = 1 without dd: integer rungs skip their weight-0 second tap.
+    sfa = _sfa()
+    case = Case(2, 200, 8, 2, 64, dtype, seed=17)
+    lo, frac = sfa.offsets_fib(1.0)
+    _bwd_check(case, 8, lo, frac, None, None, tol=TOL[dtype] if dtype == "bf16" else 2e-5, want_dd=False)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_more_than_64_slots_with_dd(dtype):
+    # 97 slots (self + 96 carry-word offsets): the key pass reads its slot
+    # table from three VGPR columns; dd and dtheta over the integer offsets.
+    sfa = _sfa()
+    case = Case(2, 300, 4, 4, 32, dtype, seed=19, rope_theta=0.0)
+    offs = sfa.offsets_christoffel(96, 256)
+    assert len(offs) == 96
+    fr = np.zeros(len(offs), dtype=np.float32)
+    _bwd_check(case, 0, offs, fr, 1.0, offs.astype(np.int32), tol=TOL[dtype] if dtype == "bf16" else 2e-5,
+               grad_tol=1e-4 if dtype == "f32" else 1e-2)
 
 
 def test_ctx2048_christoffel_full_size():
