@@ -30,6 +30,10 @@ Conventions and readings:
 
 Layouts: q [B, n, Hq, D]; k, v [B, n, Hkv, D]; everything float64 inside.
 
+transpose_edges and backward_edges (the edge-list backward) are pinned by
+brute-force membership checks of the inverted table and by torch autograd
+through a dense masked-softmax formulation with rotation.
+
 Pinned by tests/test_oracle_attention.py: torch scaled_dot_product_attention
 with an explicit multiplicity mask (integer offsets) and with is_causal (full
 window), a per-query loop that builds each interpolated key with numpy.interp,
@@ -219,3 +223,83 @@ def forward_edges(q, k, v, edges, count, rope_base=0.0, scale=None):
         j = np.where(valid, edges[:, t], 0)
         o += P[t][..., None] * _rep(v[:, j], g)
     return o, np.transpose(lse, (0, 2, 1)).copy()
+
+
+def transpose_edges(edges, count):
+    """Inverted edge table for the key-side gather of the edge-list backward.
+
+    For every key j: the slots s = i * width + t with t < count[i] and
+    edges[i, t] = j, in ascending (i, t) order.  Returns (inv int[n][cap],
+    -1 padded, inv_count int[n]) with cap the largest in-degree (at least 1).
+    """
+    edges = np.asarray(edges)
+    count = np.asarray(count)
+    n, width = edges.shape
+    lists = [[] for _ in range(n)]
+    for i in range(n):
+        for t in range(int(count[i])):
+            lists[int(edges[i, t])].append(i * width + t)
+    cap = max(1, max(len(x) for x in lists)) if n else 1
+    inv = np.full((n, cap), -1, dtype=np.int32)
+    inv_count = np.zeros(n, dtype=np.int32)
+    for j, x in enumerate(lists):
+        inv[j, : len(x)] = x
+        inv_count[j] = len(x)
+    return inv, inv_count
+
+
+def backward_edges(q, k, v, dout, edges, count, rope_base=0.0, scale=None):
+    """Gradients of L = <O, dO> for forward_edges: dict(dq, dk, dv, o, lse).
+
+    Same steps as the shared-offset backward with one plain key per slot:
+    dp = dO . v_j, Dvec = sum p dp, dS = p (dp - Dvec), dq~ = scale sum dS
+    k~_j, and every slot adds scale dS q~_i to dk~_j and p dO_i to dv_j.
+    """
+    q, k, v, g = _check(q, k, v)
+    B, n, hq, d = q.shape
+    hkv = hq // g
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    edges = np.asarray(edges)
+    count = np.asarray(count)
+    width = edges.shape[1]
+    do = np.asarray(dout, dtype=np.float64)
+    qr = _rope.rotate(q, rope_base)
+    kr = _rope.rotate(k, rope_base)
+    keys, valids = [], []
+    S = np.full((width, B, n, hq), -np.inf)
+    for t in range(width):
+        valid = t < count
+        j = np.where(valid, edges[:, t], 0)
+        keys.append(j)
+        valids.append(valid)
+        s = np.einsum("bihd,bihd->bih", qr, _rep(kr[:, j], g)) * scale
+        s[:, ~valid, :] = -np.inf
+        S[t] = s
+    P, lse = _softmax(S)
+    o = np.zeros(qr.shape)
+    dp = np.zeros(S.shape)
+    for t in range(width):
+        vt = _rep(v[:, keys[t]], g)
+        o += P[t][..., None] * vt
+        dp[t] = np.einsum("bihd,bihd->bih", do, vt)
+    dvec = (P * dp).sum(axis=0)
+    dS = P * (dp - dvec[None])
+    dqr = np.zeros(qr.shape)
+    dkr = np.zeros(kr.shape)
+    dv = np.zeros(v.shape)
+    for t in range(width):
+        j, valid = keys[t], valids[t]
+        dqr += scale * dS[t][..., None] * _rep(kr[:, j], g)
+        dkt = scale * (dS[t][..., None] * qr).reshape(B, n, hkv, g, d).sum(axis=3)
+        dvt = (P[t][..., None] * do).reshape(B, n, hkv, g, d).sum(axis=3)
+        iv = np.nonzero(valid)[0]
+        np.add.at(dkr, (slice(None), j[iv]), dkt[:, iv])
+        np.add.at(dv, (slice(None), j[iv]), dvt[:, iv])
+    return {
+        "dq": _rope.rotate_back(dqr, rope_base),
+        "dk": _rope.rotate_back(dkr, rope_base),
+        "dv": dv,
+        "o": o,
+        "lse": np.transpose(lse, (0, 2, 1)).copy(),
+    }

@@ -264,3 +264,53 @@ def test_backward_matches_autograd_of_dense_formulation():
     assert np.abs(tq.grad.numpy() - g["dq"]).max() < 1e-11
     assert np.abs(tk.grad.numpy() - g["dk"]).max() < 1e-11
     assert np.abs(tv.grad.numpy() - g["dv"]).max() < 1e-11
+
+
+# ------------------------------------------------------- edge-list backward
+
+def _torch_rope(x, base):
+    d, n = x.shape[-1], x.shape[1]
+    th = base ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
+    ang = torch.arange(n, dtype=torch.float64)[:, None] * th[None]
+    rot = torch.polar(torch.ones_like(ang), ang)[None, :, None, :]
+    z = torch.view_as_complex(x.reshape(*x.shape[:-1], d // 2, 2).contiguous())
+    return torch.view_as_real(z * rot).reshape(x.shape)
+
+
+def test_transpose_edges_brute_force():
+    n = 90
+    edges, count = powerlaw.edge_lists(n, 3, 0.8, 9, 20, seed=7)
+    inv, inv_count = A.transpose_edges(edges, count)
+    width = edges.shape[1]
+    assert inv_count.sum() == count.sum()
+    for j in range(n):
+        row = inv[j, : inv_count[j]]
+        assert np.all(np.diff(row) > 0) and np.all(inv[j, inv_count[j]:] == -1)
+        for s in row:
+            i, t = divmod(int(s), width)
+            assert t < count[i] and edges[i, t] == j
+    for i in range(n):
+        for t in range(count[i]):
+            assert i * width + t in inv[edges[i, t], : inv_count[edges[i, t]]]
+
+
+def test_edge_backward_matches_autograd_of_dense_masked_attention():
+    # Bidirectional lists that include the query itself, GQA 4/2, RoPE.
+    B, n, hq, hkv, d = 2, 40, 4, 2, 8
+    q, k, v, do = (_rand((B, n, h, d), s) for h, s in ((hq, 31), (hkv, 32), (hkv, 33), (hq, 34)))
+    edges, count = powerlaw.edge_lists(n, 2, 0.8, 5, 12, seed=3)
+    g = A.backward_edges(q, k, v, do, edges, count, 1e4)
+    M = torch.full((n, n), -math.inf, dtype=torch.float64)
+    for i in range(n):
+        M[i, torch.from_numpy(edges[i, : count[i]].astype(np.int64))] = 0.0
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    qr, kr = _torch_rope(tq, 1e4), _torch_rope(tk, 1e4)
+    kr2, v2 = kr.repeat_interleave(hq // hkv, dim=2), tv.repeat_interleave(hq // hkv, dim=2)
+    s = torch.einsum("bihd,bjhd->bhij", qr, kr2) / math.sqrt(d) + M
+    o = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, dim=-1), v2)
+    assert np.abs(o.detach().numpy() - g["o"]).max() < 1e-12
+    (o * torch.from_numpy(do)).sum().backward()
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        assert np.abs(t.grad.numpy() - g[name]).max() < 1e-11, name
+    o2, lse2 = A.forward_edges(q, k, v, edges, count, 1e4)
+    assert np.abs(o2 - g["o"]).max() < 1e-13 and np.abs(lse2 - g["lse"]).max() < 1e-13
