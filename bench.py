@@ -357,6 +357,46 @@ def main():
     log("christoffel step:", christoffel_step["ms_per_step"], ck)
     del ws_c
 
+    # Page 2's power-law layer trained: edge-list forward with LSE + its
+    # backward (inverted table built once on the host), same shape.
+    wp = si.WORKLOADS["ctx2048_powerlaw"]
+    e_h, c_h = sfa.edges_powerlaw(wp["seqlen"], wp["radius"], wp["sigma"], wp["draws"], wp["width"], si.SEED)
+    inv_h, ic_h = sfa.edges_transpose(e_h, c_h)
+    ed, cd, invd, icd = (torch.from_numpy(x).to(dev) for x in (e_h, c_h, inv_h, ic_h))
+    ws_p = torch.empty(sfa.bwd_edges_workspace_bytes(cview(sets[0][0]), cview(sets[0][1]), wp["width"]),
+                       dtype=torch.uint8, device=dev)
+
+    def pstep(t):
+        q, k, v, do = (cview(x) for x in sets[t % NSETS])
+        _, lse_ = sfa.fwd_edges(q, k, v, ed, cd, None, want_lse=True)
+        sfa.bwd_edges(q, k, v, lse_, do, ed, cd, invd, icd, None, workspace=ws_p)
+
+    for t in range(args.warmup):
+        pstep(t)
+    torch.cuda.synchronize()
+    sfa.profile_reset()
+    sfa.profile_enable(True)
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        pstep(t)
+    torch.cuda.synchronize()
+    pwall = time.perf_counter() - t0
+    sfa.profile_enable(False)
+    pk = {}
+    for name in ("fwd_edges", "bwd_edges_query", "bwd_edges_key"):
+        ms_, c_ = sfa.profile_read(name)
+        if c_:
+            pk[name] = round(1e3 * ms_ / c_, 3)
+    powerlaw_step = {
+        "workload": "ctx2048_powerlaw: 8 x 2048, 4/4 heads, D 64, bf16, 64-wide bidirectional edge lists "
+                    "(mean %.1f keys), forward with LSE + backward" % float(c_h.mean()),
+        "ms_per_step": round(1e3 * pwall / args.steps, 4),
+        "queries_per_s": round(Bc * nc / (pwall / args.steps), 1),
+        "kernels_avg_us": pk,
+    }
+    log("power-law step:", powerlaw_step["ms_per_step"], pk)
+    del ws_p
+
     out = {
         "metric": METRIC,
         "value": round(B * n / (ms_per_step * 1e-3), 1),
@@ -383,6 +423,7 @@ def main():
         "fwd_only": fwd_only,
         "integer_vs_learned": integer_vs_learned,
         "christoffel_step": christoffel_step,
+        "powerlaw_step": powerlaw_step,
         "length_extrapolation": {"workload": "page-1 layer forward, W 8, 32,768 tokens per batch", "by_seqlen": lengths},
     }
     if not args.no_cpu_baseline:

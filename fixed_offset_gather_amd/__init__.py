@@ -82,12 +82,16 @@ _sig("sfa_alpha_of_theta", _c.c_int, [_c.c_double, _c.POINTER(_c.c_double), _c.P
 _sig("sfa_offsets_christoffel", _c.c_int, [_c.c_int, _c.c_int, _i32p, _c.c_int])
 _sig("sfa_edges_powerlaw", _c.c_int, [_c.c_int, _c.c_int, _c.c_double, _c.c_int, _c.c_int,
                                       _c.c_uint64, _i32p, _i32p])
+_sig("sfa_edges_transpose", _c.c_int, [_c.c_int, _c.c_int, _i32p, _i32p, _c.c_int, _i32p, _i32p])
 _sig("sfa_rope_table", _c.c_int, [_c.c_int, _c.c_int, _c.c_double, _f32p])
 _sig("sfa_fwd", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _vp, _vp, _vp, _vp])
 _sig("sfa_fwd_edges", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _c.c_int, _vp, _vp, _vp, _vp, _vp, _vp])
 _sig("sfa_bwd_workspace_bytes", _c.c_size_t, [_c.POINTER(SfaAttn)])
 _sig("sfa_bwd", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _vp, _i32p, _c.c_double, _vp, _vp, _c.c_size_t, _vp])
+_sig("sfa_bwd_edges_workspace_bytes", _c.c_size_t, [_c.POINTER(SfaAttn), _c.c_int])
+_sig("sfa_bwd_edges", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _c.c_int, _vp, _vp, _c.c_int, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _c.c_size_t, _vp])
 _sig("sfa_profile_enable", _c.c_int, [_c.c_int])
 _sig("sfa_profile_read", _c.c_int, [_c.c_char_p, _c.POINTER(_c.c_double), _c.POINTER(_c.c_int64)])
 _sig("sfa_profile_reset", _c.c_int, [])
@@ -182,6 +186,19 @@ def edges_powerlaw(n, r, sigma, draws, width, seed):
            _lib.sfa_edges_powerlaw(n, r, float(sigma), draws, width, int(seed) & (2**64 - 1),
                                    _ip(edges), _ip(count)))
     return edges, count
+
+
+def edges_transpose(edges, count):
+    """Inverted edge table (host): (inv int32 [n, cap] -1 padded, inv_count int32 [n])."""
+    edges = np.ascontiguousarray(edges, dtype=np.int32)
+    count = np.ascontiguousarray(count, dtype=np.int32)
+    n, width = edges.shape
+    cap = _check("sfa_edges_transpose", _lib.sfa_edges_transpose(n, width, _ip(edges), _ip(count), 0, None, None))
+    inv = np.zeros((n, cap), dtype=np.int32)
+    inv_count = np.zeros(n, dtype=np.int32)
+    _check("sfa_edges_transpose",
+           _lib.sfa_edges_transpose(n, width, _ip(edges), _ip(count), cap, _ip(inv), _ip(inv_count)))
+    return inv, inv_count
 
 
 def rope_table(n, head_dim, theta):
@@ -332,6 +349,40 @@ def bwd(q, k, v, lse, dout, window=0, lo=None, frac=None, rope=None, scale=0.0,
         _ptr(dd), None if base_arr is None else _ip(base_arr), float(alpha or 0.0), _ptr(dth),
         _ptr(workspace), workspace.numel(), _stream(q)))
     return dq, dk, dv, dd, dth
+
+
+def bwd_edges_workspace_bytes(q, k, width, rope=None, scale=0.0):
+    pr = Problem(q, k, 0, None, None, rope, scale)
+    nb = _lib.sfa_bwd_edges_workspace_bytes(pr.ref(), int(width))
+    if nb == 0 and q.numel() > 0:
+        raise SfaError("sfa_bwd_edges_workspace_bytes", -1)
+    return nb
+
+
+def bwd_edges(q, k, v, lse, dout, edges, count, inv, inv_count, rope=None, scale=0.0, workspace=None):
+    """Edge-list backward: returns (dq, dk, dv).  edges/count/inv/inv_count
+    are device int32 tensors ([n, width], [n], [n, cap], [n])."""
+    torch = _torch()
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _require(t, nm, q.dtype)
+    B, n, hq, d = q.shape
+    _require(lse, "lse", torch.float32, (B, hq, n))
+    for t, nm in ((edges, "edges"), (count, "count"), (inv, "inv"), (inv_count, "inv_count")):
+        _require(t, nm, torch.int32)
+    if edges.dim() != 2 or edges.shape[0] != n or inv.dim() != 2 or inv.shape[0] != n:
+        raise ValueError("edges and inv must be [n, width] and [n, cap]")
+    if count.shape != (n,) or inv_count.shape != (n,):
+        raise ValueError("count and inv_count must be [n]")
+    pr = Problem(q, k, 0, None, None, rope, scale)
+    nb = _lib.sfa_bwd_edges_workspace_bytes(pr.ref(), int(edges.shape[1]))
+    if workspace is None:
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    _check("sfa_bwd_edges", _lib.sfa_bwd_edges(
+        pr.ref(), _ptr(edges), _ptr(count), int(edges.shape[1]), _ptr(inv), _ptr(inv_count), int(inv.shape[1]),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), workspace.numel(), _stream(q)))
+    return dq, dk, dv
 
 
 # ------------------------------------------------------------ timing

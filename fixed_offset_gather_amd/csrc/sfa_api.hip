@@ -221,6 +221,56 @@ extern "C" int sfa_fwd_edges(const sfa_attn* a, const int32_t* edges, const int3
                     "sfa_fwd_edges launch");
 }
 
+// Edge-list problems ignore window and offsets, as sfa_fwd_edges does.
+static int validate_edges_problem(const sfa_attn* a, Problem* p) {
+  if (!a) return fail(SFA_ERR_ARG, "problem is NULL");
+  sfa_attn b = *a;
+  b.window = 0;
+  b.n_off = 0;
+  return validate_problem(&b, p);
+}
+
+extern "C" size_t sfa_bwd_edges_workspace_bytes(const sfa_attn* a, int width) {
+  clear_error();
+  Problem p;
+  if (validate_edges_problem(a, &p)) return 0;
+  if (width < 1 || width > SFA_MAX_EDGE_WIDTH) {
+    fail(SFA_ERR_ARG, "sfa_bwd_edges_workspace_bytes: width must be in [1, %d]", SFA_MAX_EDGE_WIDTH);
+    return 0;
+  }
+  return bwd_edges_workspace_layout(p, width, nullptr, nullptr, nullptr, nullptr);
+}
+
+extern "C" int sfa_bwd_edges(const sfa_attn* a, const int32_t* edges, const int32_t* count, int width,
+                             const int32_t* inv, const int32_t* inv_count, int inv_width, const void* q,
+                             const void* k, const void* v, const float* lse, const void* dout, void* dq, void* dk,
+                             void* dv, void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  Problem p;
+  int rc = validate_edges_problem(a, &p);
+  if (rc) return rc;
+  if (width < 1 || width > SFA_MAX_EDGE_WIDTH)
+    return fail(SFA_ERR_ARG, "sfa_bwd_edges: width must be in [1, %d]", SFA_MAX_EDGE_WIDTH);
+  if (inv_width < 1) return fail(SFA_ERR_ARG, "sfa_bwd_edges: inv_width must be >= 1");
+  if (int64_t(p.n) * width > (int64_t(1) << 31) - 1)
+    return fail(SFA_ERR_ARG, "sfa_bwd_edges: n * width exceeds int32 slot indices");
+  if (p.B == 0 || p.n == 0) return SFA_OK;
+  if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv || !edges || !count || !inv || !inv_count)
+    return fail(SFA_ERR_ARG, "sfa_bwd_edges: NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(edges) & 3u) ||
+      (reinterpret_cast<uintptr_t>(count) & 3u) || (reinterpret_cast<uintptr_t>(inv) & 3u) ||
+      (reinterpret_cast<uintptr_t>(inv_count) & 3u))
+    return fail(SFA_ERR_ARG, "sfa_bwd_edges: misaligned pointer");
+  const size_t need = bwd_edges_workspace_layout(p, width, nullptr, nullptr, nullptr, nullptr);
+  if (!workspace || ws_bytes < need || !aligned16(workspace))
+    return fail(SFA_ERR_CAPACITY, "sfa_bwd_edges: workspace needs %zu bytes (16-byte aligned), got %zu", need,
+                ws_bytes);
+  return hip_status(launch_bwd_edges(p, edges, count, width, inv, inv_count, inv_width, q, k, v, lse, dout, dq,
+                                     dk, dv, workspace, stream),
+                    "sfa_bwd_edges launch");
+}
+
 extern "C" size_t sfa_bwd_workspace_bytes(const sfa_attn* a) {
   clear_error();
   Problem p;

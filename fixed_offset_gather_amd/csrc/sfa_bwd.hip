@@ -891,6 +891,229 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
     else SFA_DISPATCH_D(float, FN, (P).D, (P).G, __VA_ARGS__);   \
   } while (0)
 
+
+// ------------------------------------------------------- edge-list backward
+// Training with per-query key lists ("Critical power-law sparse attention",
+// item 4; "Christoffel-Balanced Sparse Attention"): gradients of
+// L = <O, dO> for the edge-list forward, one plain key per slot.
+//
+// bwd_edges_query: per query, the same lane layout as the offset query pass
+//   with keys read straight from global memory (L2-resident per KV head):
+//   p = exp(logit - lse), dp = dO . v_j, Dvec = sum p dp, dq~ = scale
+//   (sum p dp k~_j - Dvec sum p k~_j); p and dp of every valid slot go to
+//   the workspace.
+// bwd_edges_key: per key j (one lane, 16 dims), the slots that name j from
+//   the inverted table in ascending order: dK~_j = sum R(i) scale sum_h dS_h
+//   q_h(i), dV_j = sum sum_h p_h dO_h(i); dK = R(j)^T dK~.  No atomics, fixed
+//   order.
+struct EdgeBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* P;     // [B*Hkv][n][width][G]
+  float* dP;    // [B*Hkv][n][width][G]
+  float* Dvec;  // [B*Hkv][n][G]
+  const float* rope;
+  const int32_t* edges;
+  const int32_t* count;
+  const int32_t* inv;
+  const int32_t* inv_count;
+  int width, inv_width;
+  int n, hq, hkv, nblk, tiles;
+  float scale, scale_log2;
+};
+
+constexpr int kEdgeBQ = 32;  // queries per bwd_edges_query workgroup
+constexpr int kEdgeKB = 64;  // keys per bwd_edges_key workgroup (one wave)
+
+template <typename T, int D, int G, int LPQ>
+__global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdArgs a) {
+  constexpr int DC = D / LPQ;
+  const int tid = threadIdx.x;
+  const int qq = tid / LPQ;
+  const int c = tid % LPQ;
+  const int own = c % G;
+  const int tile = xcd_tile(blockIdx.x, a.tiles);
+  const int seq = tile / a.nblk;
+  const int blk = tile % a.nblk;
+  const int b = seq / a.hkv, g = seq % a.hkv;
+  const int n = a.n;
+  const int i = blk * kEdgeBQ + qq;
+  const bool active = i < n;
+
+  const T* __restrict__ Q = static_cast<const T*>(a.q);
+  const T* __restrict__ dO = static_cast<const T*>(a.dout);
+  const size_t kv_row = size_t(a.hkv) * D;
+  const T* Kseq = static_cast<const T*>(a.k) + size_t(b) * n * kv_row + size_t(g) * D + c * DC;
+  const T* Vseq = static_cast<const T*>(a.v) + size_t(b) * n * kv_row + size_t(g) * D + c * DC;
+
+  float qv[G][DC], dov[G][DC], acc_pd[G][DC], acc_p[G][DC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (active) {
+      const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC;
+      load_vec<DC>(Q + off, qv[h]);
+      if (a.rope) rotate_pairs<DC, 1>(qv[h], a.rope + size_t(i) * D, c * DC);
+      load_vec<DC>(dO + off, dov[h]);
+    } else {
+#pragma unroll
+      for (int x = 0; x < DC; ++x) qv[h][x] = dov[h][x] = 0.f;
+    }
+#pragma unroll
+    for (int x = 0; x < DC; ++x) acc_pd[h][x] = acc_p[h][x] = 0.f;
+  }
+  const float lse2 = active ? a.lse[(size_t(b) * a.hq + size_t(g) * G + own) * n + i] * kLog2e : 0.f;
+  const int cnt = active ? min(a.count[i], a.width) : 0;
+  int cmax = cnt;  // wave-uniform trip count: the longest list of the wavefront
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) cmax = max(cmax, __shfl_xor(cmax, msk));
+  const int32_t* erow = a.edges + size_t(active ? i : 0) * a.width;
+  const size_t wrow = (size_t(seq) * n + (active ? i : 0)) * a.width;
+  float dvec = 0.f;
+
+  for (int t = 0; t < cmax; ++t) {
+    const int key = t < cnt ? erow[t] : -1;
+    const bool valid = key >= 0 && key < n;
+    float kt[DC], vt[DC];
+    if (valid) {
+      load_vec<DC>(Kseq + size_t(key) * kv_row, kt);
+      if (a.rope) rotate_pairs<DC, 1>(kt, a.rope + size_t(key) * D, c * DC);
+      load_vec<DC>(Vseq + size_t(key) * kv_row, vt);
+    } else {
+#pragma unroll
+      for (int x = 0; x < DC; ++x) kt[x] = vt[x] = 0.f;
+    }
+    const float sdot = own_dot<G, LPQ, DC>(qv, kt, own);
+    const float dp = own_dot<G, LPQ, DC>(dov, vt, own);
+    const float p = valid ? __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2) : 0.f;
+    const float pdp = p * dp;
+    dvec += pdp;
+    if (valid && c < G) {
+      a.P[(wrow + t) * G + c] = p;
+      a.dP[(wrow + t) * G + c] = dp;
+    }
+    float ph[G], pdh[G];
+    Bc<G, LPQ>::run(p, ph);
+    Bc<G, LPQ>::run(pdp, pdh);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int x = 0; x < DC; ++x) {
+        acc_pd[h][x] = fmaf(pdh[h], kt[x], acc_pd[h][x]);
+        acc_p[h][x] = fmaf(ph[h], kt[x], acc_p[h][x]);
+      }
+  }
+
+  if (active && c < G) a.Dvec[(size_t(seq) * n + i) * G + c] = dvec;
+  float dvh[G];
+  Bc<G, LPQ>::run(dvec, dvh);
+  if (active) {
+    T* dQ = static_cast<T*>(a.dq);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float dq[DC];
+#pragma unroll
+      for (int x = 0; x < DC; ++x) dq[x] = a.scale * fmaf(-dvh[h], acc_p[h][x], acc_pd[h][x]);
+      if (a.rope) rotate_pairs<DC, -1>(dq, a.rope + size_t(i) * D, c * DC);
+      store_vec<DC>(dQ + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, dq);
+    }
+  }
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kEdgeKB) void bwd_edges_key_kernel(EdgeBwdArgs a) {
+  constexpr int KC = key_chunk(D);
+  constexpr int NCH = D / KC;
+  const int tid = threadIdx.x;
+  const int tile = xcd_tile(blockIdx.x, a.tiles);
+  const int c = tile % NCH;
+  const int rest = tile / NCH;
+  const int seq = rest / a.nblk;
+  const int blk = rest % a.nblk;
+  const int b = seq / a.hkv, g = seq % a.hkv;
+  const int n = a.n;
+  const int j = blk * kEdgeKB + tid;
+  const bool activej = j < n;
+
+  const T* __restrict__ Q = static_cast<const T*>(a.q);
+  const T* __restrict__ dO = static_cast<const T*>(a.dout);
+  const int cnt = activej ? min(a.inv_count[j], a.inv_width) : 0;
+  int cmax = cnt;
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) cmax = max(cmax, __shfl_xor(cmax, msk));
+  const int32_t* irow = a.inv + size_t(activej ? j : 0) * a.inv_width;
+  const int64_t nslots = int64_t(n) * a.width;
+
+  float ak[KC], av[KC];
+#pragma unroll
+  for (int x = 0; x < KC; ++x) ak[x] = av[x] = 0.f;
+  for (int u = 0; u < cmax; ++u) {
+    const int e = u < cnt ? irow[u] : -1;
+    if (e >= 0 && e < nslots) {  // anything else is not a slot of the table
+      const int i = e / a.width, t = e - i * a.width;
+      const size_t w = ((size_t(seq) * n + i) * a.width + t) * G;
+      float pg[G], dpg[G], dvg[G];
+      load_vec<G>(a.P + w, pg);
+      load_vec<G>(a.dP + w, dpg);
+      load_vec<G>(a.Dvec + (size_t(seq) * n + i) * G, dvg);
+      float yk[KC], yv[KC];
+#pragma unroll
+      for (int x = 0; x < KC; ++x) yk[x] = yv[x] = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * KC;
+        const float ds = a.scale * pg[h] * (dpg[h] - dvg[h]);
+        float qx[KC], ox[KC];
+        load_vec<KC>(Q + off, qx);
+        load_vec<KC>(dO + off, ox);
+#pragma unroll
+        for (int x = 0; x < KC; ++x) {
+          yk[x] = fmaf(ds, qx[x], yk[x]);
+          yv[x] = fmaf(pg[h], ox[x], yv[x]);
+        }
+      }
+      if (a.rope) rotate_pairs<KC, 1>(yk, a.rope + size_t(i) * D, c * KC);  // into the frame of position i
+#pragma unroll
+      for (int x = 0; x < KC; ++x) {
+        ak[x] += yk[x];
+        av[x] += yv[x];
+      }
+    }
+  }
+  if (activej) {
+    if (a.rope) rotate_pairs<KC, -1>(ak, a.rope + size_t(j) * D, c * KC);  // dK = R(j)^T dK~
+    const size_t kv_off = (size_t(b) * n + j) * size_t(a.hkv) * D + size_t(g) * D + c * KC;
+    store_vec<KC>(static_cast<T*>(a.dk) + kv_off, ak);
+    store_vec<KC>(static_cast<T*>(a.dv) + kv_off, av);
+  }
+}
+
+template <typename T, int D, int G>
+int launch_edges_t(const EdgeBwdArgs& a0, hipStream_t st) {
+  constexpr int LPQ = bwd_lpq<D, G>();
+  EdgeBwdArgs a = a0;
+  const int seqs = a0.tiles;  // B * hkv on entry
+  {
+    ProfileScope ps("bwd_edges_query", st);
+    a.nblk = (a.n + kEdgeBQ - 1) / kEdgeBQ;
+    a.tiles = a.nblk * seqs;
+    hipLaunchKernelGGL((bwd_edges_query_kernel<T, D, G, LPQ>), dim3(a.tiles), dim3(kEdgeBQ * LPQ), 0, st, a);
+  }
+  if (hipError_t e = hipGetLastError()) return int(e);
+  {
+    ProfileScope ps("bwd_edges_key", st);
+    a.nblk = (a.n + kEdgeKB - 1) / kEdgeKB;
+    a.tiles = a.nblk * seqs * (D / key_chunk(D));
+    hipLaunchKernelGGL((bwd_edges_key_kernel<T, D, G>), dim3(a.tiles), dim3(kEdgeKB), 0, st, a);
+  }
+  return int(hipGetLastError());
+}
+
 }  // namespace
 
 size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, BwdWorkspace* ws) {
@@ -953,6 +1176,49 @@ int launch_bwd_reduce(const SlotTable& t, const BwdWorkspace& ws, const float* b
   for (int k = 0; k < t.n_rungs; ++k) a.base[k] = base_f[k];
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, static_cast<hipStream_t>(stream), a);
   return int(hipGetLastError());
+}
+
+size_t bwd_edges_workspace_layout(const Problem& p, int width, void* base, float** P, float** dP, float** Dvec) {
+  auto al = [](size_t e) { return (e + 63) & ~size_t(63); };
+  const size_t pe = al(size_t(p.B) * p.hkv * size_t(p.n) * size_t(width) * p.G);
+  const size_t de = al(size_t(p.B) * p.hkv * size_t(p.n) * p.G);
+  float* f = static_cast<float*>(base);
+  if (P) *P = f;
+  if (dP) *dP = f ? f + pe : nullptr;
+  if (Dvec) *Dvec = f ? f + 2 * pe : nullptr;
+  return (2 * pe + de) * sizeof(float);
+}
+
+int launch_bwd_edges(const Problem& p, const int32_t* edges, const int32_t* count, int width, const int32_t* inv,
+                     const int32_t* inv_count, int inv_width, const void* q, const void* k, const void* v,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                     void* stream) {
+  EdgeBwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  bwd_edges_workspace_layout(p, width, workspace, &a.P, &a.dP, &a.Dvec);
+  a.rope = p.rope;
+  a.edges = edges;
+  a.count = count;
+  a.inv = inv;
+  a.inv_count = inv_count;
+  a.width = width;
+  a.inv_width = inv_width;
+  a.n = p.n;
+  a.hq = p.hq;
+  a.hkv = p.hkv;
+  a.nblk = 1;
+  a.tiles = p.B * p.hkv;
+  a.scale = p.scale;
+  a.scale_log2 = p.scale * kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  SFA_DISPATCH(launch_edges_t, p, a, st);
 }
 
 }  // namespace sfa

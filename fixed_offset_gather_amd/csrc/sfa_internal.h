@@ -58,6 +58,15 @@ struct BwdWorkspace {
 size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base,
                             BwdWorkspace* ws);
 
+// Edge-list backward: workspace p, dp [B*Hkv][n][width][G] and Dvec
+// [B*Hkv][n][G] (floats); returns its size in bytes.
+size_t bwd_edges_workspace_layout(const Problem& p, int width, void* base, float** P, float** dP,
+                                  float** Dvec);
+int launch_bwd_edges(const Problem& p, const int32_t* edges, const int32_t* count, int width,
+                     const int32_t* inv, const int32_t* inv_count, int inv_width, const void* q,
+                     const void* k, const void* v, const float* lse, const void* dout, void* dq,
+                     void* dk, void* dv, void* workspace, void* stream);
+
 int launch_bwd_query(const Problem& p, const SlotTable& t, const void* q,
                      const void* k, const void* v, const float* lse,
                      const void* dout, void* dq, const BwdWorkspace& ws,

@@ -211,6 +211,44 @@ extern "C" int sfa_edges_powerlaw(int n, int r, double sigma, int draws,
   return maxc;
 }
 
+// Inverted edge table for the key-side gather of the edge-list backward
+// (training with the per-query masks of "Critical power-law sparse
+// attention", item 4, and "Christoffel-Balanced Sparse Attention"): for
+// every key j the slots s = i * width + t with edges[i][t] = j, ascending.
+extern "C" int sfa_edges_transpose(int n, int width, const int32_t* edges, const int32_t* count, int cap,
+                                   int32_t* inv, int32_t* inv_count) {
+  if (n < 0 || width < 1 || width > SFA_MAX_EDGE_WIDTH)
+    return fail(SFA_ERR_ARG, "sfa_edges_transpose: bad n/width");
+  if (n > 0 && (!edges || !count)) return fail(SFA_ERR_ARG, "sfa_edges_transpose: NULL edges or count");
+  if (int64_t(n) * width > (int64_t(1) << 31) - 1)
+    return fail(SFA_ERR_ARG, "sfa_edges_transpose: n * width exceeds int32 slot indices");
+  std::vector<int32_t> deg(size_t(n), 0);
+  for (int i = 0; i < n; ++i) {
+    if (count[i] < 0 || count[i] > width)
+      return fail(SFA_ERR_ARG, "sfa_edges_transpose: count[%d] = %d not in [0, width]", i, count[i]);
+    for (int t = 0; t < count[i]; ++t) {
+      const int32_t j = edges[size_t(i) * size_t(width) + t];
+      if (j < 0 || j >= n) return fail(SFA_ERR_ARG, "sfa_edges_transpose: edges[%d][%d] = %d out of range", i, t, j);
+      ++deg[size_t(j)];
+    }
+  }
+  int need = 1;
+  for (int j = 0; j < n; ++j) need = std::max(need, int(deg[size_t(j)]));
+  if (!inv) return need;  // size query
+  if (!inv_count) return fail(SFA_ERR_ARG, "sfa_edges_transpose: inv_count is NULL");
+  if (cap < need) return fail(SFA_ERR_CAPACITY, "sfa_edges_transpose: needs cap >= %d, got %d", need, cap);
+  for (int j = 0; j < n; ++j) {
+    inv_count[j] = 0;
+    for (int u = 0; u < cap; ++u) inv[size_t(j) * size_t(cap) + u] = -1;
+  }
+  for (int i = 0; i < n; ++i)
+    for (int t = 0; t < count[i]; ++t) {
+      const int32_t j = edges[size_t(i) * size_t(width) + t];
+      inv[size_t(j) * size_t(cap) + size_t(inv_count[j]++)] = i * width + t;
+    }
+  return need;
+}
+
 // Rotary table: "Depth-Staggered Fibonacci Spacing for Sparse Attention",
 // gather paragraph (rotation at true positions before the gather) and
 // architecture paragraph (base 1e4); rotation of interleaved pairs.

@@ -145,6 +145,20 @@ int sfa_edges_powerlaw(int n, int r, double sigma, int draws, int width,
                        uint64_t seed, int32_t* edges, int32_t* count);
 
 /*
+ * Inverted edge table for the edge-list backward (key-side gather): pages
+ * 2 and 3 propose training with these masks ([P2] item 4, [P3]).  For every
+ * key j, inv[j][0..inv_count[j]) lists the slots s = i * width + t with
+ * t < count[i] and edges[i][t] = j, in ascending order (-1 padded to cap).
+ * edges/count as produced by sfa_edges_powerlaw (host, int32 [n][width] and
+ * [n]); every listed key must lie in [0, n).  inv == NULL: returns the cap
+ * needed (largest in-degree, at least 1) without writing.  Otherwise inv is
+ * int32 [n][cap] and inv_count int32 [n], both caller-owned; returns the cap
+ * needed, or SFA_ERR_CAPACITY if cap is smaller, SFA_ERR_ARG on bad input.
+ */
+int sfa_edges_transpose(int n, int width, const int32_t* edges, const int32_t* count, int cap, int32_t* inv,
+                        int32_t* inv_count);
+
+/*
  * Rotary table of [P1] gather and architecture paragraphs (Su et al.
  * rotation of interleaved pairs): table[m][p][0] = cos(m * theta^(-2p/D)),
  * table[m][p][1] = sin(...), computed in fp64 and stored as float, for
@@ -250,10 +264,29 @@ int sfa_bwd(const sfa_attn* a, const void* q, const void* k, const void* v,
 /* ------------------------------------------------------------------ */
 
 /*
+ * Backward of sfa_fwd_edges for L = <O, dO> (training with the per-query
+ * masks: [P2] item 4, [P3]).  edges/count: the device lists of the forward;
+ * inv/inv_count: their transpose from sfa_edges_transpose (device copies of
+ * the host output, int32 [n][inv_width] and [n]); inv must be the transpose
+ * of exactly these lists.  lse: the forward's [B][Hq][n] log-sum-exp.  Writes
+ * dQ (like q), dK, dV (like k) in the input dtype.  Window and offsets of
+ * `a` are ignored.  The workspace (device, 16-byte aligned, at least
+ * sfa_bwd_edges_workspace_bytes(a, width) bytes) holds p and dp of every
+ * slot and Dvec between the two launches.  Deterministic: no atomics, fixed
+ * summation order.  Errors as sfa_bwd.
+ */
+size_t sfa_bwd_edges_workspace_bytes(const sfa_attn* a, int width);
+int sfa_bwd_edges(const sfa_attn* a, const int32_t* edges, const int32_t* count, int width,
+                  const int32_t* inv, const int32_t* inv_count, int inv_width, const void* q,
+                  const void* k, const void* v, const float* lse, const void* dout, void* dq,
+                  void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * When enabled, every kernel launch is bracketed by two HIP events recorded
  * on its launch stream.  sfa_profile_read synchronises the recorded events
  * and returns the accumulated milliseconds and launch count of the named
  * kernel ("fwd_offsets", "fwd_edges", "bwd_query", "bwd_key",
+ * "bwd_edges_query", "bwd_edges_key",
  * "bwd_reduce"; with bf16 tensors the key pass is the two kernels
  * "bwd_key_dk" and "bwd_key_dv" instead of "bwd_key");
  * sfa_profile_reset drops all records.  Not thread-safe with

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import fixed_offset_gather_amd as sfa
+from oracle import attention as ref_att
 from oracle import christoffel as ref_chr
 from oracle import offsets as ref_off
 from oracle import powerlaw as ref_pl
@@ -207,3 +208,47 @@ def test_producer_errors():
         sfa.edges_powerlaw(64, 8, 0.8, 30, 8, 0)   # lists exceed the width
     with pytest.raises(sfa.SfaError):
         sfa.rope_table(8, 7, 1e4)
+
+
+@pytest.mark.parametrize("n,r,sigma,draws,width,seed", [(2048, 8, 0.8, 47, 64, 42), (90, 3, 0.8, 9, 20, 7)])
+def test_edges_transpose_bit_exact(n, r, sigma, draws, width, seed):
+    edges, count = sfa.edges_powerlaw(n, r, sigma, draws, width, seed)
+    inv, inv_count = sfa.edges_transpose(edges, count)
+    rinv, rcount = ref_att.transpose_edges(edges, count)
+    assert np.array_equal(inv, rinv) and np.array_equal(inv_count, rcount)
+
+
+def test_edges_transpose_errors():
+    lib = sfa.library()
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    edges = np.array([[1, 2], [0, -1], [0, 1]], dtype=np.int32)
+    count = np.array([2, 1, 2], dtype=np.int32)
+    inv = np.zeros((3, 1), dtype=np.int32)
+    ic = np.zeros(3, dtype=np.int32)
+    assert lib.sfa_edges_transpose(3, 2, ip(edges), ip(count), 0, None, None) == 2   # size query
+    assert lib.sfa_edges_transpose(3, 2, ip(edges), ip(count), 1, ip(inv), ip(ic)) == sfa.SFA_ERR_CAPACITY
+    bad = edges.copy(); bad[1, 0] = 3
+    assert lib.sfa_edges_transpose(3, 2, ip(bad), ip(count), 0, None, None) == sfa.SFA_ERR_ARG
+    badc = count.copy(); badc[0] = 3
+    assert lib.sfa_edges_transpose(3, 2, ip(edges), ip(badc), 0, None, None) == sfa.SFA_ERR_ARG
+    assert lib.sfa_edges_transpose(3, 0, ip(edges), ip(count), 0, None, None) == sfa.SFA_ERR_ARG
+
+
+def test_bwd_edges_validation_and_workspace_size():
+    # Every case below is invalid, so no call reaches a device.
+    lib = sfa.library()
+    a = _prob(batch=2, seqlen=100, hq=4, hkv=4)
+    al = lambda e: (e + 63) // 64 * 64
+    nb = lib.sfa_bwd_edges_workspace_bytes(ctypes.byref(a), 64)
+    assert nb == (2 * al(2 * 4 * 100 * 64 * 1) + al(2 * 4 * 100 * 1)) * 4
+    assert lib.sfa_bwd_edges_workspace_bytes(ctypes.byref(a), 0) == 0
+    t = [FAKE] * 8  # q, k, v, lse, dout, dq, dk, dv
+    call = lambda width, invw, ws, wsb, ptrs=t, e=FAKE: lib.sfa_bwd_edges(
+        ctypes.byref(a), e, FAKE, width, FAKE, FAKE, invw, *ptrs, ws, wsb, None)
+    assert call(0, 8, FAKE, nb) == sfa.SFA_ERR_ARG             # width
+    assert call(64, 0, FAKE, nb) == sfa.SFA_ERR_ARG            # inv_width
+    assert call(64, 8, FAKE, nb - 4) == sfa.SFA_ERR_CAPACITY   # workspace too small
+    assert call(64, 8, MISALIGNED, nb) == sfa.SFA_ERR_CAPACITY
+    assert call(64, 8, FAKE, nb, ptrs=[None] + t[1:]) == sfa.SFA_ERR_ARG
+    assert call(64, 8, FAKE, nb, ptrs=t[:5] + [MISALIGNED] + t[6:]) == sfa.SFA_ERR_ARG
+    assert call(64, 8, FAKE, nb, e=ctypes.c_void_p(0x100002)) == sfa.SFA_ERR_ARG   # edges misaligned

@@ -416,6 +416,43 @@ def test_backward_more_than_64_slots_with_dd(dtype):
                grad_tol=1e-4 if dtype == "f32" else 1e-2)
 
 
+def _edge_bwd_check(case, edges, count, sel=slice(None), tol=None):
+    sfa = _sfa()
+    ed, cd = torch.from_numpy(edges).to(DEV), torch.from_numpy(count).to(DEV)
+    inv, ic = sfa.edges_transpose(edges, count)
+    invd, icd = torch.from_numpy(inv).to(DEV), torch.from_numpy(ic).to(DEV)
+    o, lse = sfa.fwd_edges(case.qd, case.kd, case.vd, ed, cd, case.rope, want_lse=True)
+    dq, dk, dv = sfa.bwd_edges(case.qd, case.kd, case.vd, lse, case.dod, ed, cd, invd, icd, case.rope)
+    torch.cuda.synchronize()
+    g = ref.backward_edges(*case.f64(sel), edges, count, case.rope_theta)
+    tol = tol or TOL[case.dtype]
+    errs = {nm: _excess(_np(t)[sel], g[nm], case.dtype) for nm, t in (("dq", dq), ("dk", dk), ("dv", dv))}
+    print("edge bwd max err beyond output rounding", {k_: "%.3g" % e for k_, e in errs.items()}, flush=True)
+    for nm, e in errs.items():
+        assert e <= tol, nm
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("hq,hkv,D", [(8, 2, 64), (4, 4, 64), (2, 1, 32), (8, 1, 16)])
+@pytest.mark.parametrize("theta", [1e4, 0.0])
+def test_edge_backward_multi_tile_ragged(dtype, hq, hkv, D, theta):
+    sfa = _sfa()
+    case = Case(2, 200, hq, hkv, D, dtype, seed=23, rope_theta=theta)
+    edges, count = sfa.edges_powerlaw(200, 3, 0.8, 12, 24, 11)
+    _edge_bwd_check(case, edges, count, tol=TOL[dtype] if dtype == "bf16" else 2e-5)
+
+
+def test_edge_backward_ctx2048_powerlaw_full_size_and_deterministic():
+    sfa = _sfa()
+    w = si.WORKLOADS["ctx2048_powerlaw"]
+    case = Case(w["batch"], w["seqlen"], w["hq"], w["hkv"], w["head_dim"], w["dtype"], rope_theta=0.0)
+    edges, count = sfa.edges_powerlaw(w["seqlen"], w["radius"], w["sigma"], w["draws"], w["width"], si.SEED)
+    a = _edge_bwd_check(case, edges, count, sel=slice(0, 1))
+    b = _edge_bwd_check(case, edges, count, sel=slice(0, 1))
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
 def test_ctx2048_christoffel_full_size():
     sfa = _sfa()
     w = si.WORKLOADS["ctx2048_christoffel"]
