@@ -18,7 +18,10 @@ Conventions and readings:
 * Every window distance and every rung is its own logit slot, even when two
   slots name the same row (duplicates keep their multiplicity).
 * Window slot s is valid iff i - s >= 0; rung k is valid iff i >= d_k, i.e.
-  (i - lo_k) >= frac_k.  Rows at negative positions are zero (they are only
+  (i - lo_k) >= frac_k.  Signed offsets (page 3, "Christoffel-Balanced
+  Sparse Attention": bidirectional attention by signed offsets): a negative
+  integer lo_k names the later row i - lo_k = i + |lo_k|, valid iff it is
+  below n.  Rows at negative positions are zero (they are only
   ever touched with weight 0, at i = lo_k with frac_k = 0).
 * Scale is 1/sqrt(head_dim) unless given.  Query head h uses key/value head
   h // (Hq/Hkv).
@@ -50,22 +53,25 @@ from .offsets import dalpha_dtheta
 
 
 def _shift(x, s):
-    """y[:, i] = x[:, i - s] for i - s in [0, n), else 0 (sequence axis 1)."""
+    """y[:, i] = x[:, i - s] for i - s in [0, n), else 0 (sequence axis 1).
+    A negative s reads later rows (signed offsets of bidirectional layers)."""
     y = np.zeros_like(x)
     n = x.shape[1]
-    if s < 0:
-        raise ValueError("negative shift")
-    if s < n:
+    if 0 <= s < n:
         y[:, s:] = x[:, : n - s]
+    elif -n < s < 0:
+        y[:, : n + s] = x[:, -s:]
     return y
 
 
 def _unshift(x, s):
-    """Adjoint of _shift: y[:, j] = x[:, j + s] for j + s < n, else 0."""
+    """Adjoint of _shift: y[:, j] = x[:, j + s] for j + s in [0, n), else 0."""
     y = np.zeros_like(x)
     n = x.shape[1]
-    if s < n:
+    if 0 <= s < n:
         y[:, : n - s] = x[:, s:]
+    elif -n < s < 0:
+        y[:, -s:] = x[:, : n + s]
     return y
 
 
@@ -102,8 +108,10 @@ def _slot_rows(x, lo, w):
 
 
 def _valid(n, lo, w):
+    # the nearer row i - lo must exist: i >= lo + frac, and for a negative
+    # (future) offset i - lo <= n - 1
     i = np.arange(n, dtype=np.float64)
-    return (i - lo) >= w
+    return ((i - lo) >= w) & ((i - lo) <= n - 1)
 
 
 def _logits(q, k, v, window, lo, frac, rope_base, scale):

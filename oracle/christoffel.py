@@ -25,3 +25,10 @@ def carry_word(m, k):
 def offsets(m, k):
     """O = { j : c[j] == 1 }, ascending."""
     return [j for j, c in enumerate(carry_word(m, k)) if c == 1]
+
+
+def signed_offsets(m, k):
+    """Bidirectional offset set of page 3 ("signed offsets"): -O and +O,
+    ascending (keys i + o and i - o for every o in O)."""
+    o = offsets(m, k)
+    return sorted([-x for x in o] + o)

@@ -314,3 +314,47 @@ def test_edge_backward_matches_autograd_of_dense_masked_attention():
         assert np.abs(t.grad.numpy() - g[name]).max() < 1e-11, name
     o2, lse2 = A.forward_edges(q, k, v, edges, count, 1e4)
     assert np.abs(o2 - g["o"]).max() < 1e-13 and np.abs(lse2 - g["lse"]).max() < 1e-13
+
+
+# ------------------------------------------------ signed (bidirectional) offsets
+
+def test_signed_offsets_forward_and_backward_match_dense_masked_attention():
+    # Bidirectional Christoffel (self + signed carry-word offsets, page 3):
+    # keys i - o and i + o inside [0, n); GQA 4/2 with rotation.
+    B, n, hq, hkv, d = 2, 48, 4, 2, 8
+    q, k, v, do = (_rand((B, n, h, d), s) for h, s in ((hq, 41), (hkv, 42), (hkv, 43), (hq, 44)))
+    offs = np.array(christoffel.signed_offsets(4, 16), dtype=np.int32)
+    assert list(offs[:4]) == [-15, -11, -7, -3] and list(offs[4:]) == [3, 7, 11, 15]
+    fr = np.zeros(len(offs))
+    g = A.backward(q, k, v, do, 0, offs, fr, 1e4)
+    M = torch.full((n, n), -math.inf, dtype=torch.float64)
+    for i in range(n):
+        for o in [0] + list(offs):
+            if 0 <= i - o < n:
+                M[i, i - o] = 0.0
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+    qr, kr = _torch_rope(tq, 1e4), _torch_rope(tk, 1e4)
+    kr2, v2 = kr.repeat_interleave(hq // hkv, dim=2), tv.repeat_interleave(hq // hkv, dim=2)
+    s = torch.einsum("bihd,bjhd->bhij", qr, kr2) / math.sqrt(d) + M
+    o = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, dim=-1), v2)
+    assert np.abs(o.detach().numpy() - g["o"]).max() < 1e-12
+    (o * torch.from_numpy(do)).sum().backward()
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        assert np.abs(t.grad.numpy() - g[name]).max() < 1e-11, name
+
+
+def test_signed_interpolated_offset_dd_matches_finite_difference():
+    # A negative offset inside an interpolation cell: rows i + 5 (weight
+    # 0.7) and i + 4 (0.3); dd by central differences in frac.
+    B, n, h, d = 1, 30, 2, 8
+    q, k, v, do = (_rand((B, n, h, d), s) for s in (51, 52, 53, 54))
+    lo = np.array([-5, 3], dtype=np.int32)
+    fr = np.array([0.3, 0.6])
+    g = A.backward(q, k, v, do, 1, lo, fr, 1e4)
+    eps = 1e-6
+    for kk in range(2):
+        fp, fm = fr.copy(), fr.copy()
+        fp[kk] += eps
+        fm[kk] -= eps
+        num = (_loss(q, k, v, do, 1, lo, fp, 1e4) - _loss(q, k, v, do, 1, lo, fm, 1e4)) / (2 * eps)
+        assert abs(num - g["dd"][kk]) < 1e-7 * max(1.0, abs(num)), kk
