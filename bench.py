@@ -311,51 +311,55 @@ def main():
                                      for k_, v_ in lengths.items()})
 
     # Page 3's Christoffel layer trained: forward with LSE + backward (no
-    # offset gradient) at context 2048, 8 x 2048 tokens, 4/4 heads, self +
-    # 128 carry-word offsets, no rotation; views of the resident tensors.
+    # offset gradient) at context 2048, 8 x 2048 tokens, 4/4 heads, no
+    # rotation; views of the resident tensors.  Causal: self + 128
+    # carry-word offsets (m = 128, k = 1024).  Bidirectional by signed
+    # offsets: self + -O and +O of m = 64, k = 512, the same 129 slots.
     wc = si.WORKLOADS["ctx2048_christoffel"]
     Bc, nc, hc = wc["batch"], wc["seqlen"], wc["hq"]
-    offs = sfa.offsets_christoffel(wc["m"], wc["k"])
-    fr0 = np.zeros(len(offs), dtype=np.float32)
     ne = Bc * nc * hc * D
 
     def cview(t):
         return t.view(-1)[:ne].view(Bc, nc, hc, D)
 
     lse_c = lse_buf.view(-1)[:Bc * hc * nc].view(Bc, hc, nc)
-    ws_c = torch.empty(sfa.bwd_workspace_bytes(cview(sets[0][0]), cview(sets[0][1]), 0, offs, fr0, None),
-                       dtype=torch.uint8, device=dev)
 
-    def cstep(t):
-        q, k, v, do = (cview(x) for x in sets[t % NSETS])
-        sfa.fwd(q, k, v, 0, offs, fr0, None, out=cview(o_buf), lse=lse_c)
-        sfa.bwd(q, k, v, lse_c, do, 0, offs, fr0, None, workspace=ws_c, want_dd=False)
+    def time_christoffel(offs, signed):
+        fr0 = np.zeros(len(offs), dtype=np.float32)
+        ws_c = torch.empty(sfa.bwd_workspace_bytes(cview(sets[0][0]), cview(sets[0][1]), 0, offs, fr0, None,
+                                                   signed_offsets=signed), dtype=torch.uint8, device=dev)
 
-    for t in range(args.warmup):
-        cstep(t)
-    torch.cuda.synchronize()
-    sfa.profile_reset()
-    sfa.profile_enable(True)
-    t0 = time.perf_counter()
-    for t in range(args.steps):
-        cstep(t)
-    torch.cuda.synchronize()
-    cwall = time.perf_counter() - t0
-    sfa.profile_enable(False)
-    ck = {}
-    for name in ("fwd_offsets", "bwd_query", "bwd_key_dk", "bwd_key_dv"):
-        ms_, c_ = sfa.profile_read(name)
-        if c_:
-            ck[name] = round(1e3 * ms_ / c_, 3)
+        def cstep(t):
+            q, k, v, do = (cview(x) for x in sets[t % NSETS])
+            sfa.fwd(q, k, v, 0, offs, fr0, None, out=cview(o_buf), lse=lse_c, signed_offsets=signed)
+            sfa.bwd(q, k, v, lse_c, do, 0, offs, fr0, None, workspace=ws_c, want_dd=False, signed_offsets=signed)
+
+        for t in range(args.warmup):
+            cstep(t)
+        torch.cuda.synchronize()
+        sfa.profile_reset()
+        sfa.profile_enable(True)
+        t0 = time.perf_counter()
+        for t in range(args.steps):
+            cstep(t)
+        torch.cuda.synchronize()
+        cwall = time.perf_counter() - t0
+        sfa.profile_enable(False)
+        ck = {}
+        for name in ("fwd_offsets", "bwd_query", "bwd_key_dk", "bwd_key_dv"):
+            ms_, c_ = sfa.profile_read(name)
+            if c_:
+                ck[name] = round(1e3 * ms_ / c_, 3)
+        return {"slots": 1 + len(offs), "ms_per_step": round(1e3 * cwall / args.steps, 4),
+                "queries_per_s": round(Bc * nc / (cwall / args.steps), 1), "kernels_avg_us": ck}
+
     christoffel_step = {
-        "workload": "ctx2048_christoffel: 8 x 2048, 4/4 heads, D 64, bf16, W 0 + 128 offsets (129 slots), "
-                    "forward with LSE + backward without dd",
-        "ms_per_step": round(1e3 * cwall / args.steps, 4),
-        "queries_per_s": round(Bc * nc / (cwall / args.steps), 1),
-        "kernels_avg_us": ck,
+        "workload": "ctx2048_christoffel: 8 x 2048, 4/4 heads, D 64, bf16, no rotation, forward with LSE + "
+                    "backward without dd",
+        "causal_m128_k1024": time_christoffel(sfa.offsets_christoffel(wc["m"], wc["k"]), False),
+        "bidirectional_signed_m64_k512": time_christoffel(sfa.offsets_christoffel_signed(64, 512), True),
     }
-    log("christoffel step:", christoffel_step["ms_per_step"], ck)
-    del ws_c
+    log("christoffel steps:", {k_: v_["ms_per_step"] for k_, v_ in christoffel_step.items() if k_ != "workload"})
 
     # Page 2's power-law layer trained: edge-list forward with LSE + its
     # backward (inverted table built once on the host), same shape.

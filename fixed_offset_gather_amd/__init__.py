@@ -1,7 +1,7 @@
 """Python binding of libsfa: sparse fixed-offset attention on MI355X.
 
 Argument marshalling only.  Every step of the attention runs in the HIP
-kernels of ``libsfa.so`` (built in-tree by ``fixed_offset_gather_amd.build``);
+kernels of ``libsfa.so`` (built in-tree by ``fixed_offset_gather_amd/build.py``);
 the host producers (offsets, schedules, Christoffel offsets, power-law edge
 lists, rotary table) run in the same library's C++ code.  PyTorch supplies
 device memory and the current stream.  There is no fallback: if the library
@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libsfa.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        "libsfa.so is not built; run `python -m fixed_offset_gather_amd.build` "
+        "libsfa.so is not built; run `python fixed_offset_gather_amd/build.py` "
         "(hipcc, gfx950).  There is no CPU fallback.")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -40,6 +40,7 @@ SFA_ERR_HIP = -4
 SFA_F32 = 0
 SFA_BF16 = 1
 SFA_FLAG_INTERP_KERNEL = 1
+SFA_FLAG_SIGNED_OFFSETS = 2
 MAX_OFFSETS = 128
 MAX_SLOTS = 192
 SCHEDULES = {"fixed": 0, "linear": 1, "coprime": 2}
@@ -80,6 +81,7 @@ _sig("sfa_offsets_pow2", _c.c_int, [_c.c_double, _i32p, _f32p, _c.c_int])
 _sig("sfa_stagger_alpha", _c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_double)])
 _sig("sfa_alpha_of_theta", _c.c_int, [_c.c_double, _c.POINTER(_c.c_double), _c.POINTER(_c.c_double)])
 _sig("sfa_offsets_christoffel", _c.c_int, [_c.c_int, _c.c_int, _i32p, _c.c_int])
+_sig("sfa_offsets_christoffel_signed", _c.c_int, [_c.c_int, _c.c_int, _i32p, _c.c_int])
 _sig("sfa_edges_powerlaw", _c.c_int, [_c.c_int, _c.c_int, _c.c_double, _c.c_int, _c.c_int,
                                       _c.c_uint64, _i32p, _i32p])
 _sig("sfa_edges_transpose", _c.c_int, [_c.c_int, _c.c_int, _i32p, _i32p, _c.c_int, _i32p, _i32p])
@@ -179,6 +181,13 @@ def offsets_christoffel(m, k):
     return out[:cnt].copy()
 
 
+def offsets_christoffel_signed(m, k):
+    """-O and +O ascending, for a layer run with signed_offsets=True."""
+    out = np.zeros(max(2 * m, 1), dtype=np.int32)
+    cnt = _check("sfa_offsets_christoffel_signed", _lib.sfa_offsets_christoffel_signed(m, k, _ip(out), len(out)))
+    return out[:cnt].copy()
+
+
 def edges_powerlaw(n, r, sigma, draws, width, seed):
     edges = np.zeros((n, width), dtype=np.int32)
     count = np.zeros(n, dtype=np.int32)
@@ -273,11 +282,12 @@ class Problem:
 
 
 def fwd(q, k, v, window=0, lo=None, frac=None, rope=None, scale=0.0, want_lse=False, out=None, lse=None,
-        interp_kernel=False):
+        interp_kernel=False, signed_offsets=False):
     """Forward over the window 0..window plus shared offsets (lo, frac).
 
     interp_kernel=True runs the interpolating instantiation even when every
     frac is 0 (SFA_FLAG_INTERP_KERNEL); the result is the same.
+    signed_offsets=True admits negative lo (later rows; SFA_FLAG_SIGNED_OFFSETS).
     """
     torch = _torch()
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
@@ -285,7 +295,8 @@ def fwd(q, k, v, window=0, lo=None, frac=None, rope=None, scale=0.0, want_lse=Fa
     if k.shape != v.shape:
         raise ValueError("k and v shapes differ")
     B, n, hq, d = q.shape
-    pr = Problem(q, k, window, lo, frac, rope, scale, SFA_FLAG_INTERP_KERNEL if interp_kernel else 0)
+    pr = Problem(q, k, window, lo, frac, rope, scale, (SFA_FLAG_INTERP_KERNEL if interp_kernel else 0) |
+                 (SFA_FLAG_SIGNED_OFFSETS if signed_offsets else 0))
     o = torch.empty_like(q) if out is None else out
     _require(o, "out", q.dtype, q.shape)
     if want_lse and lse is None:
@@ -314,8 +325,8 @@ def fwd_edges(q, k, v, edges, count, rope=None, scale=0.0, want_lse=False, out=N
     return (o, lse) if want_lse else o
 
 
-def bwd_workspace_bytes(q, k, window=0, lo=None, frac=None, rope=None, scale=0.0):
-    pr = Problem(q, k, window, lo, frac, rope, scale)
+def bwd_workspace_bytes(q, k, window=0, lo=None, frac=None, rope=None, scale=0.0, signed_offsets=False):
+    pr = Problem(q, k, window, lo, frac, rope, scale, SFA_FLAG_SIGNED_OFFSETS if signed_offsets else 0)
     nb = _lib.sfa_bwd_workspace_bytes(pr.ref())
     if nb == 0 and q.numel() > 0:
         raise SfaError("sfa_bwd_workspace_bytes", SFA_ERR_ARG)
@@ -323,14 +334,14 @@ def bwd_workspace_bytes(q, k, window=0, lo=None, frac=None, rope=None, scale=0.0
 
 
 def bwd(q, k, v, lse, dout, window=0, lo=None, frac=None, rope=None, scale=0.0,
-        base=None, alpha=None, workspace=None, want_dd=True):
+        base=None, alpha=None, workspace=None, want_dd=True, signed_offsets=False):
     """Backward: returns (dq, dk, dv, dd or None, dtheta or None)."""
     torch = _torch()
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _require(t, nm, q.dtype)
     B, n, hq, d = q.shape
     _require(lse, "lse", torch.float32, (B, hq, n))
-    pr = Problem(q, k, window, lo, frac, rope, scale)
+    pr = Problem(q, k, window, lo, frac, rope, scale, SFA_FLAG_SIGNED_OFFSETS if signed_offsets else 0)
     nb = _lib.sfa_bwd_workspace_bytes(pr.ref())
     if workspace is None:
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)

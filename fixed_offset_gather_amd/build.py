@@ -1,6 +1,7 @@
 """Build libsfa.so (gfx950 HIP kernels + C ABI) in-tree with hipcc.
 
-Usage: python -m fixed_offset_gather_amd.build  (or __graft_entry__.build()).
+Usage: python fixed_offset_gather_amd/build.py  (or __graft_entry__.build()); a plain script, so
+it runs before the package (which needs the library) can be imported.
 Objects go to _build/ at the repository root; the shared library is written
 next to this file so that the Python binding (and a copy of the tree sent to
 a GPU machine) finds it without installation.

@@ -33,11 +33,15 @@ int validate_problem(const sfa_attn* a, Problem* p) {
     return fail(SFA_ERR_UNSUPPORTED, "n_off %d not in [0, %d]", a->n_off, SFA_MAX_OFFSETS);
   if (int64_t(a->window) + 1 + a->n_off > SFA_MAX_SLOTS)
     return fail(SFA_ERR_UNSUPPORTED, "window + 1 + n_off exceeds %d slots", SFA_MAX_SLOTS);
-  if (a->flags & ~SFA_FLAG_INTERP_KERNEL) return fail(SFA_ERR_ARG, "unknown flags 0x%x", unsigned(a->flags));
+  if (a->flags & ~(SFA_FLAG_INTERP_KERNEL | SFA_FLAG_SIGNED_OFFSETS))
+    return fail(SFA_ERR_ARG, "unknown flags 0x%x", unsigned(a->flags));
+  const int32_t lo_min = (a->flags & SFA_FLAG_SIGNED_OFFSETS) ? -(1 << 30) + 1 : 0;
   if (!std::isfinite(a->scale) || a->scale < 0.f) return fail(SFA_ERR_ARG, "scale must be finite and >= 0");
   if (a->n_off > 0 && (!a->off_lo || !a->off_frac)) return fail(SFA_ERR_ARG, "offset arrays are NULL");
   for (int k = 0; k < a->n_off; ++k) {
-    if (a->off_lo[k] < 0 || a->off_lo[k] >= (1 << 30)) return fail(SFA_ERR_ARG, "off_lo[%d] out of range", k);
+    if (a->off_lo[k] < lo_min || a->off_lo[k] >= (1 << 30))
+      return fail(SFA_ERR_ARG, "off_lo[%d] = %d out of range%s", k, a->off_lo[k],
+                  a->off_lo[k] < 0 ? " (negative offsets need SFA_FLAG_SIGNED_OFFSETS)" : "");
     const float f = a->off_frac[k];
     if (!(f >= 0.f && f < 1.f)) return fail(SFA_ERR_ARG, "off_frac[%d] not in [0,1)", k);
   }

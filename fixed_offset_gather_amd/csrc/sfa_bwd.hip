@@ -190,7 +190,7 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
       const float sdot = own_dot<G, LPQ, DC>(qv, kt, own);
       const float dp = own_dot<G, LPQ, DC>(dov, vt, own);
       const int rel = i - lo;
-      const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f));
+      const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f)) && rel < n;
       const float p = valid ? __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2) : 0.f;
       const float pdp = p * dp;
       dvec += pdp;
@@ -342,10 +342,13 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
       const int which = piece / (G * CH16);  // 0: Q, 1: dO
       const int h = (piece / CH16) % G;
       const int part = piece % CH16;
-      const T* src = (which ? dO : Q) + ((size_t(b) * n + r0 + row) * a.hq + size_t(g) * G + h) * D + c * KC +
-                     part * (16 / int(sizeof(T)));
-      *reinterpret_cast<uint4*>(Ws + row * RW + (which * G + h) * HW + part * 4) =
-          *reinterpret_cast<const uint4*>(src);
+      uint4 x = make_uint4(0, 0, 0, 0);  // rows before the sequence (negative offsets) stay zero
+      if (r0 + row >= 0) {
+        const T* src = (which ? dO : Q) + ((size_t(b) * n + r0 + row) * a.hq + size_t(g) * G + h) * D + c * KC +
+                       part * (16 / int(sizeof(T)));
+        x = *reinterpret_cast<const uint4*>(src);
+      }
+      *reinterpret_cast<uint4*>(Ws + row * RW + (which * G + h) * HW + part * 4) = x;
     }
     __syncthreads();
 
@@ -354,7 +357,7 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
     auto step_valid = [&](int sj, int tap) {
       const float w = st.frac[sj];
       const int i = j + st.lo[sj] + tap;
-      return activej && i < n && (tap == 1 || j > 0 || w == 0.f);
+      return activej && i >= 0 && i < n && (tap == 1 || j > 0 || w == 0.f);
     };
     auto load_step = [&](int sj, int tap, float (&pg)[G], float (&dpg)[G], float (&dvg)[G]) {
       if (step_valid(sj, tap)) {
@@ -405,7 +408,14 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
             yv[x] = fmaf(pg[h], oh[x], yv[x]);
           }
         }
-        if (a.rope) rotate_pairs<KC, 1>(yk, a.rope + size_t(delta) * D, c * KC);
+        if (a.rope) {
+          // R(delta) into key j's frame; a negative (future) offset rotates
+          // by R(|delta|)^T.  |delta| = |i - j| < n for a valid step.
+          if (delta >= 0)
+            rotate_pairs<KC, 1>(yk, a.rope + size_t(delta) * D, c * KC);
+          else
+            rotate_pairs<KC, -1>(yk, a.rope + size_t(-delta) * D, c * KC);
+        }
 #pragma unroll
         for (int x = 0; x < KC; ++x) {
           dk[x] = fmaf(wt, yk[x], dk[x]);
@@ -554,7 +564,7 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
   int fs = 0, ft = 0, flo = 0, ftaps = 1;
   auto load_step = [&](float (&raw)[NR][G]) {
     const int sc = fs < S ? fs : S - 1;
-    const int i = min(j + flo + ft, n - 1);
+    const int i = min(max(j + flo + ft, 0), n - 1);
     const size_t widx = (size_t(sc) * n + i) * G;
     load_vec<G>(Pseq + widx, raw[0]);
     if constexpr (PART == 0) {
@@ -565,7 +575,7 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
   // f16 weight pairs of the cursor's step: dS = scale p (dp - Dvec) for dK,
   // p for dV; zero for a masked step.
   auto convert = [&](const float (&raw)[NR][G], uint32_t (&wts)[GW]) {
-    const bool valid = fs < S && j + flo + ft < n;
+    const bool valid = fs < S && unsigned(j + flo + ft) < unsigned(n);
 #pragma unroll
     for (int hp = 0; hp < GW; ++hp) {
       const int h0 = 2 * hp, h1 = 2 * hp + 1 < G ? 2 * hp + 1 : 2 * hp;
@@ -638,8 +648,9 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
       const int xh = pc % XH;
       const bool pair = 2 * hp + 1 < G;
       const size_t rstride = size_t(a.hq) * D;
-      const bf16_t* src0 = X + (size_t(b) * n + r0) * rstride + (size_t(g) * G + 2 * hp) * D + c * KC + xh * 8;
-      const float* rope0 = rope ? a.rope + size_t(r0) * D + c * KC + xh * 8 : nullptr;
+      // addresses from signed row indices: r0 < 0 with negative offsets
+      const int64_t grow0 = int64_t(b) * n + r0;  // global query row of LDS row 0
+      const size_t col = (size_t(g) * G + 2 * hp) * D + c * KC + xh * 8;
       uint32_t* dst0 = Ws + hp * KC + xh * 8;
       for (int row0 = tid / PPR; row0 < nrows; row0 += SB * RSTEP) {
         uint4 u0[SB], u1[SB];
@@ -649,13 +660,16 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
           const int row = row0 + u * RSTEP;
           u0[u] = u1[u] = make_uint4(0, 0, 0, 0);
           ra[u] = rb[u] = make_float4(1.f, 0.f, 1.f, 0.f);
-          if (row < nrows) {
-            const bf16_t* src = src0 + size_t(row) * rstride;
+          // rows before the sequence (negative offsets) are staged as zeros:
+          // masked steps read LDS row 0 with zero weights
+          if (row < nrows && r0 + row >= 0) {
+            const bf16_t* src = X + size_t(grow0 + row) * rstride + col;
             u0[u] = *reinterpret_cast<const uint4*>(src);
             if (pair) u1[u] = *reinterpret_cast<const uint4*>(src + D);
             if (rope) {
-              ra[u] = *reinterpret_cast<const float4*>(rope0 + size_t(row) * D);
-              rb[u] = *reinterpret_cast<const float4*>(rope0 + size_t(row) * D + 4);
+              const float* rp = a.rope + size_t(r0 + row) * D + c * KC + xh * 8;
+              ra[u] = *reinterpret_cast<const float4*>(rp);
+              rb[u] = *reinterpret_cast<const float4*>(rp + 4);
             }
           }
         }
@@ -704,7 +718,7 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
         // row for it.  Masked steps read staged row 0 with zero weights.
         // Window slots run the same arithmetic with weight 1; their dd sum is
         // never stored.  One straight-line body keeps the registers put.
-        const bool valid = j + delta < n;
+        const bool valid = unsigned(j + delta) < unsigned(n);
         const int lrow = valid ? j + delta - r0 : 0;
         const uint32_t* rowp = Ws + lrow * RW;
         float y[KC];

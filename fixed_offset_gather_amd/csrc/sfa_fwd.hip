@@ -217,7 +217,9 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
           }
           const float mine = own_logit<G, LPQ, DC>(qv, kt, own);
           const int rel = i - lo;
-          const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f));
+          // the nearer row i - lo exists: i >= lo + frac, and below n for a
+          // negative (future) offset
+          const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f)) && rel < n;
           sl[j] = valid ? mine * a.scale_log2 : neg_inf();
         }
       }
@@ -494,7 +496,9 @@ __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTa
 #pragma unroll
           for (int h = 1; h < G; ++h) mine = (own == h) ? part[h] : mine;
           const int rel = i - lo;
-          const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f));
+          // the nearer row i - lo exists: i >= lo + frac, and below n for a
+          // negative (future) offset
+          const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f)) && rel < n;
           sl[j] = valid ? mine : neg_inf();
         }
       }

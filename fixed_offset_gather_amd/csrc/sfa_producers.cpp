@@ -147,6 +147,19 @@ extern "C" int sfa_offsets_christoffel(int m, int k, int32_t* offsets, int cap) 
   return w;
 }
 
+// Bidirectional form by signed offsets ("Christoffel-Balanced Sparse
+// Attention", integration paragraph): -O then +O, ascending.
+extern "C" int sfa_offsets_christoffel_signed(int m, int k, int32_t* offsets, int cap) {
+  if (k < 1 || k > (1 << 24) || m < 0 || m > k)
+    return fail(SFA_ERR_ARG, "sfa_offsets_christoffel_signed: need 1 <= k <= 2^24, 0 <= m <= k");
+  if (m > 0 && !offsets) return fail(SFA_ERR_ARG, "sfa_offsets_christoffel_signed: offsets is NULL");
+  if (cap < 2 * m) return fail(SFA_ERR_CAPACITY, "sfa_offsets_christoffel_signed: need %d entries", 2 * m);
+  const int w = sfa_offsets_christoffel(m, k, offsets + m, m);
+  if (w < 0) return w;
+  for (int t = 0; t < m; ++t) offsets[t] = -offsets[2 * m - 1 - t];
+  return 2 * m;
+}
+
 // "Critical power-law sparse attention", items 1-2, with SplitMix64 as the
 // generator (Steele, Lea and Flood 2014).
 namespace {

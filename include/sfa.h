@@ -129,6 +129,14 @@ int sfa_alpha_of_theta(double theta, double* alpha, double* dalpha_dtheta);
 int sfa_offsets_christoffel(int m, int k, int32_t* offsets, int cap);
 
 /*
+ * Bidirectional Christoffel offsets ([P3], signed offsets): -O and +O of
+ * sfa_offsets_christoffel, ascending (2m values), for a layer run with
+ * SFA_FLAG_SIGNED_OFFSETS.  Same requirements; returns 2m,
+ * SFA_ERR_CAPACITY if cap < 2m.
+ */
+int sfa_offsets_christoffel_signed(int m, int k, int32_t* offsets, int cap);
+
+/*
  * Power-law edge lists of [P2] items 1-2.  For query i: the window
  * {i-r..i+r} clipped to [0, n), plus `draws` keys j = (i + s d) mod n with
  * d ~ q(d) = d^-(1+sigma) / sum_{u <= n/2} u^-(1+sigma) and a random sign s;
@@ -183,6 +191,15 @@ int sfa_rope_table(int n, int head_dim, double theta, float* table);
  * flag exists to measure and test that.
  */
 #define SFA_FLAG_INTERP_KERNEL 1
+/*
+ * SFA_FLAG_SIGNED_OFFSETS: off_lo may be negative (|off_lo| < 2^30).  A
+ * negative offset names the later row i - lo = i + |lo| (and i - lo - 1
+ * with weight frac), valid while it is below n: page 3's bidirectional
+ * attention by signed offsets ("Christoffel-Balanced Sparse Attention",
+ * integration paragraph).  Without the flag every off_lo must be >= 0
+ * (causal).  The window slots 0..W stay causal.
+ */
+#define SFA_FLAG_SIGNED_OFFSETS 2
 
 /*
  * Problem description (plain data; host arrays are read during the call
@@ -199,7 +216,8 @@ typedef struct sfa_attn {
   int32_t n_off;    /* shared offsets, 0..SFA_MAX_OFFSETS */
   float scale;      /* logit scale; 0 -> 1/sqrt(D) ([P2] item 2, [P3]) */
   int32_t flags;    /* SFA_FLAG_* bits, 0 by default */
-  const int32_t* off_lo; /* host [n_off]: floor of each offset distance, >= 0 */
+  const int32_t* off_lo; /* host [n_off]: floor of each offset distance, >= 0
+                            (any sign with SFA_FLAG_SIGNED_OFFSETS) */
   const float* off_frac; /* host [n_off]: interpolation weight in [0, 1) */
   const float* rope;     /* device [n][D/2][2] from sfa_rope_table, or NULL
                             for no rotation */

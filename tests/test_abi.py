@@ -139,7 +139,7 @@ def _fwd(a, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None):
     (dict(lo=[1], frac=[float("nan")]), sfa.SFA_ERR_ARG),
     (dict(scale=float("nan")), sfa.SFA_ERR_ARG),
     (dict(scale=-1.0), sfa.SFA_ERR_ARG),
-    (dict(flags=2), sfa.SFA_ERR_ARG),
+    (dict(flags=4), sfa.SFA_ERR_ARG),
     (dict(batch=-1), sfa.SFA_ERR_ARG),
 ])
 def test_fwd_rejects_invalid_problem(kw, code):
@@ -252,3 +252,21 @@ def test_bwd_edges_validation_and_workspace_size():
     assert call(64, 8, FAKE, nb, ptrs=[None] + t[1:]) == sfa.SFA_ERR_ARG
     assert call(64, 8, FAKE, nb, ptrs=t[:5] + [MISALIGNED] + t[6:]) == sfa.SFA_ERR_ARG
     assert call(64, 8, FAKE, nb, e=ctypes.c_void_p(0x100002)) == sfa.SFA_ERR_ARG   # edges misaligned
+
+
+@pytest.mark.parametrize("m,k", [(64, 512), (4, 16), (128, 1024)])
+def test_christoffel_signed_bit_exact(m, k):
+    assert list(sfa.offsets_christoffel_signed(m, k)) == ref_chr.signed_offsets(m, k)
+
+
+def test_negative_offsets_need_the_signed_flag():
+    lib = sfa.library()
+    lo = np.array([-7, 7], dtype=np.int32)
+    fr = np.zeros(2, dtype=np.float32)
+    a = _prob(lo=lo, frac=fr, window=0)
+    assert lib.sfa_bwd_workspace_bytes(ctypes.byref(a)) == 0
+    assert _fwd(a) == sfa.SFA_ERR_ARG
+    a.flags = sfa.SFA_FLAG_SIGNED_OFFSETS
+    assert lib.sfa_bwd_workspace_bytes(ctypes.byref(a)) > 0
+    a.flags = 4
+    assert lib.sfa_bwd_workspace_bytes(ctypes.byref(a)) == 0

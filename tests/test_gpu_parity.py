@@ -78,9 +78,9 @@ class Case:
         return [si.to_f64(t[sel]) for t in (self.q, self.k, self.v, self.do)]
 
 
-def _fwd_check(case, W, lo, frac, sel=slice(None), tol=None):
+def _fwd_check(case, W, lo, frac, sel=slice(None), tol=None, signed=False):
     sfa = _sfa()
-    o, lse = sfa.fwd(case.qd, case.kd, case.vd, W, lo, frac, case.rope, want_lse=True)
+    o, lse = sfa.fwd(case.qd, case.kd, case.vd, W, lo, frac, case.rope, want_lse=True, signed_offsets=signed)
     torch.cuda.synchronize()
     q, k, v, _ = case.f64(sel)
     ro, rl = ref.forward(q, k, v, W, lo, frac, case.rope_theta)
@@ -92,12 +92,13 @@ def _fwd_check(case, W, lo, frac, sel=slice(None), tol=None):
     return o, lse
 
 
-def _bwd_check(case, W, lo, frac, alpha, base, sel=slice(None), tol=None, grad_tol=None, want_dd=True):
+def _bwd_check(case, W, lo, frac, alpha, base, sel=slice(None), tol=None, grad_tol=None, want_dd=True,
+               signed=False):
     sfa = _sfa()
-    o, lse = sfa.fwd(case.qd, case.kd, case.vd, W, lo, frac, case.rope, want_lse=True)
+    o, lse = sfa.fwd(case.qd, case.kd, case.vd, W, lo, frac, case.rope, want_lse=True, signed_offsets=signed)
     dq, dk, dv, dd, dth = sfa.bwd(case.qd, case.kd, case.vd, lse, case.dod, W, lo, frac, case.rope,
                                   base=base if want_dd else None, alpha=alpha if want_dd else None,
-                                  want_dd=want_dd)
+                                  want_dd=want_dd, signed_offsets=signed)
     if not want_dd:
         assert dd is None and dth is None
     torch.cuda.synchronize()
@@ -451,6 +452,46 @@ def test_edge_backward_ctx2048_powerlaw_full_size_and_deterministic():
     a = _edge_bwd_check(case, edges, count, sel=slice(0, 1))
     b = _edge_bwd_check(case, edges, count, sel=slice(0, 1))
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("W", [0, 3])
+def test_signed_christoffel_multi_tile(dtype, W):
+    # Page 3's bidirectional layer by signed offsets: keys i - o and i + o.
+    sfa = _sfa()
+    case = Case(2, 200, 8, 2, 64, dtype, seed=29)
+    offs = sfa.offsets_christoffel_signed(8, 64)
+    assert offs[0] == -63 and offs[-1] == 63
+    fr = np.zeros(len(offs), dtype=np.float32)
+    tol = TOL[dtype] if dtype == "bf16" else 2e-5
+    _fwd_check(case, W, offs, fr, signed=True, tol=tol)
+    _bwd_check(case, W, offs, fr, 1.0, np.abs(offs).astype(np.int32), tol=tol,
+               grad_tol=1e-4 if dtype == "f32" else 1e-2, signed=True)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_negative_interpolated_offsets(dtype):
+    # Later rows between i + 4 and i + 5 (weight 0.3 on i + 4), an integer
+    # future offset, and an ordinary rung, with dd.
+    sfa = _sfa()
+    case = Case(2, 150, 4, 2, 32, dtype, seed=31)
+    lo = np.array([-5, -2, 3], dtype=np.int32)
+    fr = np.array([0.3, 0.0, 0.6], dtype=np.float32)
+    tol = TOL[dtype] if dtype == "bf16" else 2e-5
+    _bwd_check(case, 2, lo, fr, 1.0, np.array([5, 2, 3], dtype=np.int32), tol=tol,
+               grad_tol=1e-4 if dtype == "f32" else 1e-2, signed=True)
+
+
+def test_bidirectional_christoffel_full_size():
+    # m = 64, k = 512 made bidirectional: 128 signed offsets + self, the same
+    # 129 slots as the causal m = 128 layer; context 2048, sequence 0 of 8.
+    sfa = _sfa()
+    w = si.WORKLOADS["ctx2048_christoffel"]
+    case = Case(w["batch"], w["seqlen"], w["hq"], w["hkv"], w["head_dim"], w["dtype"], rope_theta=0.0)
+    offs = sfa.offsets_christoffel_signed(64, 512)
+    fr = np.zeros(len(offs), dtype=np.float32)
+    _fwd_check(case, 0, offs, fr, sel=slice(0, 1), signed=True)
+    _bwd_check(case, 0, offs, fr, None, None, sel=slice(0, 1), want_dd=False, signed=True)
 
 
 def test_ctx2048_christoffel_full_size():
