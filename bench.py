@@ -14,7 +14,8 @@ Prints ONE JSON line: queries/s of the whole step (value), the step's
 algorithmic HBM GB/s, a roofline object for the dominant kernel (timed with
 HIP events on its launch stream over the timed region), the forward alone on
 the fixed-alpha page-1 layer (window 8, integer rungs), and the fp64 CPU
-oracle timed on a bounded sample of the same step.
+oracle timed on a bounded sample of the same step on one core, and on the
+whole batch over all host cores (one worker process per core, at most 16).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -133,6 +134,49 @@ def cpu_baseline(w, alpha, seqs):
     }
 
 
+def _oracle_worker(job):
+    """One all-core baseline worker (a fresh process): the fp64 oracle step
+    on sequences [a, b) of the seeded batch, one thread; returns seconds."""
+    wname, alpha, a, b = job
+    from threadpoolctl import threadpool_limits
+
+    import synth_inputs as si
+    from oracle import attention as ref
+    from oracle import offsets as ref_off
+
+    w = si.WORKLOADS[wname]
+    q, k, v = si.qkv(w["batch"], w["seqlen"], w["hq"], w["hkv"], w["head_dim"], w["dtype"])
+    do = si.upstream(w["batch"], w["seqlen"], w["hq"], w["head_dim"], w["dtype"])
+    f = [si.to_f64(t[a:b]) for t in (q, k, v, do)]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        lo, frac = ref_off.rung_offsets(alpha)
+        ref.forward(f[0], f[1], f[2], w["window"], lo, frac, w["rope_theta"])
+        g = ref.backward(*f, w["window"], lo, frac, w["rope_theta"])
+        ref.dtheta_from_dd(g["dd"], ref_off.FIB_BASE, alpha)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline_all_cores(wname, alpha, batch, seqlen):
+    """The same oracle step on every sequence of the batch, spread over the
+    host's cores (at most 16 worker processes, started by spawn)."""
+    import multiprocessing as mp
+    cores = min(len(os.sched_getaffinity(0)), 16, batch)
+    per = (batch + cores - 1) // cores
+    jobs = [(wname, alpha, a, min(a + per, batch)) for a in range(0, batch, per)]
+    with mp.get_context("spawn").Pool(len(jobs)) as pool:
+        secs = pool.map(_oracle_worker, jobs)
+    t = max(secs)
+    return {
+        "value": batch * seqlen / t,
+        "unit": "queries/s",
+        "cores": len(jobs),
+        "kind": "oracle",
+        "sample": "all %d sequences of the step, %d worker processes of one thread each (%d sequences each); "
+                  "slowest worker %.1f s" % (batch, len(jobs), per, t),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +192,14 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
+
+    # The all-core oracle leg starts its worker processes here, before this
+    # process touches the GPU, and ends them before the GPU work begins.
+    if not args.no_cpu_baseline:
+        import synth_inputs as si
+        wl = si.WORKLOADS["page1_learned_step"]
+        all_cores = cpu_baseline_all_cores("page1_learned_step", si.learned_alpha(), wl["batch"], wl["seqlen"])
+        log("cpu baseline (all cores):", all_cores)
 
     import numpy as np
     import torch
@@ -432,6 +484,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, alpha, args.cpu_seqs)
+        out["cpu_baseline_all_cores"] = all_cores
     print(json.dumps(out), flush=True)
 
 
