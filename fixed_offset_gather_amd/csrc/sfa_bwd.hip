@@ -54,31 +54,19 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
-template <int G, int LPQ>
-struct Bc {
-  template <int H = 0>
-  static __device__ __forceinline__ void run(float x, float (&out)[G]) {
-    if constexpr (H < G) {
-      out[H] = owner_bcast<G, LPQ, H>(x);
-      run<H + 1>(x, out);
-    }
-  }
-};
-
+// Dot product of the lane's own head with a key chunk, summed over the lanes
+// of the query (HeadSlice register order and reduce-scatter).
 template <int G, int LPQ, int DC>
-__device__ __forceinline__ float own_dot(const float (&a)[G][DC], const float (&b)[DC], int own) {
+__device__ __forceinline__ float own_dot(const float (&a)[G][DC], const float (&b)[DC]) {
   float part[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float acc = 0.f;
 #pragma unroll
     for (int x = 0; x < DC; ++x) acc = fmaf(a[h][x], b[x], acc);
-    part[h] = group_sum<LPQ>(acc);
+    part[h] = acc;
   }
-  float mine = part[0];
-#pragma unroll
-  for (int h = 1; h < G; ++h) mine = (own == h) ? part[h] : mine;
-  return mine;
+  return HeadSlice<G, LPQ>::reduce(part);
 }
 
 template <typename T, int D, int G, int LPQ, int CAP>
@@ -88,13 +76,14 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
   constexpr int E = 16 / sizeof(T);
   constexpr int CPR = D / E;
   constexpr int NT = BQ * LPQ;
+  using HS = HeadSlice<G, LPQ>;
   __shared__ __align__(16) float Ks[CAP * KS];
   __shared__ __align__(16) float Vs[CAP * KS];
 
   const int tid = threadIdx.x;
   const int qq = tid / LPQ;
   const int c = tid % LPQ;
-  const int own = c % G;
+  const int own = HS::own(c);
   const int tile = xcd_tile(blockIdx.x, a.tiles);
   const int seq = tile / a.nblk;
   const int blk = a.nblk - 1 - tile % a.nblk;
@@ -111,20 +100,21 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
   const T* __restrict__ dO = static_cast<const T*>(a.dout);
 
   // acc_pd = sum p dp k~, acc_p = sum p k~ ; dq~ = scale (acc_pd - Dvec acc_p)
+  // Register j of a lane holds head HS::head(c, j) of the group.
   float qv[G][DC], dov[G][DC], acc_pd[G][DC], acc_p[G][DC];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int j = 0; j < G; ++j) {
     if (active) {
-      const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC;
-      load_vec<DC>(Q + off, qv[h]);
-      if (a.rope) rotate_pairs<DC, 1>(qv[h], a.rope + size_t(i) * D, c * DC);
-      load_vec<DC>(dO + off, dov[h]);
+      const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + HS::head(c, j)) * D + c * DC;
+      load_vec<DC>(Q + off, qv[j]);
+      if (a.rope) rotate_pairs<DC, 1>(qv[j], a.rope + size_t(i) * D, c * DC);
+      load_vec<DC>(dO + off, dov[j]);
     } else {
 #pragma unroll
-      for (int x = 0; x < DC; ++x) qv[h][x] = dov[h][x] = 0.f;
+      for (int x = 0; x < DC; ++x) qv[j][x] = dov[j][x] = 0.f;
     }
 #pragma unroll
-    for (int x = 0; x < DC; ++x) acc_pd[h][x] = acc_p[h][x] = 0.f;
+    for (int x = 0; x < DC; ++x) acc_pd[j][x] = acc_p[j][x] = 0.f;
   }
   const float lse2 = active ? a.lse[(size_t(b) * a.hq + size_t(g) * G + own) * n + i] * kLog2e : 0.f;
   float dvec = 0.f;  // rowsum(dO * O) of the own head, as sum_slots p dp
@@ -187,44 +177,56 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
           vt[x] = fmaf(w, vb[x] - vt[x], vt[x]);
         }
       }
-      const float sdot = own_dot<G, LPQ, DC>(qv, kt, own);
-      const float dp = own_dot<G, LPQ, DC>(dov, vt, own);
+      float sp[G], dps[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int x = 0; x < DC; ++x) {
+          s1 = fmaf(qv[j][x], kt[x], s1);
+          s2 = fmaf(dov[j][x], vt[x], s2);
+        }
+        sp[j] = s1;
+        dps[j] = s2;
+      }
+      const float sdot = HS::reduce(sp);
+      const float dp = HS::reduce(dps);
       const int rel = i - lo;
       const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f)) && rel < n;
       const float p = valid ? __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2) : 0.f;
       const float pdp = p * dp;
       dvec += pdp;
-      if (active && c < G) {  // p = 0 where the slot has no row for query i
-        const size_t widx = ((ws_seq + sj) * n + i) * G + c;
+      if (active && HS::writer(c)) {  // p = 0 where the slot has no row for query i
+        const size_t widx = ((ws_seq + sj) * n + i) * G + own;
         a.P[widx] = p;
         a.dP[widx] = dp;
       }
       float ph[G], pdh[G];
-      Bc<G, LPQ>::run(p, ph);
-      Bc<G, LPQ>::run(pdp, pdh);
+      HS::bcast(p, ph);
+      HS::bcast(pdp, pdh);
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int j = 0; j < G; ++j)
 #pragma unroll
         for (int x = 0; x < DC; ++x) {
-          acc_pd[h][x] = fmaf(pdh[h], kt[x], acc_pd[h][x]);
-          acc_p[h][x] = fmaf(ph[h], kt[x], acc_p[h][x]);
+          acc_pd[j][x] = fmaf(pdh[j], kt[x], acc_pd[j][x]);
+          acc_p[j][x] = fmaf(ph[j], kt[x], acc_p[j][x]);
         }
     }
     s = e;
   }
 
-  if (active && c < G) a.Dvec[(size_t(seq) * n + i) * G + c] = dvec;
+  if (active && HS::writer(c)) a.Dvec[(size_t(seq) * n + i) * G + own] = dvec;
   float dvh[G];
-  Bc<G, LPQ>::run(dvec, dvh);
+  HS::bcast(dvec, dvh);
   if (active) {
     T* dQ = static_cast<T*>(a.dq);
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int j = 0; j < G; ++j) {
       float dq[DC];
 #pragma unroll
-      for (int x = 0; x < DC; ++x) dq[x] = a.scale * fmaf(-dvh[h], acc_p[h][x], acc_pd[h][x]);
+      for (int x = 0; x < DC; ++x) dq[x] = a.scale * fmaf(-dvh[j], acc_p[j][x], acc_pd[j][x]);
       if (a.rope) rotate_pairs<DC, -1>(dq, a.rope + size_t(i) * D, c * DC);
-      store_vec<DC>(dQ + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, dq);
+      store_vec<DC>(dQ + ((size_t(b) * n + i) * a.hq + size_t(g) * G + HS::head(c, j)) * D + c * DC, dq);
     }
   }
 }
@@ -951,7 +953,8 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
   const int tid = threadIdx.x;
   const int qq = tid / LPQ;
   const int c = tid % LPQ;
-  const int own = c % G;
+  using HS = HeadSlice<G, LPQ>;
+  const int own = HS::own(c);
   const int tile = xcd_tile(blockIdx.x, a.tiles);
   const int seq = tile / a.nblk;
   const int blk = tile % a.nblk;
@@ -970,7 +973,7 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     if (active) {
-      const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC;
+      const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + HS::head(c, h)) * D + c * DC;
       load_vec<DC>(Q + off, qv[h]);
       if (a.rope) rotate_pairs<DC, 1>(qv[h], a.rope + size_t(i) * D, c * DC);
       load_vec<DC>(dO + off, dov[h]);
@@ -1002,18 +1005,18 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
 #pragma unroll
       for (int x = 0; x < DC; ++x) kt[x] = vt[x] = 0.f;
     }
-    const float sdot = own_dot<G, LPQ, DC>(qv, kt, own);
-    const float dp = own_dot<G, LPQ, DC>(dov, vt, own);
+    const float sdot = own_dot<G, LPQ, DC>(qv, kt);
+    const float dp = own_dot<G, LPQ, DC>(dov, vt);
     const float p = valid ? __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2) : 0.f;
     const float pdp = p * dp;
     dvec += pdp;
-    if (valid && c < G) {
-      a.P[(wrow + t) * G + c] = p;
-      a.dP[(wrow + t) * G + c] = dp;
+    if (valid && HS::writer(c)) {
+      a.P[(wrow + t) * G + own] = p;
+      a.dP[(wrow + t) * G + own] = dp;
     }
     float ph[G], pdh[G];
-    Bc<G, LPQ>::run(p, ph);
-    Bc<G, LPQ>::run(pdp, pdh);
+    HS::bcast(p, ph);
+    HS::bcast(pdp, pdh);
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -1023,9 +1026,9 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
       }
   }
 
-  if (active && c < G) a.Dvec[(size_t(seq) * n + i) * G + c] = dvec;
+  if (active && HS::writer(c)) a.Dvec[(size_t(seq) * n + i) * G + own] = dvec;
   float dvh[G];
-  Bc<G, LPQ>::run(dvec, dvh);
+  HS::bcast(dvec, dvh);
   if (active) {
     T* dQ = static_cast<T*>(a.dq);
 #pragma unroll
@@ -1034,7 +1037,7 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
 #pragma unroll
       for (int x = 0; x < DC; ++x) dq[x] = a.scale * fmaf(-dvh[h], acc_p[h][x], acc_pd[h][x]);
       if (a.rope) rotate_pairs<DC, -1>(dq, a.rope + size_t(i) * D, c * DC);
-      store_vec<DC>(dQ + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, dq);
+      store_vec<DC>(dQ + ((size_t(b) * n + i) * a.hq + size_t(g) * G + HS::head(c, h)) * D + c * DC, dq);
     }
   }
 }

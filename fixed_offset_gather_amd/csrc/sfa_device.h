@@ -222,22 +222,6 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Value of lane H of the caller's aligned group of L lanes.
-template <int L, int H>
-__device__ __forceinline__ float group_bcast(float x) {
-  static_assert(H < L, "lane in group");
-  if constexpr (L == 1) {
-    return x;
-  } else if constexpr (L == 2) {
-    return dpp<quad_perm(H, H, 2 + H, 2 + H)>(x);
-  } else if constexpr (L == 4) {
-    return dpp<quad_perm(H, H, H, H)>(x);
-  } else {
-    const int lane = __lane_id();
-    return __shfl(x, (lane & ~(L - 1)) + H);
-  }
-}
-
 // Value held by the lanes that own head H, where lane c of a query's
 // aligned group of L lanes owns head c % G (L a multiple of G, so the owners
 // repeat every G lanes and all owners of one head hold the same value).
@@ -261,6 +245,76 @@ __device__ __forceinline__ float owner_bcast(float x) {
     return ((__lane_id() >> 2) & 1) == (H >> 2) ? v : w;
   }
 }
+
+// Butterfly partner inside aligned groups of SPAN lanes (SPAN <= 16): lane c
+// reads lane c ^ (SPAN - 1), one DPP move (mirror, half mirror, quad
+// reverse, pair swap).
+template <int SPAN>
+__device__ __forceinline__ float bfly(float x) {
+  static_assert(SPAN == 2 || SPAN == 4 || SPAN == 8 || SPAN == 16, "span");
+  if constexpr (SPAN == 16) return dpp<kDppRowMirror>(x);
+  else if constexpr (SPAN == 8) return dpp<kDppRowHalfMirror>(x);
+  else if constexpr (SPAN == 4) return dpp<quad_perm(3, 2, 1, 0)>(x);
+  else return dpp<quad_perm(1, 0, 3, 2)>(x);
+}
+
+constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x >> 1); }
+
+// Per-head sums over an aligned group of L lanes that all hold partial sums
+// of the same G heads (a reduce-scatter).  Lane c keeps its G partials in a
+// lane-specific order: register j holds head head(c, j).  Exchange step t
+// (t = 0 widest) pairs lane c with lane c ^ ((L >> t) - 1); the first
+// log2(G) steps each send half of the remaining registers and keep the other
+// half, the rest add the one remaining register.  A full reduction costs
+// log2(L) DPP adds instead of G log2(L), and ends with lane c holding the sum
+// of head own(c) = c >> log2(L / G), bit-identical in every lane of that
+// head (each add has the same two operands).  bcast spreads one value per
+// head back into the lane's register order with G - 1 DPP moves.
+template <int G, int L>
+struct HeadSlice {
+  static_assert(G >= 1 && L >= G && L <= 16 && L % G == 0, "head group");
+  static constexpr int S = ilog2c(G);
+  static constexpr int SH = ilog2c(L / G);
+  static constexpr int NSTEP = ilog2c(L);
+
+  __device__ static int own(int c) { return c >> SH; }
+  // One lane per head (for stores of per-head values).
+  __device__ static bool writer(int c) { return (c & ((1 << SH) - 1)) == 0; }
+  __device__ static int head(int c, int j) {
+    int m = 0;
+    for (int t = 0; t < S; ++t)
+      if ((j >> (S - 1 - t)) & 1) m ^= (L >> t) - 1;
+    return (c ^ m) >> SH;
+  }
+
+  template <int T = 0>
+  __device__ static float reduce(float (&x)[G]) {
+    if constexpr (T < S) {
+      constexpr int half = G >> (T + 1);
+#pragma unroll
+      for (int j = 0; j < half; ++j) x[j] += bfly<(L >> T)>(x[j + half]);
+      return reduce<T + 1>(x);
+    } else if constexpr (T < NSTEP) {
+      x[0] += bfly<(L >> T)>(x[0]);
+      return reduce<T + 1>(x);
+    } else {
+      return x[0];
+    }
+  }
+
+  template <int B = 0>
+  __device__ static void fill(float (&out)[G]) {
+    if constexpr (B < S) {
+#pragma unroll
+      for (int j = 1 << B; j < (2 << B); ++j) out[j] = bfly<(L >> (S - 1 - B))>(out[j - (1 << B)]);
+      fill<B + 1>(out);
+    }
+  }
+  __device__ static void bcast(float v, float (&out)[G]) {
+    out[0] = v;
+    fill(out);
+  }
+};
 
 // Sum over the whole 64-lane wavefront (result valid in every lane).
 __device__ __forceinline__ float wave_sum(float x) {
