@@ -817,17 +817,30 @@ __global__ __launch_bounds__(kReduceThreads) void bwd_reduce_kernel(ReduceArgs a
   }
 }
 
-// Lanes per query in bwd_query: at least two per head of the group and at
-// most 8 dims per lane (four G x DC register tiles live across the loop),
-// never fewer than 2 dims (rotation pairs) or more than 16 lanes.
+// Lanes per query in bwd_query.  The LDS of a workgroup is fixed by its
+// stage rows, so more lanes per query put more waves on a CU; that pays
+// where the G x DC register tiles are large: with G >= 4 a lane takes 4 dims
+// (D = 64, G = 4: 16 lanes, 117 VGPRs, 4 waves per SIMD, against 8 lanes,
+// 192 VGPRs and 2 waves), with fewer heads 8 dims (there a lane's dot is so
+// short that the extra reduction steps cost more than the waves gain).  At
+// least two lanes per head, never fewer than 2 dims (rotation pairs) or more
+// than 16 lanes.
 template <int D, int G>
 constexpr int bwd_lpq() {
-  constexpr int a = 2 * G > D / 8 ? 2 * G : D / 8;
+  constexpr int dims = G >= 4 ? 4 : 8;
+  constexpr int a = 2 * G > D / dims ? 2 * G : D / dims;
   constexpr int b = a < D / 2 ? a : D / 2;
   return b < 16 ? b : 16;
 }
 
-
+// Lanes per query in bwd_edges_query (keys straight from global memory):
+// at most 8 dims per lane, same other limits.
+template <int D, int G>
+constexpr int edge_lpq() {
+  constexpr int a = 2 * G > D / 8 ? 2 * G : D / 8;
+  constexpr int b = a < D / 2 ? a : D / 2;
+  return b < 16 ? b : 16;
+}
 
 BwdArgs make_args(const Problem& p, const SlotTable& t, const BwdWorkspace& ws) {
   BwdArgs a{};
@@ -1112,7 +1125,7 @@ __global__ __launch_bounds__(kEdgeKB) void bwd_edges_key_kernel(EdgeBwdArgs a) {
 
 template <typename T, int D, int G>
 int launch_edges_t(const EdgeBwdArgs& a0, hipStream_t st) {
-  constexpr int LPQ = bwd_lpq<D, G>();
+  constexpr int LPQ = edge_lpq<D, G>();
   EdgeBwdArgs a = a0;
   const int seqs = a0.tiles;  // B * hkv on entry
   {
