@@ -191,9 +191,15 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
       }
       const float sdot = HS::reduce(sp);
       const float dp = HS::reduce(dps);
-      const int rel = i - lo;
-      const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f)) && rel < n;
-      const float p = valid ? __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2) : 0.f;
+      // The nearer row i - lo exists when mn <= i - lo <= n - 1, mn = 1 for
+      // an interpolated slot (its farther row i - lo - 1 must exist too).
+      // One unsigned compare and a select, no branch.  Queries past n (the
+      // ragged last block) have zero q and dO, so their p stays finite and
+      // is never stored.
+      const int mn = w != 0.f ? 1 : 0;
+      const bool valid = unsigned(i - lo - mn) < unsigned(n - mn);
+      const float ex = __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2);
+      const float p = valid ? ex : 0.f;
       const float pdp = p * dp;
       dvec += pdp;
       if (active && HS::writer(c)) {  // p = 0 where the slot has no row for query i
@@ -1020,7 +1026,8 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
     }
     const float sdot = own_dot<G, LPQ, DC>(qv, kt);
     const float dp = own_dot<G, LPQ, DC>(dov, vt);
-    const float p = valid ? __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2) : 0.f;
+    const float ex = __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2);  // finite: kt = 0 if invalid
+    const float p = valid ? ex : 0.f;
     const float pdp = p * dp;
     dvec += pdp;
     if (valid && HS::writer(c)) {
