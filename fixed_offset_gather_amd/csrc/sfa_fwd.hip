@@ -198,14 +198,24 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
     __syncthreads();
 
     for (int s0 = s; s0 < e; s0 += SC) {
+      // The chunk's slot entries, read together (one wait for all of them).
+      int lo_c[SC];
+      float w_c[SC], mult_c[SC];
+#pragma unroll
+      for (int j = 0; j < SC; ++j) {
+        const int sc = min(s0 + j, e - 1);
+        lo_c[j] = s_lo[sc];
+        w_c[j] = s_w[sc];
+        mult_c[j] = s_mult[sc];
+      }
       float sl[SC];
 #pragma unroll
       for (int j = 0; j < SC; ++j) {
         sl[j] = neg_inf();
         const int sj = s0 + j;
         if (sj < e) {
-          const int lo = __builtin_amdgcn_readfirstlane(s_lo[sj]);
-          const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_w[sj])));
+          const int lo = __builtin_amdgcn_readfirstlane(lo_c[j]);
+          const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w_c[j])));
           const int r = i - lo - r0;  // in [0, nrows) for every lane of the block
           float kt[DC];
           load_vec<DC>(Ks + r * KS + c * DC, kt);
@@ -216,10 +226,10 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
             for (int x = 0; x < DC; ++x) kt[x] = fmaf(w, kb[x] - kt[x], kt[x]);
           }
           const float mine = own_logit<G, LPQ, DC>(qv, kt, own);
-          const int rel = i - lo;
-          // the nearer row i - lo exists: i >= lo + frac, and below n for a
-          // negative (future) offset
-          const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f)) && rel < n;
+          // the nearer row i - lo exists: mn <= i - lo <= n - 1 (as in the
+          // bf16 kernel below)
+          const int mn = w != 0.f ? 1 : 0;
+          const bool valid = unsigned(i - lo - mn) < unsigned(n - mn);
           sl[j] = valid ? mine * a.scale_log2 : neg_inf();
         }
       }
@@ -233,7 +243,7 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
 #pragma unroll
       for (int j = 0; j < SC; ++j) {
         p[j] = __builtin_amdgcn_exp2f(sl[j] - mref);
-        if (s0 + j < e) p[j] *= s_mult[s0 + j];
+        if (s0 + j < e) p[j] *= mult_c[j];
         ps += p[j];
       }
       l = l * corr + ps;
@@ -466,14 +476,25 @@ __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTa
     __syncthreads();
 
     for (int s0 = s; s0 < e; s0 += SC) {
+      // The chunk's slot entries, read together (one wait for all of them
+      // instead of one before each slot's row reads).
+      int lo_c[SC];
+      float w_c[SC], mult_c[SC];
+#pragma unroll
+      for (int j = 0; j < SC; ++j) {
+        const int sc = min(s0 + j, e - 1);
+        lo_c[j] = s_lo[sc];
+        w_c[j] = s_w[sc];
+        mult_c[j] = s_mult[sc];
+      }
       float sl[SC];
 #pragma unroll
       for (int j = 0; j < SC; ++j) {
         sl[j] = neg_inf();
         const int sj = s0 + j;
         if (sj < e) {
-          const int lo = __builtin_amdgcn_readfirstlane(s_lo[sj]);
-          const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_w[sj])));
+          const int lo = __builtin_amdgcn_readfirstlane(lo_c[j]);
+          const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w_c[j])));
           const int r = i - lo - r0;
           uint32_t kw[DW];
           load_words<DW>(Ks + r * RW + c * DW, kw);
@@ -495,10 +516,12 @@ __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTa
           float mine = part[0];
 #pragma unroll
           for (int h = 1; h < G; ++h) mine = (own == h) ? part[h] : mine;
-          const int rel = i - lo;
-          // the nearer row i - lo exists: i >= lo + frac, and below n for a
-          // negative (future) offset
-          const bool valid = active && (rel > 0 || (rel == 0 && w == 0.f)) && rel < n;
+          // The nearer row i - lo exists (i >= lo + frac, and below n for a
+          // negative offset): mn <= i - lo <= n - 1 with mn = 1 for an
+          // interpolated slot, one unsigned compare.  Queries past n have
+          // zero q; their state stays finite and is never stored.
+          const int mn = w != 0.f ? 1 : 0;
+          const bool valid = unsigned(i - lo - mn) < unsigned(n - mn);
           sl[j] = valid ? mine : neg_inf();
         }
       }
@@ -512,7 +535,7 @@ __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTa
 #pragma unroll
       for (int j = 0; j < SC; ++j) {
         p[j] = __builtin_amdgcn_exp2f(sl[j] - mref);
-        if (s0 + j < e) p[j] *= s_mult[s0 + j];
+        if (s0 + j < e) p[j] *= mult_c[j];
         ps += p[j];
       }
       l = l * corr + ps;
