@@ -40,6 +40,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (packed FMA counted)
+
+
+def algorithmic_flops(B, n, hq, hkv, D, S, n_interp):
+    """FLOPs each kernel must do by definition, per launch: 2 S D per
+    query-head for every dot product or weighted sum over the S slots (forward:
+    logits and the value sum; query pass: logits, dp and dq; each key-pass
+    half: dK or dV), plus 6 D per (KV head, query, interpolated rung) for the
+    row interpolation."""
+    qh = B * n * hq
+    lerp = 6 * D * n_interp * B * n * hkv
+    return {
+        "fwd_offsets": 4 * S * D * qh + lerp,
+        "bwd_query": 6 * S * D * qh + lerp,
+        "bwd_key_dk": 2 * S * D * qh + lerp,
+        "bwd_key_dv": 2 * S * D * qh + lerp,
+        "bwd_reduce": 0,
+    }
+
+
 def algorithmic_bytes(B, n, hq, hkv, D, esize):
     """Bytes each kernel must move by definition (every tensor once)."""
     q = B * n * hq * D * esize
@@ -270,6 +290,21 @@ def main():
         "traffic": measured_traffic(dom),
         "algorithmic_bytes_per_launch": ab[dom],
         "avg_launch_us": round(kern[dom]["avg_us"], 3),
+    }
+    # The same launch against the fp32 vector (VALU) peak: by arithmetic
+    # intensity the backward kernels sit above the machine balance
+    # (157.3 TFLOP/s / 8 TB/s), so this is the roofline that binds them.
+    n_interp = sum(1 for f_ in frac if f_ > 0.0)
+    af = algorithmic_flops(B, n, hq, hkv, D, W + 1 + len(lo), n_interp)
+    dom_tf = af[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e12
+    roofline["alu"] = {
+        "achieved": round(dom_tf, 2),
+        "peak": VALU_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(dom_tf / VALU_PEAK_TFLOPS, 4),
+        "flops_per_launch": af[dom],
+        "slots": W + 1 + len(lo),
+        "interpolated_rungs": n_interp,
     }
 
     # Forward alone on the fixed-alpha page-1 layer (window 8, integer rungs).
