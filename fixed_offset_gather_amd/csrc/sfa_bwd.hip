@@ -964,7 +964,7 @@ struct EdgeBwdArgs {
 };
 
 constexpr int kEdgeBQ = 32;  // queries per bwd_edges_query workgroup
-constexpr int kEdgeKB = 64;  // keys per bwd_edges_key workgroup (one wave)
+constexpr int kEdgeKB = 64;  // lanes per bwd_edges_key workgroup (one wave)
 
 template <typename T, int D, int G, int LPQ>
 __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdArgs a) {
@@ -1062,19 +1062,22 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
   }
 }
 
+// One wave holds all D / KC chunks of kEdgeKB / (D / KC) keys (lane = key x
+// chunk), so the chunk lanes of a key read one whole head row of Q and dO
+// together and share its list entry and P, dP, Dvec loads.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kEdgeKB) void bwd_edges_key_kernel(EdgeBwdArgs a) {
   constexpr int KC = key_chunk(D);
   constexpr int NCH = D / KC;
+  constexpr int KPW = kEdgeKB / NCH;  // keys per workgroup
   const int tid = threadIdx.x;
   const int tile = xcd_tile(blockIdx.x, a.tiles);
-  const int c = tile % NCH;
-  const int rest = tile / NCH;
-  const int seq = rest / a.nblk;
-  const int blk = rest % a.nblk;
+  const int c = tid % NCH;
+  const int seq = tile / a.nblk;
+  const int blk = tile % a.nblk;
   const int b = seq / a.hkv, g = seq % a.hkv;
   const int n = a.n;
-  const int j = blk * kEdgeKB + tid;
+  const int j = blk * KPW + tid / NCH;
   const bool activej = j < n;
 
   const T* __restrict__ Q = static_cast<const T*>(a.q);
@@ -1089,37 +1092,46 @@ __global__ __launch_bounds__(kEdgeKB) void bwd_edges_key_kernel(EdgeBwdArgs a) {
   float ak[KC], av[KC];
 #pragma unroll
   for (int x = 0; x < KC; ++x) ak[x] = av[x] = 0.f;
+  // Branch-free over the wave's longest list: the next entry of the list is
+  // read one iteration ahead, so each entry costs one round trip (its P, dP,
+  // Dvec, Q and dO rows, all addressed by the entry) rather than two; an
+  // entry past the lane's count, or one that is not a slot of the table,
+  // reads slot 0 and enters with zero weights.
+  int e_next = cnt > 0 ? irow[0] : -1;
+#pragma unroll 2
   for (int u = 0; u < cmax; ++u) {
-    const int e = u < cnt ? irow[u] : -1;
-    if (e >= 0 && e < nslots) {  // anything else is not a slot of the table
-      const int i = e / a.width, t = e - i * a.width;
-      const size_t w = ((size_t(seq) * n + i) * a.width + t) * G;
-      float pg[G], dpg[G], dvg[G];
-      load_vec<G>(a.P + w, pg);
-      load_vec<G>(a.dP + w, dpg);
-      load_vec<G>(a.Dvec + (size_t(seq) * n + i) * G, dvg);
-      float yk[KC], yv[KC];
+    const int e = e_next;
+    e_next = u + 1 < cnt ? irow[u + 1] : -1;
+    const bool ok = e >= 0 && e < nslots;
+    const int ec = ok ? e : 0;
+    const int i = ec / a.width, t = ec - i * a.width;
+    const size_t w = ((size_t(seq) * n + i) * a.width + t) * G;
+    float pg[G], dpg[G], dvg[G];
+    load_vec<G>(a.P + w, pg);
+    load_vec<G>(a.dP + w, dpg);
+    load_vec<G>(a.Dvec + (size_t(seq) * n + i) * G, dvg);
+    float yk[KC], yv[KC];
 #pragma unroll
-      for (int x = 0; x < KC; ++x) yk[x] = yv[x] = 0.f;
+    for (int x = 0; x < KC; ++x) yk[x] = yv[x] = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * KC;
-        const float ds = a.scale * pg[h] * (dpg[h] - dvg[h]);
-        float qx[KC], ox[KC];
-        load_vec<KC>(Q + off, qx);
-        load_vec<KC>(dO + off, ox);
-#pragma unroll
-        for (int x = 0; x < KC; ++x) {
-          yk[x] = fmaf(ds, qx[x], yk[x]);
-          yv[x] = fmaf(pg[h], ox[x], yv[x]);
-        }
-      }
-      if (a.rope) rotate_pairs<KC, 1>(yk, a.rope + size_t(i) * D, c * KC);  // into the frame of position i
+    for (int h = 0; h < G; ++h) {
+      const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * KC;
+      const float ds = ok ? a.scale * pg[h] * (dpg[h] - dvg[h]) : 0.f;
+      const float pw = ok ? pg[h] : 0.f;
+      float qx[KC], ox[KC];
+      load_vec<KC>(Q + off, qx);
+      load_vec<KC>(dO + off, ox);
 #pragma unroll
       for (int x = 0; x < KC; ++x) {
-        ak[x] += yk[x];
-        av[x] += yv[x];
+        yk[x] = fmaf(ds, qx[x], yk[x]);
+        yv[x] = fmaf(pw, ox[x], yv[x]);
       }
+    }
+    if (a.rope) rotate_pairs<KC, 1>(yk, a.rope + size_t(i) * D, c * KC);  // into the frame of position i
+#pragma unroll
+    for (int x = 0; x < KC; ++x) {
+      ak[x] += yk[x];
+      av[x] += yv[x];
     }
   }
   if (activej) {
@@ -1144,8 +1156,9 @@ int launch_edges_t(const EdgeBwdArgs& a0, hipStream_t st) {
   if (hipError_t e = hipGetLastError()) return int(e);
   {
     ProfileScope ps("bwd_edges_key", st);
-    a.nblk = (a.n + kEdgeKB - 1) / kEdgeKB;
-    a.tiles = a.nblk * seqs * (D / key_chunk(D));
+    constexpr int KPW = kEdgeKB / (D / key_chunk(D));
+    a.nblk = (a.n + KPW - 1) / KPW;
+    a.tiles = a.nblk * seqs;
     hipLaunchKernelGGL((bwd_edges_key_kernel<T, D, G>), dim3(a.tiles), dim3(kEdgeKB), 0, st, a);
   }
   return int(hipGetLastError());
