@@ -475,7 +475,10 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
 // heads interleaved in pairs (word [hp][x] = (head 2hp, head 2hp+1) of dim
 // x), so each head sum is one v_dot2c_f32_f16 per head pair and dim,
 // accumulated in fp32; dS and p enter as f16 pairs.  Half a row per kernel
-// halves the LDS and registers per wave, so four waves share a SIMD.
+// halves the LDS and registers per wave, so four waves share a SIMD.  With
+// one head per KV head (G = 1) a pair would leave half of every f16 word
+// empty, so there the staged words hold the fp32 rows and the weights stay
+// fp32: one FMA per dim and step instead of a v_dot2c doing one useful MAC.
 // SMALL: at most 64 slots (one VGPR per slot-table column).
 template <int D, int G, int PART, bool SMALL>
 __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, SlotTable st) {
@@ -592,7 +595,7 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
         w0 = a.scale * w0 * (raw[1][h0] - raw[2][h0]);
         w1 = a.scale * w1 * (raw[1][h1] - raw[2][h1]);
       }
-      const uint32_t pk = pack_h2(w0, w1);
+      const uint32_t pk = G == 1 ? __float_as_uint(w0) : pack_h2(w0, w1);
       wts[hp] = valid ? pk : 0u;
     }
   };
@@ -700,8 +703,13 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
                 const float ra1 = a1 * c_ - b1 * s_, rb1 = a1 * s_ + b1 * c_;
                 a0 = ra0; b0 = rb0; a1 = ra1; b1 = rb1;
               }
-              wv[2 * x] = pack_h2(a0, a1);
-              wv[2 * x + 1] = pack_h2(b0, b1);
+              if constexpr (G == 1) {
+                wv[2 * x] = __float_as_uint(a0);
+                wv[2 * x + 1] = __float_as_uint(b0);
+              } else {
+                wv[2 * x] = pack_h2(a0, a1);
+                wv[2 * x + 1] = pack_h2(b0, b1);
+              }
             }
             uint32_t* dst = dst0 + row * RW;
             *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
@@ -729,8 +737,23 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
         const bool valid = unsigned(j + delta) < unsigned(n);
         const int lrow = valid ? j + delta - r0 : 0;
         const uint32_t* rowp = Ws + lrow * RW;
-        float y[KC];
-        {
+        float part = 0.f;
+        if constexpr (G == 1) {
+          // y = w0 x: acc += (wt w0) x, and y . own = w0 (x . own)
+          uint32_t xw[KC];
+          load_words<KC>(rowp, xw);
+          const float w0 = __uint_as_float(wts[0]);
+          const float ww = wt * w0;
+          float xo = 0.f;
+#pragma unroll
+          for (int x = 0; x < KC; ++x) {
+            const float xf = __uint_as_float(xw[x]);
+            acc[x] = fmaf(ww, xf, acc[x]);
+            xo = fmaf(xf, own[x], xo);
+          }
+          part = w0 * xo;
+        } else {
+          float y[KC];
           uint32_t xw[KC];
           load_words<KC>(rowp, xw);
 #pragma unroll
@@ -741,12 +764,11 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
 #pragma unroll
             for (int x = 0; x < KC; ++x) y[x] = dot2_h(wts[hp], xw[x], y[x]);
           }
-        }
-        float part = 0.f;
 #pragma unroll
-        for (int x = 0; x < KC; ++x) {
-          acc[x] = fmaf(wt, y[x], acc[x]);
-          part = fmaf(y[x], own[x], part);
+          for (int x = 0; x < KC; ++x) {
+            acc[x] = fmaf(wt, y[x], acc[x]);
+            part = fmaf(y[x], own[x], part);
+          }
         }
         ddacc += tap ? part : -part;
 
