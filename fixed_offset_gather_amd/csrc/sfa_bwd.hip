@@ -28,10 +28,6 @@ namespace sfa {
 
 namespace {
 
-#ifndef SFA_BWD_BQ
-#define SFA_BWD_BQ 32
-#endif
-constexpr int BQ = SFA_BWD_BQ;  // queries per bwd_query workgroup
 constexpr int kCap = 128;
 
 struct BwdArgs {
@@ -69,7 +65,7 @@ __device__ __forceinline__ float own_dot(const float (&a)[G][DC], const float (&
   return HeadSlice<G, LPQ>::reduce(part);
 }
 
-template <typename T, int D, int G, int LPQ, int CAP>
+template <typename T, int D, int G, int LPQ, int CAP, int BQ>
 __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable st) {
   constexpr int DC = D / LPQ;
   constexpr int KS = D + 4;
@@ -861,6 +857,15 @@ constexpr int bwd_lpq() {
   return b < 16 ? b : 16;
 }
 
+// Queries per bwd_query workgroup.  A workgroup's LDS (its stage rows) lets
+// two share a CU; with G >= 4 the 16-lane queries already give 8 waves per
+// workgroup, with fewer heads 8-lane queries need 64 queries for the same
+// (Christoffel query pass 210 -> 163 us; G = 4 at 64 queries: 124 -> 142 us).
+template <int G>
+constexpr int bwd_bq() {
+  return G >= 4 ? 32 : 64;
+}
+
 // Lanes per query in bwd_edges_query (keys straight from global memory):
 // at most 8 dims per lane, same other limits.
 template <int D, int G>
@@ -880,8 +885,8 @@ BwdArgs make_args(const Problem& p, const SlotTable& t, const BwdWorkspace& ws) 
   a.n = p.n;
   a.hq = p.hq;
   a.hkv = p.hkv;
-  a.nblk = (p.n + BQ - 1) / BQ;
-  a.tiles = a.nblk * p.B * p.hkv;
+  a.nblk = 1;  // each launcher sets its own blocks per sequence; tiles / nblk = sequences
+  a.tiles = p.B * p.hkv;
   a.S = t.count;
   a.n_rungs = t.n_rungs;
   a.scale = p.scale;
@@ -890,9 +895,13 @@ BwdArgs make_args(const Problem& p, const SlotTable& t, const BwdWorkspace& ws) 
 }
 
 template <typename T, int D, int G>
-int launch_query_t(const BwdArgs& a, const SlotTable& t, hipStream_t st) {
+int launch_query_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
   constexpr int LPQ = bwd_lpq<D, G>();
-  hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, kCap>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+  constexpr int BQ = bwd_bq<G>();
+  BwdArgs a = a0;
+  a.nblk = (a.n + BQ - 1) / BQ;
+  a.tiles = a.nblk * (a0.tiles / a0.nblk);
+  hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, kCap, BQ>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
   return int(hipGetLastError());
 }
 
@@ -1189,7 +1198,6 @@ int launch_edges_t(const EdgeBwdArgs& a0, hipStream_t st) {
 }  // namespace
 
 size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, BwdWorkspace* ws) {
-  const int nblk = (p.n + BQ - 1) / BQ;
   auto al = [](size_t e) { return (e + 63) & ~size_t(63); };  // 256-byte aligned sections
   const size_t pe = al(size_t(p.B) * p.hkv * t.count * size_t(p.n) * p.G);  // floats per array
   const size_t de = al(size_t(p.B) * p.hkv * size_t(p.n) * p.G);
@@ -1198,7 +1206,6 @@ size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, Bw
   const bool h16 = p.dtype == SFA_BF16;
   const int kb = h16 ? kKeyBlockH16 : key_block(4, p.G, p.D);
   ws->blocks = ((p.n + kb - 1) / kb) * p.B * p.hkv * (p.D / key_chunk(p.D)) * (h16 ? 2 : 1);
-  (void)nblk;
   const size_t dd_e = size_t(ws->blocks) * (t.n_rungs > 0 ? t.n_rungs : 1);
   float* f = static_cast<float*>(base);
   ws->p = f;
