@@ -12,7 +12,10 @@ Cache) so HBM, not the cache, serves them.
 
 Prints ONE JSON line: queries/s of the whole step (value), the step's
 algorithmic HBM GB/s, a roofline object for the dominant kernel (timed with
-HIP events on its launch stream over the timed region), the forward alone on
+HIP events on its launch stream over the timed region; only that kernel's
+launches are bracketed there, since each recorded launch adds event packets
+that hold back the next kernel; the per-kernel breakdown comes from a second
+pass of the same steps with every launch recorded), the forward alone on
 the fixed-alpha page-1 layer (window 8, integer rungs), and the fp64 CPU
 oracle timed on a bounded sample of the same step on one core, and on the
 whole batch over all host cores (one worker process per core, at most 16).
@@ -113,6 +116,24 @@ def measured_traffic(kernel):
     if fields.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return int(fields["hbm_bytes_per_launch"])
+
+
+def measured_valu_busy(kernel):
+    """VALU-busy percent of `kernel` from the committed counter summary
+    (rocprofv3's derived VALUBusy counter), or None when there is none or the
+    kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "%s__page1_learned_step__valu_busy.txt" % kernel)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_hash() or "valu_busy_pct" not in fields:
+        return None
+    return float(fields["valu_busy_pct"])
 
 
 def calibration_copy():
@@ -257,29 +278,44 @@ def main():
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
+    # Per-kernel breakdown: the same number of steps with every launch
+    # bracketed by HIP events on its stream.  Each recorded launch adds two
+    # event packets that also hold back the next kernel (about 35 us per
+    # step with all five kernels recorded), so this pass is not the timed one.
     sfa.profile_reset()
     sfa.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for t in range(args.steps):
         step(t)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     sfa.profile_enable(False)
     kern = {}
     for name in ("fwd_offsets", "bwd_query", "bwd_key_dk", "bwd_key_dv", "bwd_reduce"):
         ms, cnt = sfa.profile_read(name)
         if cnt:
             kern[name] = {"avg_us": 1e3 * ms / cnt, "launches": cnt}
+    dom = max(kern, key=lambda k_: kern[k_]["avg_us"] * kern[k_]["launches"])
+
+    # The timed region: K steps, HIP events only around the dominant kernel
+    # (its average launch time for the roofline, measured live here).
+    sfa.profile_reset()
+    sfa.profile_enable(True, only=dom)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        step(t)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sfa.profile_enable(False, only=None)
+    dms, dcnt = sfa.profile_read(dom)
+    dom_us = 1e3 * dms / dcnt
     ms_per_step = 1e3 * wall / args.steps
     esize = 2
     ab = algorithmic_bytes(B, n, hq, hkv, D, esize)
     step_gbs = ab["step"] / (ms_per_step * 1e-3) / 1e9
     log("kernel avg us:", {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
-        "step ms %.4f" % ms_per_step)
+        "step ms %.4f" % ms_per_step, "%s in the timed region %.2f us" % (dom, dom_us))
 
-    dom = max(kern, key=lambda k_: kern[k_]["avg_us"] * kern[k_]["launches"])
-    dom_gbs = ab[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e9
+    dom_gbs = ab[dom] / (dom_us * 1e-6) / 1e9
     roofline = {
         "kernel": dom,
         "bound": "hbm",
@@ -289,14 +325,14 @@ def main():
         "frac": round(dom_gbs / HBM_PEAK_GBS, 4),
         "traffic": measured_traffic(dom),
         "algorithmic_bytes_per_launch": ab[dom],
-        "avg_launch_us": round(kern[dom]["avg_us"], 3),
+        "avg_launch_us": round(dom_us, 3),
     }
     # The same launch against the fp32 vector (VALU) peak: by arithmetic
     # intensity the backward kernels sit above the machine balance
     # (157.3 TFLOP/s / 8 TB/s), so this is the roofline that binds them.
     n_interp = sum(1 for f_ in frac if f_ > 0.0)
     af = algorithmic_flops(B, n, hq, hkv, D, W + 1 + len(lo), n_interp)
-    dom_tf = af[dom] / (kern[dom]["avg_us"] * 1e-6) / 1e12
+    dom_tf = af[dom] / (dom_us * 1e-6) / 1e12
     roofline["alu"] = {
         "achieved": round(dom_tf, 2),
         "peak": VALU_PEAK_TFLOPS,
@@ -305,6 +341,7 @@ def main():
         "flops_per_launch": af[dom],
         "slots": W + 1 + len(lo),
         "interpolated_rungs": n_interp,
+        "valu_busy_pct": measured_valu_busy(dom),
     }
 
     # Forward alone on the fixed-alpha page-1 layer (window 8, integer rungs).
@@ -424,13 +461,17 @@ def main():
         for t in range(args.warmup):
             cstep(t)
         torch.cuda.synchronize()
-        sfa.profile_reset()
-        sfa.profile_enable(True)
         t0 = time.perf_counter()
         for t in range(args.steps):
             cstep(t)
         torch.cuda.synchronize()
         cwall = time.perf_counter() - t0
+        # per-kernel breakdown from a second pass with HIP events (not timed)
+        sfa.profile_reset()
+        sfa.profile_enable(True)
+        for t in range(args.steps):
+            cstep(t)
+        torch.cuda.synchronize()
         sfa.profile_enable(False)
         ck = {}
         for name in ("fwd_offsets", "bwd_query", "bwd_key_dk", "bwd_key_dv"):
@@ -465,13 +506,16 @@ def main():
     for t in range(args.warmup):
         pstep(t)
     torch.cuda.synchronize()
-    sfa.profile_reset()
-    sfa.profile_enable(True)
     t0 = time.perf_counter()
     for t in range(args.steps):
         pstep(t)
     torch.cuda.synchronize()
     pwall = time.perf_counter() - t0
+    sfa.profile_reset()
+    sfa.profile_enable(True)
+    for t in range(args.steps):
+        pstep(t)
+    torch.cuda.synchronize()
     sfa.profile_enable(False)
     pk = {}
     for name in ("fwd_edges", "bwd_edges_query", "bwd_edges_key"):

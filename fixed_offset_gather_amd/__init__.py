@@ -97,6 +97,7 @@ _sig("sfa_bwd_edges", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _c.c_int, _vp, _
 _sig("sfa_profile_enable", _c.c_int, [_c.c_int])
 _sig("sfa_profile_read", _c.c_int, [_c.c_char_p, _c.POINTER(_c.c_double), _c.POINTER(_c.c_int64)])
 _sig("sfa_profile_reset", _c.c_int, [])
+_sig("sfa_profile_select", _c.c_int, [_c.c_char_p])
 
 
 class SfaError(RuntimeError):
@@ -398,7 +399,10 @@ def bwd_edges(q, k, v, lse, dout, edges, count, inv, inv_count, rope=None, scale
 
 # ------------------------------------------------------------ timing
 
-def profile_enable(on=True):
+def profile_enable(on=True, only=None):
+    """Record HIP events around kernel launches; `only` restricts the
+    recording to the launches of that kernel (None: every kernel)."""
+    _lib.sfa_profile_select(only.encode() if only else None)
     _lib.sfa_profile_enable(1 if on else 0)
 
 

@@ -102,6 +102,7 @@ struct Pending {
 };
 std::mutex g_prof_mu;
 bool g_prof_on = false;
+std::string g_prof_only;  // record only this kernel's launches when not empty
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_free;  // recycled events: no creation per launch
 std::map<std::string, std::pair<double, int64_t>> g_totals;
@@ -121,6 +122,7 @@ hipEvent_t take_event() {
 
 ProfileScope::ProfileScope(const char* nm, void* st) : name(nm), stream(st), ev0(nullptr) {
   if (!g_prof_on || !nm) return;  // a null name records nothing
+  if (!g_prof_only.empty() && g_prof_only != nm) return;
   hipEvent_t e = take_event();
   if (e && hipEventRecord(e, static_cast<hipStream_t>(stream)) == hipSuccess) ev0 = e;
 }
@@ -164,6 +166,12 @@ using namespace sfa;
 extern "C" int sfa_profile_enable(int on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;
+  return SFA_OK;
+}
+
+extern "C" int sfa_profile_select(const char* kernel) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_only = kernel ? kernel : "";
   return SFA_OK;
 }
 

@@ -307,10 +307,14 @@ int sfa_bwd_edges(const sfa_attn* a, const int32_t* edges, const int32_t* count,
  * "bwd_edges_query", "bwd_edges_key",
  * "bwd_reduce"; with bf16 tensors the key pass is the two kernels
  * "bwd_key_dk" and "bwd_key_dv" instead of "bwd_key");
- * sfa_profile_reset drops all records.  Not thread-safe with
- * concurrent launches.
+ * sfa_profile_reset drops all records.  sfa_profile_select(name) restricts
+ * the recording to the launches of the named kernel (each recorded launch
+ * adds two event packets to its stream, which also delay the stream's next
+ * kernel); sfa_profile_select(NULL) records every kernel again.  Not
+ * thread-safe with concurrent launches.
  */
 int sfa_profile_enable(int on);
+int sfa_profile_select(const char* kernel);
 int sfa_profile_read(const char* kernel, double* total_ms, int64_t* launches);
 int sfa_profile_reset(void);
 

@@ -270,3 +270,16 @@ def test_negative_offsets_need_the_signed_flag():
     assert lib.sfa_bwd_workspace_bytes(ctypes.byref(a)) > 0
     a.flags = 4
     assert lib.sfa_bwd_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_profile_controls_without_launches():
+    """The profiling controls work without a device: select one kernel, read
+    a kernel that was never launched (zero), select all again, reset."""
+    lib = sfa.library()
+    assert lib.sfa_profile_select(b"bwd_query") == 0
+    assert lib.sfa_profile_select(None) == 0
+    sfa.profile_enable(True, only="bwd_query")
+    sfa.profile_enable(False)
+    sfa.profile_reset()
+    assert sfa.profile_read("bwd_query") == (0.0, 0)
+    sfa.profile_enable(False, only=None)
