@@ -1043,21 +1043,23 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
   const size_t wrow = (size_t(seq) * n + (active ? i : 0)) * a.width;
   float dvec = 0.f;
 
+  // Branch-free over the wave's longest list, the next list entry read one
+  // step ahead: a padding entry (or a key outside [0, n)) reads row 0 and is
+  // masked by p = 0.
+  int key_next = cnt > 0 ? erow[0] : -1;
+#pragma unroll 2
   for (int t = 0; t < cmax; ++t) {
-    const int key = t < cnt ? erow[t] : -1;
+    const int key = key_next;
+    key_next = t + 1 < cnt ? erow[t + 1] : -1;
     const bool valid = key >= 0 && key < n;
+    const int kc = valid ? key : 0;
     float kt[DC], vt[DC];
-    if (valid) {
-      load_vec<DC>(Kseq + size_t(key) * kv_row, kt);
-      if (a.rope) rotate_pairs<DC, 1>(kt, a.rope + size_t(key) * D, c * DC);
-      load_vec<DC>(Vseq + size_t(key) * kv_row, vt);
-    } else {
-#pragma unroll
-      for (int x = 0; x < DC; ++x) kt[x] = vt[x] = 0.f;
-    }
+    load_vec<DC>(Kseq + size_t(kc) * kv_row, kt);
+    if (a.rope) rotate_pairs<DC, 1>(kt, a.rope + size_t(kc) * D, c * DC);
+    load_vec<DC>(Vseq + size_t(kc) * kv_row, vt);
     const float sdot = own_dot<G, LPQ, DC>(qv, kt);
     const float dp = own_dot<G, LPQ, DC>(dov, vt);
-    const float ex = __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2);  // finite: kt = 0 if invalid
+    const float ex = __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2);
     const float p = valid ? ex : 0.f;
     const float pdp = p * dp;
     dvec += pdp;
