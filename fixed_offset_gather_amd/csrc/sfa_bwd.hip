@@ -1047,7 +1047,6 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
   // step ahead: a padding entry (or a key outside [0, n)) reads row 0 and is
   // masked by p = 0.
   int key_next = cnt > 0 ? erow[0] : -1;
-#pragma unroll 2
   for (int t = 0; t < cmax; ++t) {
     const int key = key_next;
     key_next = t + 1 < cnt ? erow[t + 1] : -1;
@@ -1131,7 +1130,6 @@ __global__ __launch_bounds__(kEdgeKB) void bwd_edges_key_kernel(EdgeBwdArgs a) {
   // entry past the lane's count, or one that is not a slot of the table,
   // reads slot 0 and enters with zero weights.
   int e_next = cnt > 0 ? irow[0] : -1;
-#pragma unroll 2
   for (int u = 0; u < cmax; ++u) {
     const int e = e_next;
     e_next = u + 1 < cnt ? irow[u + 1] : -1;
