@@ -55,6 +55,16 @@ extern "C" {
 
 #define SFA_F32 0  /* float32 tensors */
 #define SFA_BF16 1 /* bfloat16 tensors (accumulation is float32) */
+/*
+ * With SFA_BF16 the kernels take their products on f16 operands: the staged
+ * K and V rows (K rotated), the scaled query, the staged rows of the key
+ * pass and the probability weights are rounded to f16, and every sum is
+ * accumulated in float32.  Inputs must therefore stay within f16's range:
+ * every element of Q, K, V and dO, after rotation (which can grow one
+ * element of a pair by up to sqrt 2), below 65504 in magnitude; values below
+ * 2^-14 keep only f16's subnormal precision.  bf16's wider exponent range is
+ * not supported and is not checked.
+ */
 
 #define SFA_MAX_OFFSETS 128 /* shared offsets per call */
 #define SFA_MAX_SLOTS 192   /* window + 1 + offsets */
