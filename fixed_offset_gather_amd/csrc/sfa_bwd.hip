@@ -625,7 +625,15 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
     advance();
     load_step(raw);
   }
+  // The staged rows form a ring in LDS: query j0 + q sits in slot
+  // (q - q0) mod kcap, q0 the first stage's first row.  Stages run in
+  // increasing offset order and each spans at most kcap rows, so rows that an
+  // earlier stage staged and the new stage still needs ([lo0, have_hi]) are
+  // intact, and only the rows above have_hi are staged (consecutive rungs
+  // share most of their rows).
   const int kcap = a.kcap;
+  int q0 = 0, have_hi = 0;
+  bool first_stage = true;
   int s = 0;
   while (s < S) {
     const int lo0 = slot_i(vlo, s);
@@ -640,6 +648,15 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
     }
     const int r0 = j0 + lo0;
     const int nrows = min(lomax - lo0 + KB + 1, n - r0);
+    const int hi = lo0 + nrows - 1;  // last row of the stage, relative to j0
+    if (first_stage) {
+      q0 = lo0;
+      have_hi = lo0 - 1;
+      first_stage = false;
+    }
+    const int base = (lo0 - q0) % kcap;    // ring slot of row lo0 (lo0 >= q0)
+    const int fnew = max(lo0, have_hi + 1);  // first row not staged yet
+    const int nnew = hi - fnew + 1;
 
     __syncthreads();
 
@@ -655,11 +672,12 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
       const int xh = pc % XH;
       const bool pair = 2 * hp + 1 < G;
       const size_t rstride = size_t(a.hq) * D;
-      // addresses from signed row indices: r0 < 0 with negative offsets
-      const int64_t grow0 = int64_t(b) * n + r0;  // global query row of LDS row 0
+      // addresses from signed row indices: rows < 0 with negative offsets
+      const int rn = j0 + fnew;                   // query of the first new row
+      const int64_t grow0 = int64_t(b) * n + rn;  // its global row
       const size_t col = (size_t(g) * G + 2 * hp) * D + c * KC + xh * 8;
       uint32_t* dst0 = Ws + hp * KC + xh * 8;
-      for (int row0 = tid / PPR; row0 < nrows; row0 += SB * RSTEP) {
+      for (int row0 = tid / PPR; row0 < nnew; row0 += SB * RSTEP) {
         uint4 u0[SB], u1[SB];
         float4 ra[SB], rb[SB];
 #pragma unroll
@@ -669,12 +687,12 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
           ra[u] = rb[u] = make_float4(1.f, 0.f, 1.f, 0.f);
           // rows before the sequence (negative offsets) are staged as zeros:
           // masked steps read LDS row 0 with zero weights
-          if (row < nrows && r0 + row >= 0) {
+          if (row < nnew && rn + row >= 0) {
             const bf16_t* src = X + size_t(grow0 + row) * rstride + col;
             u0[u] = *reinterpret_cast<const uint4*>(src);
             if (pair) u1[u] = *reinterpret_cast<const uint4*>(src + D);
             if (rope) {
-              const float* rp = a.rope + size_t(r0 + row) * D + c * KC + xh * 8;
+              const float* rp = a.rope + size_t(rn + row) * D + c * KC + xh * 8;
               ra[u] = *reinterpret_cast<const float4*>(rp);
               rb[u] = *reinterpret_cast<const float4*>(rp + 4);
             }
@@ -683,7 +701,7 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
 #pragma unroll
         for (int u = 0; u < SB; ++u) {
           const int row = row0 + u * RSTEP;
-          if (row < nrows) {
+          if (row < nnew) {
             const uint32_t e0[4] = {u0[u].x, u0[u].y, u0[u].z, u0[u].w};
             const uint32_t e1[4] = {u1[u].x, u1[u].y, u1[u].z, u1[u].w};
             const float cs[8] = {ra[u].x, ra[u].y, ra[u].z, ra[u].w, rb[u].x, rb[u].y, rb[u].z, rb[u].w};
@@ -707,7 +725,9 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
                 wv[2 * x + 1] = pack_h2(b0, b1);
               }
             }
-            uint32_t* dst = dst0 + row * RW;
+            int slot = fnew - lo0 + row + base;  // < 2 kcap
+            slot = slot >= kcap ? slot - kcap : slot;
+            uint32_t* dst = dst0 + slot * RW;
             *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
             *reinterpret_cast<uint4*>(dst + 4) = make_uint4(wv[4], wv[5], wv[6], wv[7]);
           }
@@ -715,6 +735,7 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
       }
     }
     __syncthreads();
+    have_hi = max(have_hi, hi);
 
     for (int sj = s; sj < e; ++sj) {
       const int lo = slot_i(vlo, sj);
@@ -731,7 +752,9 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
         // Window slots run the same arithmetic with weight 1; their dd sum is
         // never stored.  One straight-line body keeps the registers put.
         const bool valid = unsigned(j + delta) < unsigned(n);
-        const int lrow = valid ? j + delta - r0 : 0;
+        int slot = j + delta - r0 + base;  // j + delta - r0 in [0, nrows) when valid
+        slot = slot >= kcap ? slot - kcap : slot;
+        const int lrow = valid ? slot : 0;
         const uint32_t* rowp = Ws + lrow * RW;
         float part = 0.f;
         if constexpr (G == 1) {
