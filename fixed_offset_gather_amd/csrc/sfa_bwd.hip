@@ -4,23 +4,28 @@
 // floor-plus-one rows keeps a gradient to the offset distance, hence to
 // alpha and theta through the alpha parameterisation).
 //
-// Three launches on one stream, no atomics, fixed summation order:
+// Launches on one stream, no atomics, fixed summation order:
 //
 // bwd_query (query-centric, same staging as the forward): recomputes each
 //   logit, p = exp(logit - lse) and dp = dO.v~ in one pass over the slots.
 //   Dvec = rowsum(dO*O) is formed exactly as sum_slots p dp (not from the
 //   rounded forward output), and dq~ = scale sum p (dp - Dvec) k~ is
 //   accumulated as scale (sum p dp k~ - Dvec sum p k~), then rotated back to
-//   dQ.  p (0 where the slot has no row), dp and Dvec of every (query,
-//   slot, head) go to the workspace.
+//   dQ.  The per-slot dot sums over a query's lanes are a reduce-scatter
+//   over the heads (HeadSlice).  p (0 where the slot has no row), dp and
+//   Dvec of every (query, slot, head) go to the workspace.
 // bwd_key (key-centric transpose gather): key j receives from query j+lo
 //   (weight 1-frac) and j+lo+1 (weight frac) of every slot; those queries
 //   form contiguous ranges, so each lane gathers instead of scattering.
-//   dK uses the relative rotation R(j)^T R(i) = R(i-j) with i-j fixed per
-//   (slot, tap), so unrotated Q rows are combined first and rotated once.
-//   It also sums the per-block partials of dL/dd_k.
+//   fp32: one kernel; dK uses the relative rotation R(j)^T R(i) = R(i-j)
+//   with i-j fixed per (slot, tap), so unrotated Q rows are combined first
+//   and rotated once.  bf16: two kernels (dK, dV), each staging half a query
+//   row into an LDS ring of rows that consecutive stages share.  Both also
+//   sum the per-block partials of dL/dd_k.
 // bwd_reduce: sums the dd partials in block order; dalpha = sum f_k dd_k;
 //   dtheta = (alpha - 1/2)(3/2 - alpha) dalpha.
+// The edge-list backward (bwd_edges_query, bwd_edges_key, further below)
+// does the same per query and per key over explicit lists.
 #include "sfa_device.h"
 #include "sfa_internal.h"
 
