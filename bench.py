@@ -24,6 +24,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -273,6 +274,12 @@ def main():
         o, lse = sfa.fwd(q, k, v, W, lo_, frac_, rope, out=o_buf, lse=lse_buf)
         return sfa.bwd(q, k, v, lse, do, W, lo_, frac_, rope, base=base, alpha=alpha, workspace=ws)
 
+    # Python's cyclic garbage collector stays off through the GPU sections:
+    # a generation-2 collection (tens of ms once the process holds torch and
+    # the oracle's objects) landing in a timed loop would be charged to the
+    # kernels.  Reference counting still frees everything the loops drop.
+    gc.collect()
+    gc.disable()
     if args.calibrate_copy:
         calibration_copy()
     for t in range(args.warmup):
@@ -561,6 +568,7 @@ def main():
         "powerlaw_step": powerlaw_step,
         "length_extrapolation": {"workload": "page-1 layer forward, W 8, 32,768 tokens per batch", "by_seqlen": lengths},
     }
+    gc.enable()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, alpha, args.cpu_seqs)
         out["cpu_baseline_all_cores"] = all_cores
