@@ -690,8 +690,8 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
           const int row = row0 + u * RSTEP;
           u0[u] = u1[u] = make_uint4(0, 0, 0, 0);
           ra[u] = rb[u] = make_float4(1.f, 0.f, 1.f, 0.f);
-          // rows before the sequence (negative offsets) are staged as zeros:
-          // masked steps read LDS row 0 with zero weights
+          // rows before the sequence (negative offsets) are staged as zeros;
+          // masked steps read ring slot 0 with zero weights
           if (row < nnew && rn + row >= 0) {
             const bf16_t* src = X + size_t(grow0 + row) * rstride + col;
             u0[u] = *reinterpret_cast<const uint4*>(src);
@@ -753,7 +753,7 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
         const int delta = lo + tap;
         const float wt = tap ? w : 1.f - w;
         // Query j + delta; the query pass stored p = 0 where the slot has no
-        // row for it.  Masked steps read staged row 0 with zero weights.
+        // row for it.  Masked steps read ring slot 0 with zero weights.
         // Window slots run the same arithmetic with weight 1; their dd sum is
         // never stored.  One straight-line body keeps the registers put.
         const bool valid = unsigned(j + delta) < unsigned(n);
