@@ -26,28 +26,7 @@
 
 namespace sfa {
 
-// Tuning knobs (compile-time): rows per LDS stage of the f16 kernel, whether
-// a stage's global loads are all issued before conversion, and the waves
-// per SIMD the register allocation must allow (0 = compiler's choice).
-#ifndef SFA_FWD_CAP
-#define SFA_FWD_CAP 128
-#endif
-#ifndef SFA_FWD_HOIST
-#define SFA_FWD_HOIST 0
-#endif
-#ifndef SFA_FWD_MINWAVES
-#define SFA_FWD_MINWAVES 0
-#endif
-// bf16 tensors: 0 = fp32 kernel, 1 = f16 keys and values, 2 = f16 keys and
-// fp32 values.
-#ifndef SFA_FWD_BF16_PATH
-#define SFA_FWD_BF16_PATH 1
-#endif
-
-#ifndef SFA_FWD_BQ
-#define SFA_FWD_BQ 64
-#endif
-constexpr int BQ = SFA_FWD_BQ;  // queries per workgroup
+constexpr int BQ = 64;   // queries per workgroup
 constexpr int SC = 8;    // slots per online-softmax chunk
 constexpr int ESC = 4;   // edges per chunk (keys come from global memory)
 
@@ -304,23 +283,16 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
 // f16 products per instruction, fp32 accumulation), interpolation is packed
 // f16 arithmetic, and the value sum is a mixed-precision FMA into fp32
 // accumulators.  The softmax and the output accumulation stay in fp32.
-#if SFA_FWD_MINWAVES > 0
-#define SFA_FWD_BOUNDS(T) __launch_bounds__(T, SFA_FWD_MINWAVES)
-#else
-#define SFA_FWD_BOUNDS(T) __launch_bounds__(T)
-#endif
-
-template <int D, int G, int LPQ, int CAP, bool VF32, bool INTERP>
-__global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTable st) {
+template <int D, int G, int LPQ, int CAP, bool INTERP>
+__global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTable st) {
   constexpr int DC = D / LPQ;  // dims per lane
   constexpr int DW = DC / 2;   // f16 pairs per lane
   constexpr int RW = D / 2 + 4;  // 32-bit words per LDS row (16-byte pad)
-  constexpr int VRW = VF32 ? D + 4 : RW;  // words per value row
   constexpr int CPR = D / 8;     // 16-byte global chunks (8 bf16) per row
   constexpr int NT = BQ * LPQ;
   static_assert(DC >= 2 && DC % 2 == 0, "lane chunk");
   __shared__ __align__(16) uint32_t Ks[CAP * RW];
-  __shared__ __align__(16) uint32_t Vs[CAP * VRW];
+  __shared__ __align__(16) uint32_t Vs[CAP * RW];
 
   const int tid = threadIdx.x;
   const int qq = tid / LPQ;
@@ -397,60 +369,6 @@ __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTa
     const int nrows = lomax - lo0 + BQ;
 
     __syncthreads();
-#if SFA_FWD_HOIST
-    {
-      // Issue every global load of this thread's chunks first (they overlap
-      // in flight), then rotate, convert and store.
-      constexpr int PER = (CAP * CPR + NT - 1) / NT;
-      uint4 kr[PER], vr[PER];
-      float4 cs0[PER], cs1[PER];
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int t = tid + u * NT;
-        const int row = t / CPR, cc = t % CPR;
-        const int pos = r0 + row;
-        kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
-        cs0[u] = cs1[u] = make_float4(1.f, 0.f, 1.f, 0.f);
-        if (t < nrows * CPR && pos >= 0 && pos < n) {
-          kr[u] = *reinterpret_cast<const uint4*>(Kseq + size_t(pos) * kv_row + cc * 8);
-          vr[u] = *reinterpret_cast<const uint4*>(Vseq + size_t(pos) * kv_row + cc * 8);
-          if (a.rope) {
-            const float4* rp = reinterpret_cast<const float4*>(a.rope + size_t(pos) * D + cc * 8);
-            cs0[u] = rp[0];
-            cs1[u] = rp[1];
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int t = tid + u * NT;
-        if (t < nrows * CPR) {
-          const int row = t / CPR, cc = t % CPR;
-          const uint32_t kw4[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
-          const float cs[8] = {cs0[u].x, cs0[u].y, cs0[u].z, cs0[u].w, cs1[u].x, cs1[u].y, cs1[u].z, cs1[u].w};
-          uint32_t ko[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const float e0 = bf16_lo(kw4[x]), e1 = bf16_hi(kw4[x]);
-            const float c_ = cs[2 * x], s_ = cs[2 * x + 1];
-            ko[x] = pack_h2(e0 * c_ - e1 * s_, e0 * s_ + e1 * c_);
-          }
-          *reinterpret_cast<uint4*>(Ks + row * RW + cc * 4) = make_uint4(ko[0], ko[1], ko[2], ko[3]);
-          if constexpr (VF32) {
-            float* vrow = reinterpret_cast<float*>(Vs + row * VRW) + cc * 8;
-            *reinterpret_cast<float4*>(vrow) =
-                make_float4(bf16_lo(vr[u].x), bf16_hi(vr[u].x), bf16_lo(vr[u].y), bf16_hi(vr[u].y));
-            *reinterpret_cast<float4*>(vrow + 4) =
-                make_float4(bf16_lo(vr[u].z), bf16_hi(vr[u].z), bf16_lo(vr[u].w), bf16_hi(vr[u].w));
-          } else {
-            *reinterpret_cast<uint4*>(Vs + row * VRW + cc * 4) =
-                make_uint4(pack_h2(bf16_lo(vr[u].x), bf16_hi(vr[u].x)), pack_h2(bf16_lo(vr[u].y), bf16_hi(vr[u].y)),
-                           pack_h2(bf16_lo(vr[u].z), bf16_hi(vr[u].z)), pack_h2(bf16_lo(vr[u].w), bf16_hi(vr[u].w)));
-          }
-        }
-      }
-    }
-#else
     for (int t = tid; t < nrows * CPR; t += NT) {
       const int row = t / CPR, cc = t % CPR;
       const int pos = r0 + row;
@@ -465,14 +383,9 @@ __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTa
       }
       *reinterpret_cast<uint4*>(Ks + row * RW + cc * 4) =
           make_uint4(pack_h2(kf[0], kf[1]), pack_h2(kf[2], kf[3]), pack_h2(kf[4], kf[5]), pack_h2(kf[6], kf[7]));
-      if constexpr (VF32) {
-        store_vec<8>(reinterpret_cast<float*>(Vs + row * VRW) + cc * 8, vf);
-      } else {
-        *reinterpret_cast<uint4*>(Vs + row * VRW + cc * 4) =
-            make_uint4(pack_h2(vf[0], vf[1]), pack_h2(vf[2], vf[3]), pack_h2(vf[4], vf[5]), pack_h2(vf[6], vf[7]));
-      }
+      *reinterpret_cast<uint4*>(Vs + row * RW + cc * 4) =
+          make_uint4(pack_h2(vf[0], vf[1]), pack_h2(vf[2], vf[3]), pack_h2(vf[4], vf[5]), pack_h2(vf[6], vf[7]));
     }
-#endif
     __syncthreads();
 
     for (int s0 = s; s0 < e; s0 += SC) {
@@ -555,38 +468,22 @@ __global__ SFA_FWD_BOUNDS(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTa
           const int r = i - lo - r0;
           float ph[G];
           Bcast<G, LPQ>::run(p[j], ph);
-          if constexpr (VF32) {
-            const float* vrow = reinterpret_cast<const float*>(Vs + r * VRW) + c * DC;
-            float vt[DC];
-            load_vec<DC>(vrow, vt);
-            if (INTERP && w != 0.f) {
-              float vb[DC];
-              load_vec<DC>(vrow - VRW, vb);
+          uint32_t vw[DW];
+          load_words<DW>(Vs + r * RW + c * DW, vw);
+          if (INTERP && w != 0.f) {
+            uint32_t vb[DW];
+            load_words<DW>(Vs + (r - 1) * RW + c * DW, vb);
+            const half2_t w2 = {(_Float16)w, (_Float16)w};
 #pragma unroll
-              for (int x = 0; x < DC; ++x) vt[x] = fmaf(w, vb[x] - vt[x], vt[x]);
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-              for (int x = 0; x < DC; ++x) o[h][x] = fmaf(ph[h], vt[x], o[h][x]);
-          } else {
-            uint32_t vw[DW];
-            load_words<DW>(Vs + r * VRW + c * DW, vw);
-            if (INTERP && w != 0.f) {
-              uint32_t vb[DW];
-              load_words<DW>(Vs + (r - 1) * VRW + c * DW, vb);
-              const half2_t w2 = {(_Float16)w, (_Float16)w};
-#pragma unroll
-              for (int x = 0; x < DW; ++x) vw[x] = lerp_h2(vw[x], vb[x], w2);
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-              for (int x = 0; x < DW; ++x) {
-                o[h][2 * x] = fma_lo(ph[h], vw[x], o[h][2 * x]);
-                o[h][2 * x + 1] = fma_hi(ph[h], vw[x], o[h][2 * x + 1]);
-              }
+            for (int x = 0; x < DW; ++x) vw[x] = lerp_h2(vw[x], vb[x], w2);
           }
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int x = 0; x < DW; ++x) {
+              o[h][2 * x] = fma_lo(ph[h], vw[x], o[h][2 * x]);
+              o[h][2 * x + 1] = fma_hi(ph[h], vw[x], o[h][2 * x + 1]);
+            }
         }
       }
     }
@@ -761,8 +658,8 @@ constexpr int fwd_lpq() {
 template <typename T, int D, int G, bool INTERP>
 void launch_fwd_offsets_i(const SlotTable& t, const FwdArgs& a, hipStream_t st) {
   constexpr int LPQ = fwd_lpq<D, G>();
-  if constexpr (sizeof(T) == 2 && SFA_FWD_BF16_PATH > 0) {
-    hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, SFA_FWD_CAP, SFA_FWD_BF16_PATH == 2, INTERP>),
+  if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, kCap, INTERP>),
                        dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
   } else {
     hipLaunchKernelGGL((fwd_offsets_kernel<T, D, G, LPQ, kCap, INTERP>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a,
