@@ -84,7 +84,9 @@ int build_slots(const sfa_attn* a, SlotTable* t, bool merge) {
       continue;
     }
     t->lo[c] = v[s].lo;
-    t->frac[c] = v[s].frac;
+    // Kernels test frac != 0 on its bit pattern (a scalar compare), so a
+    // zero fraction is stored as +0.
+    t->frac[c] = v[s].frac == 0.f ? 0.f : v[s].frac;
     t->mult[c] = 1.f;
     t->rung[c] = v[s].rung;
     ++c;

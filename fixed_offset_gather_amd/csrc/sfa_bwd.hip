@@ -78,8 +78,16 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
   constexpr int CPR = D / E;
   constexpr int NT = BQ * LPQ;
   using HS = HeadSlice<G, LPQ>;
-  __shared__ __align__(16) float Ks[CAP * KS];
-  __shared__ __align__(16) float Vs[CAP * KS];
+  // K and V rows of a stage in one LDS array, each led by a pad row:
+  // [pad][K rows 0..CAP-1][pad][V rows 0..CAP-1].  Row r - 1 of a slot (its
+  // interpolation partner, or a pad row when r = 0) is then never below the
+  // array, and the four rows a slot reads lie at fixed byte offsets from it,
+  // so one address per slot serves all of them.
+  constexpr int VOFF = (CAP + 1) * KS;  // floats from a K row to the same V row
+  static_assert((VOFF + KS) * 4 < 65536, "row offsets fit a ds_read offset");
+  __shared__ __align__(16) float KV[(2 * CAP + 2) * KS];
+  float* const Ks = KV + KS;
+  float* const Vs = Ks + VOFF;
 
   const int tid = threadIdx.x;
   const int qq = tid / LPQ;
@@ -124,6 +132,9 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
   const T* Kseq = K + size_t(b) * n * kv_row + size_t(g) * D;
   const T* Vseq = V + size_t(b) * n * kv_row + size_t(g) * D;
   const size_t ws_seq = size_t(seq) * a.S;
+  // Byte offset of this lane's (query, head) entry within one slot's plane
+  // of the p / dp workspace; the plane's base is uniform.
+  const unsigned ws_lane = unsigned(i * G + own) * 4u;
 
   int s = 0;
   const int S = st.count;
@@ -161,17 +172,23 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
     }
     __syncthreads();
 
+    // K row r - 1 of the slot at lo = 0; a slot's rows are lo rows earlier.
+    const float* const lane_kv = Ks + (i - r0 - 1) * KS + c * DC;
     for (int sj = s; sj < e; ++sj) {
       const int lo = st.lo[sj];
-      const float w = st.frac[sj];
-      const int r = i - lo - r0;
+      // frac is +0 or positive: its bit pattern, read as an integer, decides
+      // interpolation with a scalar compare.
+      const int wbits = reinterpret_cast<const int*>(st.frac)[sj];
+      const float w = __int_as_float(wbits);
+      const bool interp = wbits != 0;
+      const float* const kp = lane_kv - lo * KS;  // K row r - 1
       float kt[DC], vt[DC];
-      load_vec<DC>(Ks + r * KS + c * DC, kt);
-      load_vec<DC>(Vs + r * KS + c * DC, vt);
-      if (w != 0.f) {
+      load_vec<DC>(kp + KS, kt);
+      load_vec<DC>(kp + KS + VOFF, vt);
+      if (interp) {
         float kb[DC], vb[DC];
-        load_vec<DC>(Ks + (r - 1) * KS + c * DC, kb);
-        load_vec<DC>(Vs + (r - 1) * KS + c * DC, vb);
+        load_vec<DC>(kp, kb);
+        load_vec<DC>(kp + VOFF, vb);
 #pragma unroll
         for (int x = 0; x < DC; ++x) {
           kt[x] = fmaf(w, kb[x] - kt[x], kt[x]);
@@ -193,20 +210,27 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
       const float sdot = HS::reduce(sp);
       const float dp = HS::reduce(dps);
       // The nearer row i - lo exists when mn <= i - lo <= n - 1, mn = 1 for
-      // an interpolated slot (its farther row i - lo - 1 must exist too).
-      // One unsigned compare and a select, no branch.  Queries past n (the
-      // ragged last block) have zero q and dO, so their p stays finite and
-      // is never stored.
-      const int mn = w != 0.f ? 1 : 0;
+      // an interpolated slot (its farther row i - lo - 1 must exist too):
+      // one unsigned compare and a select, no branch.  mn comes from integer
+      // arithmetic on the fraction's bits (a non-negative int), so it stays
+      // in an SGPR.  Queries past n (the ragged last block) have zero q and
+      // dO, so their p stays finite and is never stored.
+      const int mn = min(wbits, 1);
       const bool valid = unsigned(i - lo - mn) < unsigned(n - mn);
       const float ex = __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2);
       const float p = valid ? ex : 0.f;
       const float pdp = p * dp;
       dvec += pdp;
       if (active && HS::writer(c)) {  // p = 0 where the slot has no row for query i
-        const size_t widx = ((ws_seq + sj) * n + i) * G + own;
-        a.P[widx] = p;
-        a.dP[widx] = dp;
+        // The slot's plane bases stay scalar (global_store with an SGPR
+        // base and the lane's 32-bit offset); the empty asm keeps them from
+        // being folded into per-lane 64-bit pointers.
+        const size_t plane = (ws_seq + sj) * size_t(n) * G;
+        float* pb = a.P + plane;
+        float* db = a.dP + plane;
+        asm volatile("" : "+s"(pb), "+s"(db));
+        store_global_at(pb, ws_lane, p);
+        store_global_at(db, ws_lane, dp);
       }
       float ph[G], pdh[G];
       HS::bcast(p, ph);

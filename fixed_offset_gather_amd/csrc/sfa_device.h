@@ -84,6 +84,18 @@ __device__ __forceinline__ void load_vec(const bf16_t* __restrict__ p, float (&o
   }
 }
 
+// One float at a uniform base plus a 32-bit per-lane byte offset, stored
+// through the global address space (global_store with an SGPR base).
+__device__ __forceinline__ void store_global_at(float* base, unsigned byte_off, float v) {
+  typedef __attribute__((address_space(1))) char gchar;
+  typedef __attribute__((address_space(1))) float gfloat;
+  // The empty asm keeps the offset a 32-bit VGPR at the store, so its
+  // zero-extension is matched into the instruction instead of being hoisted
+  // into a 64-bit register pair.
+  asm volatile("" : "+v"(byte_off));
+  *(gfloat*)((gchar*)base + byte_off) = v;  // C cast: address-space conversion
+}
+
 template <int N>
 __device__ __forceinline__ void store_vec(float* __restrict__ p, const float (&in)[N]) {
   if constexpr (N % 4 == 0) {

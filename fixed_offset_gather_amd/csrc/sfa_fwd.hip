@@ -27,7 +27,7 @@
 namespace sfa {
 
 constexpr int BQ = 64;   // queries per workgroup
-constexpr int SC = 8;    // slots per online-softmax chunk
+constexpr int SC = 4;    // slots per online-softmax chunk
 constexpr int ESC = 4;   // edges per chunk (keys come from global memory)
 
 template <int D>
@@ -291,8 +291,16 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
   constexpr int CPR = D / 8;     // 16-byte global chunks (8 bf16) per row
   constexpr int NT = BQ * LPQ;
   static_assert(DC >= 2 && DC % 2 == 0, "lane chunk");
-  __shared__ __align__(16) uint32_t Ks[CAP * RW];
-  __shared__ __align__(16) uint32_t Vs[CAP * RW];
+  // K and V rows of a stage in one LDS array, each led by a pad row:
+  // [pad][K rows 0..CAP-1][pad][V rows 0..CAP-1].  Row r - 1 of a slot (its
+  // interpolation partner, or a pad row when r = 0) is never below the
+  // array, and the four rows a slot reads lie at fixed byte offsets from it,
+  // so one address per slot serves all of them.
+  constexpr int VOFF = (CAP + 1) * RW;  // words from a K row to the same V row
+  static_assert((VOFF + RW) * 4 < 65536, "row offsets fit a ds_read offset");
+  __shared__ __align__(16) uint32_t KV[(2 * CAP + 2) * RW];
+  uint32_t* const Ks = KV + RW;
+  uint32_t* const Vs = Ks + VOFF;
 
   const int tid = threadIdx.x;
   const int qq = tid / LPQ;
@@ -310,12 +318,15 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
 
   // Slot table copied to LDS once: the hot loops read it with uniform
   // addresses instead of scalar loads from the kernel arguments.
+  // The fraction is kept as its bit pattern: frac is +0 or positive, so the
+  // bits read as a non-negative integer decide interpolation with scalar
+  // integer operations.
   __shared__ int s_lo[SFA_MAX_SLOTS];
-  __shared__ float s_w[SFA_MAX_SLOTS];
+  __shared__ int s_wb[SFA_MAX_SLOTS];
   __shared__ float s_mult[SFA_MAX_SLOTS];
   for (int t = threadIdx.x; t < st.count; t += blockDim.x) {
     s_lo[t] = st.lo[t];
-    s_w[t] = st.frac[t];
+    s_wb[t] = __float_as_int(st.frac[t]);
     s_mult[t] = st.mult[t];
   }
   __syncthreads();
@@ -388,16 +399,18 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
     }
     __syncthreads();
 
+    // K row r - 1 of the slot at lo = 0; a slot's rows are lo rows earlier.
+    const uint32_t* const lane_kv = Ks + (i - r0 - 1) * RW + c * DW;
     for (int s0 = s; s0 < e; s0 += SC) {
       // The chunk's slot entries, read together (one wait for all of them
       // instead of one before each slot's row reads).
-      int lo_c[SC];
-      float w_c[SC], mult_c[SC];
+      int lo_c[SC], wb_c[SC];
+      float mult_c[SC];
 #pragma unroll
       for (int j = 0; j < SC; ++j) {
         const int sc = min(s0 + j, e - 1);
         lo_c[j] = s_lo[sc];
-        w_c[j] = s_w[sc];
+        wb_c[j] = s_wb[sc];
         mult_c[j] = s_mult[sc];
       }
       float sl[SC];
@@ -407,13 +420,14 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
         const int sj = s0 + j;
         if (sj < e) {
           const int lo = __builtin_amdgcn_readfirstlane(lo_c[j]);
-          const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(w_c[j])));
-          const int r = i - lo - r0;
+          const int wbits = __builtin_amdgcn_readfirstlane(wb_c[j]);
+          const uint32_t* const kp = lane_kv - lo * RW;  // K row r - 1
           uint32_t kw[DW];
-          load_words<DW>(Ks + r * RW + c * DW, kw);
-          if (INTERP && w != 0.f) {
+          load_words<DW>(kp + RW, kw);
+          if (INTERP && wbits != 0) {
             uint32_t kb[DW];
-            load_words<DW>(Ks + (r - 1) * RW + c * DW, kb);
+            load_words<DW>(kp, kb);
+            const float w = __int_as_float(wbits);
             const half2_t w2 = {(_Float16)w, (_Float16)w};
 #pragma unroll
             for (int x = 0; x < DW; ++x) kw[x] = lerp_h2(kw[x], kb[x], w2);
@@ -431,9 +445,10 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
           for (int h = 1; h < G; ++h) mine = (own == h) ? part[h] : mine;
           // The nearer row i - lo exists (i >= lo + frac, and below n for a
           // negative offset): mn <= i - lo <= n - 1 with mn = 1 for an
-          // interpolated slot, one unsigned compare.  Queries past n have
+          // interpolated slot (integer arithmetic on the fraction's bits,
+          // so it stays scalar), one unsigned compare.  Queries past n have
           // zero q; their state stays finite and is never stored.
-          const int mn = w != 0.f ? 1 : 0;
+          const int mn = INTERP ? min(wbits, 1) : 0;
           const bool valid = unsigned(i - lo - mn) < unsigned(n - mn);
           sl[j] = valid ? mine : neg_inf();
         }
@@ -463,27 +478,36 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
       for (int j = 0; j < SC; ++j) {
         const int sj = s0 + j;
         if (sj < e) {
-          const int lo = __builtin_amdgcn_readfirstlane(s_lo[sj]);
-          const float w = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_w[sj])));
-          const int r = i - lo - r0;
+          const int lo = __builtin_amdgcn_readfirstlane(lo_c[j]);
+          const int wbits = __builtin_amdgcn_readfirstlane(wb_c[j]);
+          const uint32_t* const kp = lane_kv - lo * RW;  // K row r - 1
           float ph[G];
           Bcast<G, LPQ>::run(p[j], ph);
           uint32_t vw[DW];
-          load_words<DW>(Vs + r * RW + c * DW, vw);
-          if (INTERP && w != 0.f) {
+          load_words<DW>(kp + RW + VOFF, vw);
+          if (INTERP && wbits != 0) {
             uint32_t vb[DW];
-            load_words<DW>(Vs + (r - 1) * RW + c * DW, vb);
+            load_words<DW>(kp + VOFF, vb);
+            const float w = __int_as_float(wbits);
             const half2_t w2 = {(_Float16)w, (_Float16)w};
 #pragma unroll
             for (int x = 0; x < DW; ++x) vw[x] = lerp_h2(vw[x], vb[x], w2);
           }
+          // Each value element is widened to fp32 once and then feeds G
+          // plain fp32 FMAs; the empty asm keeps the widening from being
+          // folded back into G mixed-precision FMAs, which issue at half
+          // the rate.
+          float vf[DC];
+#pragma unroll
+          for (int x = 0; x < DW; ++x) {
+            vf[2 * x] = float(as_h2(vw[x]).x);
+            vf[2 * x + 1] = float(as_h2(vw[x]).y);
+            asm volatile("" : "+v"(vf[2 * x]), "+v"(vf[2 * x + 1]));
+          }
 #pragma unroll
           for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int x = 0; x < DW; ++x) {
-              o[h][2 * x] = fma_lo(ph[h], vw[x], o[h][2 * x]);
-              o[h][2 * x + 1] = fma_hi(ph[h], vw[x], o[h][2 * x + 1]);
-            }
+            for (int x = 0; x < DC; ++x) o[h][x] = fmaf(ph[h], vf[x], o[h][x]);
         }
       }
     }
