@@ -22,12 +22,12 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float -> bfloat16 bits, round to nearest even, NaN kept quiet.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two floats -> packed bfloat16 bits (low half = lo), round to nearest
+// even: one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // ---------------------------------------------------------------- loads
@@ -117,27 +117,26 @@ __device__ __forceinline__ void store_vec(bf16_t* __restrict__ p, const float (&
 #pragma unroll
     for (int x = 0; x < N; x += 8) {
       uint4 t;
-      t.x = f2bf(in[x]) | (f2bf(in[x + 1]) << 16);
-      t.y = f2bf(in[x + 2]) | (f2bf(in[x + 3]) << 16);
-      t.z = f2bf(in[x + 4]) | (f2bf(in[x + 5]) << 16);
-      t.w = f2bf(in[x + 6]) | (f2bf(in[x + 7]) << 16);
+      t.x = pack_bf2(in[x], in[x + 1]);
+      t.y = pack_bf2(in[x + 2], in[x + 3]);
+      t.z = pack_bf2(in[x + 4], in[x + 5]);
+      t.w = pack_bf2(in[x + 6], in[x + 7]);
       *reinterpret_cast<uint4*>(p + x) = t;
     }
   } else if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int x = 0; x < N; x += 4) {
       uint2 t;
-      t.x = f2bf(in[x]) | (f2bf(in[x + 1]) << 16);
-      t.y = f2bf(in[x + 2]) | (f2bf(in[x + 3]) << 16);
+      t.x = pack_bf2(in[x], in[x + 1]);
+      t.y = pack_bf2(in[x + 2], in[x + 3]);
       *reinterpret_cast<uint2*>(p + x) = t;
     }
   } else if constexpr (N % 2 == 0) {
 #pragma unroll
-    for (int x = 0; x < N; x += 2)
-      *reinterpret_cast<uint32_t*>(p + x) = f2bf(in[x]) | (f2bf(in[x + 1]) << 16);
+    for (int x = 0; x < N; x += 2) *reinterpret_cast<uint32_t*>(p + x) = pack_bf2(in[x], in[x + 1]);
   } else {
 #pragma unroll
-    for (int x = 0; x < N; ++x) p[x] = bf16_t(f2bf(in[x]));
+    for (int x = 0; x < N; ++x) p[x] = bf16_t(pack_bf2(in[x], 0.f) & 0xffffu);
   }
 }
 
