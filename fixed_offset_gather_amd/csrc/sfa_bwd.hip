@@ -598,14 +598,22 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
   const float* __restrict__ Dseq = a.Dvec + size_t(seq) * n * G;
   // the prefetch cursor: step (fs, ft) and its slot's min(lo, n) and taps
   int fs = 0, ft = 0, flo = 0, ftaps = 1;
+  // The three loads share the lane's 32-bit byte offset i * G * 4 from
+  // uniform bases (the slot's planes of p and dp, and Dvec), so the address
+  // arithmetic is scalar except for that offset.
   auto load_step = [&](float (&raw)[NR][G]) {
     const int sc = fs < S ? fs : S - 1;
     const int i = min(max(j + flo + ft, 0), n - 1);
-    const size_t widx = (size_t(sc) * n + i) * G;
-    load_vec<G>(Pseq + widx, raw[0]);
+    const unsigned ioff = unsigned(i) * unsigned(G * 4);
+    const float* pb = Pseq + size_t(sc) * n * G;
+    asm volatile("" : "+s"(pb));
+    load_global_at<G>(pb, ioff, raw[0]);
     if constexpr (PART == 0) {
-      load_vec<G>(dPseq + widx, raw[1]);
-      load_vec<G>(Dseq + size_t(i) * G, raw[2]);
+      const float* db = dPseq + size_t(sc) * n * G;
+      const float* vb = Dseq;
+      asm volatile("" : "+s"(db), "+s"(vb));
+      load_global_at<G>(db, ioff, raw[1]);
+      load_global_at<G>(vb, ioff, raw[2]);
     }
   };
   // f16 weight pairs of the cursor's step: dS = scale p (dp - Dvec) for dK,
@@ -661,6 +669,11 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
   // intact, and only the rows above have_hi are staged (consecutive rungs
   // share most of their rows).
   const int kcap = a.kcap;
+  // Byte offset of ring slot tid.  Opaque to the compiler, which would
+  // otherwise fold it back into (tid + soff) * RW * 4 per step, a
+  // quarter-rate integer multiply.
+  unsigned tid_b = unsigned(tid * RW * 4);
+  asm volatile("" : "+v"(tid_b));
   int q0 = 0, have_hi = 0;
   bool first_stage = true;
   int s = 0;
@@ -780,11 +793,15 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
         // row for it.  Masked steps read ring slot 0 with zero weights.
         // Window slots run the same arithmetic with weight 1; their dd sum is
         // never stored.  One straight-line body keeps the registers put.
+        // Ring slot of query j + delta: tid + soff (soff uniform), wrapped
+        // once past kcap; as a byte offset, the lane's tid * RW * 4 plus a
+        // scalar term, minus the ring size where tid >= kcap - soff.
         const bool valid = unsigned(j + delta) < unsigned(n);
-        int slot = j + delta - r0 + base;  // j + delta - r0 in [0, nrows) when valid
-        slot = slot >= kcap ? slot - kcap : slot;
-        const int lrow = valid ? slot : 0;
-        const uint32_t* rowp = Ws + lrow * RW;
+        const int soff = delta - lo0 + base;  // j + delta - r0 = tid + delta - lo0
+        const unsigned wrap = tid >= kcap - soff ? unsigned(kcap * RW * 4) : 0u;
+        const unsigned roff = tid_b + unsigned(soff * RW * 4) - wrap;
+        const uint32_t* rowp = reinterpret_cast<const uint32_t*>(
+            reinterpret_cast<const char*>(Ws) + (valid ? roff : 0u));
         float part = 0.f;
         if constexpr (G == 1) {
           // y = w0 x: acc += (wt w0) x, and y . own = w0 (x . own)

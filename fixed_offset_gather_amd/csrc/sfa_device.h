@@ -84,6 +84,34 @@ __device__ __forceinline__ void load_vec(const bf16_t* __restrict__ p, float (&o
   }
 }
 
+// N consecutive floats at a uniform base plus a 32-bit per-lane byte offset,
+// loaded through the global address space (global_load with an SGPR base).
+// The caller keeps `base` uniform; the empty asm keeps the offset a 32-bit
+// VGPR at the load (see store_global_at).
+template <int N>
+__device__ __forceinline__ void load_global_at(const float* base, unsigned byte_off, float (&out)[N]) {
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(1))) const char gcchar;
+  typedef __attribute__((address_space(1))) const v4f gcv4f;
+  typedef __attribute__((address_space(1))) const v2f gcv2f;
+  typedef __attribute__((address_space(1))) const float gcfloat;
+  asm volatile("" : "+v"(byte_off));
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 4) {
+      const v4f t = *(gcv4f*)((gcchar*)base + byte_off + 16u * (x / 4));
+      out[x] = t.x; out[x + 1] = t.y; out[x + 2] = t.z; out[x + 3] = t.w;
+    }
+  } else if constexpr (N == 2) {
+    const v2f t = *(gcv2f*)((gcchar*)base + byte_off);
+    out[0] = t.x; out[1] = t.y;
+  } else {
+    static_assert(N == 1, "1, 2 or a multiple of 4 floats");
+    out[0] = *(gcfloat*)((gcchar*)base + byte_off);
+  }
+}
+
 // One float at a uniform base plus a 32-bit per-lane byte offset, stored
 // through the global address space (global_store with an SGPR base).
 __device__ __forceinline__ void store_global_at(float* base, unsigned byte_off, float v) {
