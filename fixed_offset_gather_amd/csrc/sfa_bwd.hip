@@ -498,12 +498,12 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
 // gathers yv = sum_h p_h dO_h: dV += w yv, and the value term of dd_k is
 // yv . v_j.  A staged row holds the chunk of every head as f16 with the
 // heads interleaved in pairs (word [hp][x] = (head 2hp, head 2hp+1) of dim
-// x), so each head sum is one v_dot2c_f32_f16 per head pair and dim,
+// x), so each head sum is one v_dot2_f32_f16 per head pair and dim,
 // accumulated in fp32; dS and p enter as f16 pairs.  Half a row per kernel
 // halves the LDS and registers per wave, so four waves share a SIMD.  With
 // one head per KV head (G = 1) a pair would leave half of every f16 word
 // empty, so there the staged words hold the fp32 rows and the weights stay
-// fp32: one FMA per dim and step instead of a v_dot2c doing one useful MAC.
+// fp32: one FMA per dim and step instead of a dot2 doing one useful MAC.
 // SMALL: at most 64 slots (one VGPR per slot-table column).
 template <int D, int G, int PART, bool SMALL>
 __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, SlotTable st) {

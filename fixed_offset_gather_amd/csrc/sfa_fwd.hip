@@ -279,10 +279,11 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
 // bf16 tensors: the same algorithm with f16 operands.  LDS holds K rotated
 // at its true position and V, both as packed f16 (half the footprint of
 // fp32 rows, so more workgroups fit on a CU); the query is rotated, scaled
-// by scale*log2(e) and packed to f16 once.  Logits use v_dot2c_f32_f16 (two
+// by scale*log2(e) and packed to f16 once.  Logits use v_dot2_f32_f16 (two
 // f16 products per instruction, fp32 accumulation), interpolation is packed
-// f16 arithmetic, and the value sum is a mixed-precision FMA into fp32
-// accumulators.  The softmax and the output accumulation stay in fp32.
+// f16 arithmetic, and each value element is widened to fp32 once and feeds
+// fp32 FMAs for all G heads.  The softmax and the output accumulation stay
+// in fp32.
 template <int D, int G, int LPQ, int CAP, bool INTERP>
 __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTable st) {
   constexpr int DC = D / LPQ;  // dims per lane
