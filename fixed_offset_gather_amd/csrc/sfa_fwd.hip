@@ -14,9 +14,11 @@
 // Work split: one workgroup per (sequence, kv head, query block); LPQ lanes
 // per query, each holding DC = D/LPQ dims of all G query heads of the group,
 // so one LDS read of a key/value element feeds G FMAs.  Logits are reduced
-// across the LPQ lanes with DPP; lane c owns the softmax state of head
-// c % G; probabilities and rescale factors are broadcast back with DPP.
-// Online softmax in the log2 domain over chunks of SC slots.
+// across the LPQ lanes with DPP (bf16: a reduce-scatter over the heads,
+// after which each lane owns one head's softmax state; fp32: per-head sums,
+// lane c owning head c % G); probabilities and rescale factors are
+// broadcast back with DPP.  Online softmax in the log2 domain over chunks
+// of SC slots.
 //
 // fwd_edges: attention over per-query edge lists ("Critical power-law
 // sparse attention", item 2): rows are arbitrary, so keys are read straight
@@ -43,7 +45,8 @@ struct FwdArgs {
   float* lse;
   const float* rope;
   int n, hq, hkv, nblk, tiles;
-  float scale_log2;  // scale * log2(e)
+  int tiles_per_blk;  // sequences (batch x kv heads): tiles = nblk * this
+  float scale_log2;   // scale * log2(e)
 };
 
 // Logit of lane's own head for one key chunk; `own` selects head c % G.
@@ -283,15 +286,19 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
 // f16 products per instruction, fp32 accumulation), interpolation is packed
 // f16 arithmetic, and each value element is widened to fp32 once and feeds
 // fp32 FMAs for all G heads.  The softmax and the output accumulation stay
-// in fp32.
-template <int D, int G, int LPQ, int CAP, bool INTERP>
-__global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTable st) {
+// in fp32.  Register j of a lane holds head HeadSlice::head(c, j), so the
+// per-slot logit is a reduce-scatter (each lane ends with its own head's
+// sum) and p is spread back with G - 1 DPP moves; BQH queries per
+// workgroup.
+template <int D, int G, int LPQ, int BQH, int CAP, bool INTERP>
+__global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTable st) {
   constexpr int DC = D / LPQ;  // dims per lane
   constexpr int DW = DC / 2;   // f16 pairs per lane
   constexpr int RW = D / 2 + 4;  // 32-bit words per LDS row (16-byte pad)
   constexpr int CPR = D / 8;     // 16-byte global chunks (8 bf16) per row
-  constexpr int NT = BQ * LPQ;
+  constexpr int NT = BQH * LPQ;
   static_assert(DC >= 2 && DC % 2 == 0, "lane chunk");
+  using HS = HeadSlice<G, LPQ>;
   // K and V rows of a stage in one LDS array, each led by a pad row:
   // [pad][K rows 0..CAP-1][pad][V rows 0..CAP-1].  Row r - 1 of a slot (its
   // interpolation partner, or a pad row when r = 0) is never below the
@@ -306,16 +313,16 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
   const int tid = threadIdx.x;
   const int qq = tid / LPQ;
   const int c = tid % LPQ;
-  const int own = c % G;
+  const int own = HS::own(c);
   const int tile = xcd_tile(blockIdx.x, a.tiles);
   const int seq = tile / a.nblk;
   const int blk = a.nblk - 1 - tile % a.nblk;  // longest blocks first
   const int b = seq / a.hkv, g = seq % a.hkv;
   const int n = a.n;
-  const int i0 = blk * BQ;
+  const int i0 = blk * BQH;
   const int i = i0 + qq;
   const bool active = i < n;
-  const int i_last = min(i0 + BQ, n) - 1;
+  const int i_last = min(i0 + BQH, n) - 1;
 
   // Slot table copied to LDS once: the hot loops read it with uniform
   // addresses instead of scalar loads from the kernel arguments.
@@ -336,12 +343,13 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
   const bf16_t* __restrict__ K = static_cast<const bf16_t*>(a.k);
   const bf16_t* __restrict__ V = static_cast<const bf16_t*>(a.v);
 
+  // Register j of a lane holds head HS::head(c, j) of the group.
   uint32_t qh[G][DW];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float qf[DC];
     if (active) {
-      load_vec<DC>(Q + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, qf);
+      load_vec<DC>(Q + ((size_t(b) * n + i) * a.hq + size_t(g) * G + HS::head(c, h)) * D + c * DC, qf);
       if (a.rope) rotate_pairs<DC, 1>(qf, a.rope + size_t(i) * D, c * DC);
     } else {
 #pragma unroll
@@ -373,12 +381,12 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
       const int le = st.lo[e];
       if (le > i_last) break;
       const int need = max(lomax, le + ((INTERP && st.frac[e] > 0.f) ? 1 : 0));
-      if (need - lo0 + BQ > CAP) break;
+      if (need - lo0 + BQH > CAP) break;
       lomax = need;
       ++e;
     }
     const int r0 = i0 - lomax;
-    const int nrows = lomax - lo0 + BQ;
+    const int nrows = lomax - lo0 + BQH;
 
     __syncthreads();
     for (int t = tid; t < nrows * CPR; t += NT) {
@@ -433,17 +441,17 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
 #pragma unroll
             for (int x = 0; x < DW; ++x) kw[x] = lerp_h2(kw[x], kb[x], w2);
           }
+          // Per-head partial dots, summed over the query's lanes as a
+          // reduce-scatter: each lane ends with its own head's logit.
           float part[G];
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             float acc = 0.f;
 #pragma unroll
             for (int x = 0; x < DW; ++x) acc = dot2_h(qh[h][x], kw[x], acc);
-            part[h] = group_sum<LPQ>(acc);
+            part[h] = acc;
           }
-          float mine = part[0];
-#pragma unroll
-          for (int h = 1; h < G; ++h) mine = (own == h) ? part[h] : mine;
+          const float mine = HS::reduce(part);
           // The nearer row i - lo exists (i >= lo + frac, and below n for a
           // negative offset): mn <= i - lo <= n - 1 with mn = 1 for an
           // interpolated slot (integer arithmetic on the fraction's bits,
@@ -470,7 +478,7 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
       l = l * corr + ps;
       m = mx;
       float ch[G];
-      Bcast<G, LPQ>::run(corr, ch);
+      HS::bcast(corr, ch);
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -483,7 +491,7 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
           const int wbits = __builtin_amdgcn_readfirstlane(wb_c[j]);
           const uint32_t* const kp = lane_kv - lo * RW;  // K row r - 1
           float ph[G];
-          Bcast<G, LPQ>::run(p[j], ph);
+          HS::bcast(p[j], ph);
           uint32_t vw[DW];
           load_words<DW>(kp + RW + VOFF, vw);
           if (INTERP && wbits != 0) {
@@ -516,7 +524,7 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
   }
 
   float lh[G];
-  Bcast<G, LPQ>::run(l, lh);
+  HS::bcast(l, lh);
   if (active) {
     bf16_t* O = static_cast<bf16_t*>(a.o);
 #pragma unroll
@@ -525,9 +533,10 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Slo
       float out[DC];
 #pragma unroll
       for (int x = 0; x < DC; ++x) out[x] = o[h][x] * inv;
-      store_vec<DC>(O + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, out);
+      store_vec<DC>(O + ((size_t(b) * n + i) * a.hq + size_t(g) * G + HS::head(c, h)) * D + c * DC, out);
     }
-    if (a.lse && c < G) a.lse[(size_t(b) * a.hq + size_t(g) * G + c) * n + i] = (m + log2f(l)) * kLn2;
+    if (a.lse && HS::writer(c))
+      a.lse[(size_t(b) * a.hq + size_t(g) * G + own) * n + i] = (m + log2f(l)) * kLn2;
   }
 }
 
@@ -680,13 +689,37 @@ constexpr int fwd_lpq() {
   return G > D / 16 ? G : D / 16;
 }
 
+// f16 kernel: lanes per query and queries per workgroup (256 threads at
+// most, 64 queries at most).  At least two lanes per head: with one lane
+// per head (the whole group reduced by a full permutation of the lanes'
+// registers) the page-1 layer measured slower than plain per-head sums
+// (83.5 against 80.9 us), with two it is faster (77.6 us, 8 lanes of 8 dims
+// at G = 4); at most 16 lanes and at least 2 dims per lane.
+template <int D, int G>
+constexpr int fwd_h16_lpq() {
+  constexpr int want = 2 * G > D / 16 ? 2 * G : D / 16;
+  constexpr int cap = D / 2 < 16 ? D / 2 : 16;
+  return want < cap ? want : cap;
+}
+template <int D, int G>
+constexpr int fwd_h16_bq() {
+  return fwd_h16_lpq<D, G>() >= 8 ? 256 / fwd_h16_lpq<D, G>() : 64;
+}
+
 template <typename T, int D, int G, bool INTERP>
-void launch_fwd_offsets_i(const SlotTable& t, const FwdArgs& a, hipStream_t st) {
-  constexpr int LPQ = fwd_lpq<D, G>();
+void launch_fwd_offsets_i(const SlotTable& t, const FwdArgs& a0, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
-    hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, kCap, INTERP>),
-                       dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+    constexpr int LPQ = fwd_h16_lpq<D, G>();
+    constexpr int BQH = fwd_h16_bq<D, G>();
+    static_assert(BQH + 64 <= kCap, "stage capacity");
+    FwdArgs a = a0;
+    a.nblk = (a.n + BQH - 1) / BQH;
+    a.tiles = a.nblk * a.tiles_per_blk;
+    hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, BQH, kCap, INTERP>),
+                       dim3(a.tiles), dim3(BQH * LPQ), 0, st, a, t);
   } else {
+    constexpr int LPQ = fwd_lpq<D, G>();
+    const FwdArgs& a = a0;
     hipLaunchKernelGGL((fwd_offsets_kernel<T, D, G, LPQ, kCap, INTERP>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a,
                        t);
   }
@@ -752,7 +785,8 @@ int launch_fwd_offsets(const Problem& p, const SlotTable& t, const void* q, cons
   a.hq = p.hq;
   a.hkv = p.hkv;
   a.nblk = (p.n + BQ - 1) / BQ;
-  a.tiles = a.nblk * p.B * p.hkv;
+  a.tiles_per_blk = p.B * p.hkv;
+  a.tiles = a.nblk * a.tiles_per_blk;
   a.scale_log2 = p.scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(stream);
   SFA_DISPATCH(launch_fwd_offsets_t, p, p, t, a, st);
