@@ -51,15 +51,14 @@ def algorithmic_flops(B, n, hq, hkv, D, S, n_interp):
     """FLOPs each kernel must do by definition, per launch: 2 S D per
     query-head for every dot product or weighted sum over the S slots (forward:
     logits and the value sum; query pass: logits, dp and dq; each key-pass
-    half: dK or dV), plus 6 D per (KV head, query, interpolated rung) for the
-    row interpolation."""
+    pass: dK and dV), plus 6 D per (KV head, query, interpolated rung) for the
+    row interpolation (the key pass interpolates both its gathers)."""
     qh = B * n * hq
     lerp = 6 * D * n_interp * B * n * hkv
     return {
         "fwd_offsets": 4 * S * D * qh + lerp,
         "bwd_query": 6 * S * D * qh + lerp,
-        "bwd_key_dk": 2 * S * D * qh + lerp,
-        "bwd_key_dv": 2 * S * D * qh + lerp,
+        "bwd_key": 4 * S * D * qh + 2 * lerp,
         "bwd_reduce": 0,
     }
 
@@ -74,11 +73,8 @@ def algorithmic_bytes(B, n, hq, hkv, D, esize):
         "fwd_offsets": q + 2 * kv + q + lse,
         # read Q, K, V, dO, LSE; write dQ
         "bwd_query": q + 2 * kv + q + lse + q,
-        # read Q, dO, K, V; write dK, dV (bf16: the dK kernel reads Q and K
-        # and writes dK, the dV kernel reads dO and V and writes dV)
+        # read Q, dO, K, V; write dK, dV
         "bwd_key": 2 * q + 2 * kv + 2 * kv,
-        "bwd_key_dk": q + kv + kv,
-        "bwd_key_dv": q + kv + kv,
         "bwd_reduce": 0,
         # the step: forward + backward, each tensor once per pass
         "step": (q + 2 * kv + q + lse) + (q + 2 * kv + q + lse + q + 2 * kv),
@@ -296,7 +292,7 @@ def main():
     torch.cuda.synchronize()
     sfa.profile_enable(False)
     kern = {}
-    for name in ("fwd_offsets", "bwd_query", "bwd_key_dk", "bwd_key_dv", "bwd_reduce"):
+    for name in ("fwd_offsets", "bwd_query", "bwd_key", "bwd_reduce"):
         ms, cnt = sfa.profile_read(name)
         if cnt:
             kern[name] = {"avg_us": 1e3 * ms / cnt, "launches": cnt}
@@ -481,7 +477,7 @@ def main():
         torch.cuda.synchronize()
         sfa.profile_enable(False)
         ck = {}
-        for name in ("fwd_offsets", "bwd_query", "bwd_key_dk", "bwd_key_dv"):
+        for name in ("fwd_offsets", "bwd_query", "bwd_key"):
             ms_, c_ = sfa.profile_read(name)
             if c_:
                 ck[name] = round(1e3 * ms_ / c_, 3)

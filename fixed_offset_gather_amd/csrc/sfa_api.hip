@@ -336,8 +336,7 @@ extern "C" int sfa_bwd(const sfa_attn* a, const void* q, const void* k, const vo
     if (rc) return rc;
   }
   {
-    // bf16: the launcher records its two kernels as bwd_key_dk / bwd_key_dv
-    ProfileScope ps(p.dtype == SFA_BF16 ? nullptr : "bwd_key", stream);
+    ProfileScope ps("bwd_key", stream);
     rc = hip_status(launch_bwd_key(p, t, q, k, v, dout, dk, dv, ws, dd || dtheta, stream), "sfa_bwd key launch");
     if (rc) return rc;
   }

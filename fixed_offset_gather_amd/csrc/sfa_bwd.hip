@@ -19,9 +19,9 @@
 //   form contiguous ranges, so each lane gathers instead of scattering.
 //   fp32: one kernel; dK uses the relative rotation R(j)^T R(i) = R(i-j)
 //   with i-j fixed per (slot, tap), so unrotated Q rows are combined first
-//   and rotated once.  bf16: two kernels (dK, dV), each staging half a query
-//   row into an LDS ring of rows that consecutive stages share.  Both also
-//   sum the per-block partials of dL/dd_k.
+//   and rotated once.  bf16: one launch of dK and dV workgroups, each
+//   staging half a query row into an LDS ring of rows that consecutive
+//   stages share.  Both also sum the per-block partials of dL/dd_k.
 // bwd_reduce: sums the dd partials in block order; dalpha = sum f_k dd_k;
 //   dtheta = (alpha - 1/2)(3/2 - alpha) dalpha.
 // The edge-list backward (bwd_edges_query, bwd_edges_key, further below)
@@ -489,8 +489,9 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
   }
 }
 
-// bf16 tensors: the key pass with f16 operands, split into two kernels that
-// each stage half of a query row.  PART 0 (dK) stages q~ = R(i) q of the
+// bf16 tensors: the key pass with f16 operands, split into two halves that
+// each stage half of a query row (one launch, bwd_key_h16_kernel below, runs
+// both).  PART 0 (dK) stages q~ = R(i) q of the
 // chunk (rotated while staging) and gathers yk~ = sum_h dS_h q~_h; dK~ =
 // sum w yk~ is rotated back once, dK = R(j)^T dK~, and the key term of dd_k
 // is yk~ . k~_j with k~_j = R(j) k_j (the relative rotation R(i - j) =
@@ -499,14 +500,15 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
 // yv . v_j.  A staged row holds the chunk of every head as f16 with the
 // heads interleaved in pairs (word [hp][x] = (head 2hp, head 2hp+1) of dim
 // x), so each head sum is one v_dot2_f32_f16 per head pair and dim,
-// accumulated in fp32; dS and p enter as f16 pairs.  Half a row per kernel
-// halves the LDS and registers per wave, so four waves share a SIMD.  With
+// accumulated in fp32; dS and p enter as f16 pairs.  Half a row per
+// workgroup halves the LDS and registers per wave, so four waves share a
+// SIMD.  With
 // one head per KV head (G = 1) a pair would leave half of every f16 word
 // empty, so there the staged words hold the fp32 rows and the weights stay
 // fp32: one FMA per dim and step instead of a dot2 doing one useful MAC.
 // SMALL: at most 64 slots (one VGPR per slot-table column).
 template <int D, int G, int PART, bool SMALL>
-__global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, SlotTable st) {
+__device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable& st, const int tile) {
   constexpr int KB = kKeyBlockH16;
   constexpr int KC = key_chunk(D);
   constexpr int NCH = D / KC;
@@ -524,7 +526,6 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
 
   const int tid = threadIdx.x;
   const int wave = tid / 64;
-  const int tile = xcd_tile(blockIdx.x, a.tiles);
   const int c = tile % NCH;
   const int rest = tile / NCH;
   const int seq = rest / a.nblk;
@@ -864,6 +865,19 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_half_kernel(BwdArgs a, S
   }
 }
 
+// Both halves in one launch: tiles [0, T) are dK tiles and [T, 2T) dV
+// tiles, dispatched in that order, so dV workgroups start on the CUs that
+// dK workgroups leave instead of waiting for the slowest of them (page-1 key
+// pass 146 -> 137 us, Christoffel 298 -> 266 us against two launches).
+template <int D, int G, bool SMALL>
+__global__ __launch_bounds__(kKeyBlockH16) void bwd_key_h16_kernel(BwdArgs a, SlotTable st) {
+  const int t2 = xcd_tile(blockIdx.x, 2 * a.tiles);
+  if (t2 < a.tiles)
+    key_half_body<D, G, 0, SMALL>(a, st, t2);
+  else
+    key_half_body<D, G, 1, SMALL>(a, st, t2 - a.tiles);
+}
+
 struct ReduceArgs {
   const float* dd_part;
   float* dd;
@@ -984,20 +998,10 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
     a.kcap = key_half_cap(G, D, t.n_rungs);
     const size_t lds = (size_t(a.kcap) * key_half_row_words(G, D) + size_t(KB / 64) * t.n_rungs) * 4;
     const bool small = t.count <= 64;
-    {
-      ProfileScope ps("bwd_key_dk", st);
-      if (small)
-        hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 0, true>), dim3(a.tiles), dim3(KB), lds, st, a, t);
-      else
-        hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 0, false>), dim3(a.tiles), dim3(KB), lds, st, a, t);
-    }
-    {
-      ProfileScope ps("bwd_key_dv", st);
-      if (small)
-        hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 1, true>), dim3(a.tiles), dim3(KB), lds, st, a, t);
-      else
-        hipLaunchKernelGGL((bwd_key_half_kernel<D, G, 1, false>), dim3(a.tiles), dim3(KB), lds, st, a, t);
-    }
+    if (small)
+      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, true>), dim3(2 * a.tiles), dim3(KB), lds, st, a, t);
+    else
+      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, false>), dim3(2 * a.tiles), dim3(KB), lds, st, a, t);
   } else {
     constexpr int KB = key_block(sizeof(T), G, D);
     a.nblk = (a.n + KB - 1) / KB;

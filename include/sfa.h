@@ -314,9 +314,7 @@ int sfa_bwd_edges(const sfa_attn* a, const int32_t* edges, const int32_t* count,
  * on its launch stream.  sfa_profile_read synchronises the recorded events
  * and returns the accumulated milliseconds and launch count of the named
  * kernel ("fwd_offsets", "fwd_edges", "bwd_query", "bwd_key",
- * "bwd_edges_query", "bwd_edges_key",
- * "bwd_reduce"; with bf16 tensors the key pass is the two kernels
- * "bwd_key_dk" and "bwd_key_dv" instead of "bwd_key");
+ * "bwd_edges_query", "bwd_edges_key", "bwd_reduce");
  * sfa_profile_reset drops all records.  sfa_profile_select(name) restricts
  * the recording to the launches of the named kernel (each recorded launch
  * adds two event packets to its stream, which also delay the stream's next
