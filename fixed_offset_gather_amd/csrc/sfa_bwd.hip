@@ -35,6 +35,9 @@ namespace {
 
 constexpr int kCap = 128;
 
+// Dims per key-pass tile (and per chunk of a packed key-pass row).
+constexpr int key_chunk(int D) { return D >= 16 ? 16 : D; }
+
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -48,6 +51,8 @@ struct BwdArgs {
   float* dP;
   float* Dvec;
   float* dd_part;
+  uint32_t* xq;  // packed key-pass rows (see BwdWorkspace), or null
+  uint32_t* xd;
   const float* rope;
   int n, hq, hkv, nblk, tiles, S, n_rungs;
   int kcap;     // bwd_key: rows one stage may hold (dynamic LDS)
@@ -223,8 +228,8 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
       dvec += pdp;
       if (active && HS::writer(c)) {  // p = 0 where the slot has no row for query i
         // The slot's plane bases stay scalar (global_store with an SGPR
-        // base and the lane's 32-bit offset); the empty asm keeps them from
-        // being folded into per-lane 64-bit pointers.
+        // base and the lane's 32-bit offset) instead of being folded into
+        // per-lane 64-bit pointers.
         const size_t plane = (ws_seq + sj) * size_t(n) * G;
         float* pb = a.P + plane;
         float* db = a.dP + plane;
@@ -244,6 +249,41 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
         }
     }
     s = e;
+  }
+
+  // bf16 with G >= 2: this query's rows for the key pass, q~ = R(i) q and
+  // dO as f16 head pairs in the key pass's LDS row layout, written once
+  // here so that the key pass copies them instead of converting (and for q
+  // rotating) them again in every stage that holds the row.  A lane's
+  // registers are in HeadSlice order, so each pair picks its two heads.
+  if constexpr (sizeof(T) == 2 && G >= 2) {
+    if (active && a.xq) {
+      constexpr int KC = key_chunk(D);
+      constexpr int GW = G / 2;
+      static_assert(KC % DC == 0, "a lane's dims lie in one chunk");
+      const int ch = (c * DC) / KC, x0 = (c * DC) % KC;
+      const size_t wrow = ((size_t(seq) * n + i) * (D / KC) + ch) * (GW * KC) + x0;
+#pragma unroll
+      for (int hp = 0; hp < GW; ++hp) {
+        uint32_t wq[DC], wd[DC];
+#pragma unroll
+        for (int x = 0; x < DC; ++x) {
+          float q0 = 0.f, q1 = 0.f, d0 = 0.f, d1 = 0.f;
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            const int h = HS::head(c, j);
+            q0 = h == 2 * hp ? qv[j][x] : q0;
+            q1 = h == 2 * hp + 1 ? qv[j][x] : q1;
+            d0 = h == 2 * hp ? dov[j][x] : d0;
+            d1 = h == 2 * hp + 1 ? dov[j][x] : d1;
+          }
+          wq[x] = pack_h2(q0, q1);
+          wd[x] = pack_h2(d0, d1);
+        }
+        store_words<DC>(a.xq + wrow + hp * KC, wq);
+        store_words<DC>(a.xd + wrow + hp * KC, wd);
+      }
+    }
   }
 
   if (active && HS::writer(c)) a.Dvec[(size_t(seq) * n + i) * G + own] = dvec;
@@ -276,7 +316,6 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
 // elements of the chunk for all G heads, so each row read from L2 serves
 // every (slot, tap) of the stage.  p, dp and Dvec of the next (slot, tap)
 // are loaded one step ahead.
-constexpr int key_chunk(int D) { return D >= 16 ? 16 : D; }
 
 // Keys per workgroup: 128 (two waves) when a staged row (Q and dO of the
 // chunk for all heads) is at most 256 bytes, else 64; a stage holds the
@@ -606,13 +645,11 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
     const int sc = fs < S ? fs : S - 1;
     const int i = min(max(j + flo + ft, 0), n - 1);
     const unsigned ioff = unsigned(i) * unsigned(G * 4);
-    const float* pb = Pseq + size_t(sc) * n * G;
-    asm volatile("" : "+s"(pb));
+    const float* pb = uniform_ptr(Pseq + size_t(sc) * n * G);
     load_global_at<G>(pb, ioff, raw[0]);
     if constexpr (PART == 0) {
-      const float* db = dPseq + size_t(sc) * n * G;
-      const float* vb = Dseq;
-      asm volatile("" : "+s"(db), "+s"(vb));
+      const float* db = uniform_ptr(dPseq + size_t(sc) * n * G);
+      const float* vb = uniform_ptr(Dseq);
       load_global_at<G>(db, ioff, raw[1]);
       load_global_at<G>(vb, ioff, raw[2]);
     }
@@ -704,10 +741,50 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
     __syncthreads();
 
     // Thread t always stages piece t % PPR of a row, rows t / PPR,
-    // t / PPR + KB / PPR, ...  Batches of SB pieces: all their global loads
-    // are issued before the first conversion.  dK rows are rotated by their
-    // own position, R(i) q, on the way.
-    {
+    // t / PPR + KB / PPR, ...  With G >= 2 the query pass has written the
+    // rows already in this layout (f16 head pairs, q rotated by its own
+    // position), so a piece is a copy of 8 words.
+    if constexpr (G >= 2) {
+      constexpr int SB = 4;
+      constexpr int RSTEP = KB / PPR;
+      const int pc = tid % PPR;
+      const int hp = pc / XH;
+      const int xh = pc % XH;
+      const uint32_t* __restrict__ XP = PART == 0 ? a.xq : a.xd;
+      const int rn = j0 + fnew;  // query of the first new row
+      // word offset of piece (hp, xh) of chunk c within a packed row
+      const uint32_t* src0 = XP + size_t(seq) * n * (D * GW) + (c * GW + hp) * KC + xh * 8;
+      uint32_t* dst0 = Ws + hp * KC + xh * 8;
+      for (int row0 = tid / PPR; row0 < nnew; row0 += SB * RSTEP) {
+        uint4 u0[SB], u1[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const int row = row0 + u * RSTEP;
+          u0[u] = u1[u] = make_uint4(0, 0, 0, 0);
+          // rows before the sequence (negative offsets) are staged as zeros;
+          // masked steps read ring slot 0 with zero weights
+          if (row < nnew && rn + row >= 0) {
+            const uint32_t* src = src0 + int64_t(rn + row) * (D * GW);
+            u0[u] = *reinterpret_cast<const uint4*>(src);
+            u1[u] = *reinterpret_cast<const uint4*>(src + 4);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+          const int row = row0 + u * RSTEP;
+          if (row < nnew) {
+            int slot = fnew - lo0 + row + base;  // < 2 kcap
+            slot = slot >= kcap ? slot - kcap : slot;
+            uint32_t* dst = dst0 + slot * RW;
+            *reinterpret_cast<uint4*>(dst) = u0[u];
+            *reinterpret_cast<uint4*>(dst + 4) = u1[u];
+          }
+        }
+      }
+    } else {
+      // G = 1: fp32 words, converted here; dK rows are rotated by their own
+      // position, R(i) q, on the way.  Batches of SB pieces: all their
+      // global loads are issued before the first conversion.
       constexpr int SB = PART == 0 ? 2 : 4;  // dK also holds rotary rows
       constexpr int RSTEP = KB / PPR;
       const int pc = tid % PPR;
@@ -964,6 +1041,8 @@ BwdArgs make_args(const Problem& p, const SlotTable& t, const BwdWorkspace& ws) 
   a.dP = ws.dp;
   a.Dvec = ws.dvec;
   a.dd_part = ws.dd_part;
+  a.xq = ws.xq;
+  a.xd = ws.xd;
   a.rope = p.rope;
   a.n = p.n;
   a.hq = p.hq;
@@ -1279,13 +1358,17 @@ size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, Bw
   const bool h16 = p.dtype == SFA_BF16;
   const int kb = h16 ? kKeyBlockH16 : key_block(4, p.G, p.D);
   ws->blocks = ((p.n + kb - 1) / kb) * p.B * p.hkv * (p.D / key_chunk(p.D)) * (h16 ? 2 : 1);
-  const size_t dd_e = size_t(ws->blocks) * (t.n_rungs > 0 ? t.n_rungs : 1);
+  const size_t dd_e = al(size_t(ws->blocks) * (t.n_rungs > 0 ? t.n_rungs : 1));
+  // packed key-pass rows (bf16, G >= 2): D * G / 2 words per (sequence, row)
+  const size_t xe = (h16 && p.G >= 2) ? al(size_t(p.B) * p.hkv * size_t(p.n) * p.D * (p.G / 2)) : 0;
   float* f = static_cast<float*>(base);
   ws->p = f;
   ws->dp = f ? f + pe : nullptr;
   ws->dvec = f ? f + 2 * pe : nullptr;
   ws->dd_part = f ? f + 2 * pe + de : nullptr;
-  ws->bytes = (2 * pe + de + dd_e) * sizeof(float);
+  ws->xq = (f && xe) ? reinterpret_cast<uint32_t*>(f + 2 * pe + de + dd_e) : nullptr;
+  ws->xd = (f && xe) ? reinterpret_cast<uint32_t*>(f + 2 * pe + de + dd_e + xe) : nullptr;
+  ws->bytes = (2 * pe + de + dd_e + 2 * xe) * sizeof(float);
   return ws->bytes;
 }
 

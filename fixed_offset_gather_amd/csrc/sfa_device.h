@@ -112,6 +112,17 @@ __device__ __forceinline__ void load_global_at(const float* base, unsigned byte_
   }
 }
 
+// A pointer that is the same in every lane, held in SGPRs (both halves read
+// from the first lane), so it can serve as the scalar base of a global
+// load or store.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<P*>((uint64_t(hi) << 32) | lo);
+}
+
 // One float at a uniform base plus a 32-bit per-lane byte offset, stored
 // through the global address space (global_store with an SGPR base).
 __device__ __forceinline__ void store_global_at(float* base, unsigned byte_off, float v) {
@@ -194,6 +205,21 @@ __device__ __forceinline__ uint32_t lerp_h2(uint32_t a, uint32_t b, half2_t w) {
 // fp32 c + p * (f16 element): one mixed-precision FMA, no unpacking.
 __device__ __forceinline__ float fma_lo(float p, uint32_t w, float c) { return fmaf(p, (float)as_h2(w).x, c); }
 __device__ __forceinline__ float fma_hi(float p, uint32_t w, float c) { return fmaf(p, (float)as_h2(w).y, c); }
+
+// N 32-bit words to p (N * 4 bytes, aligned to the widest vector used).
+template <int N>
+__device__ __forceinline__ void store_words(uint32_t* __restrict__ p, const uint32_t (&w)[N]) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 4) *reinterpret_cast<uint4*>(p + x) = make_uint4(w[x], w[x + 1], w[x + 2], w[x + 3]);
+  } else if constexpr (N % 2 == 0) {
+#pragma unroll
+    for (int x = 0; x < N; x += 2) *reinterpret_cast<uint2*>(p + x) = make_uint2(w[x], w[x + 1]);
+  } else {
+#pragma unroll
+    for (int x = 0; x < N; ++x) p[x] = w[x];
+  }
+}
 
 template <int N>
 __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint32_t (&out)[N]) {

@@ -52,6 +52,12 @@ struct BwdWorkspace {
   float* dp;       // [B][Hkv][S][n][G] dO . v~
   float* dvec;     // [B][Hkv][n][G] rowsum(dO * O) = sum_slots p dp
   float* dd_part;  // [n_rungs][blocks] per-block partial sums of dL/dd_k
+  // bf16 with G >= 2: the query pass's rows for the key pass, as f16 head
+  // pairs in the key pass's LDS row layout, [B][Hkv][n][D/16][G/2][16] words
+  // (word = heads (2hp, 2hp+1) of one dim): q rotated by its own position,
+  // and dO.  Null otherwise (the key pass then stages from q and dO).
+  uint32_t* xq;
+  uint32_t* xd;
   size_t bytes;
   int blocks;
 };

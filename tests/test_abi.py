@@ -173,9 +173,12 @@ def test_bwd_validation_and_workspace_size():
     pe = al(2 * 2 * S * 100 * 4)          # p and dp: [B][Hkv][S][n][G]
     de = al(2 * 2 * 100 * 4)              # Dvec: [B][Hkv][n][G]
     # dd partials: one per key-pass tile (128-key blocks x B x Hkv x 16-dim
-    # chunks) from each of the bf16 dK and dV kernels
+    # chunks) from each of the bf16 dK and dV halves
     blocks = 1 * 2 * 2 * 4 * 2
-    assert nb == (2 * pe + de + blocks * 15) * 4
+    dd = al(blocks * 15)
+    # packed key-pass rows of q and dO (bf16, G >= 2): D * G / 2 words per row
+    xe = al(2 * 2 * 100 * 64 * 2)
+    assert nb == (2 * pe + de + dd + 2 * xe) * 4
     assert lib.sfa_bwd_workspace_bytes(ctypes.byref(_prob(head_dim=48))) == 0
     base = sfa.base_fib()
     bp = base.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
