@@ -254,8 +254,11 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
   // bf16 with G >= 2: this query's rows for the key pass, q~ = R(i) q and
   // dO as f16 head pairs in the key pass's LDS row layout, written once
   // here so that the key pass copies them instead of converting (and for q
-  // rotating) them again in every stage that holds the row.  A lane's
-  // registers are in HeadSlice order, so each pair picks its two heads.
+  // rotating) them again in every stage that holds the row.  Register j of
+  // lane c holds head own(c) ^ head(0, j), and registers 2m, 2m + 1 hold
+  // the two heads of one pair: pack in register order, pick the lane's
+  // register pair for each head pair, swap the halves where the even
+  // register holds the odd head (v_perm with a per-lane selector).
   if constexpr (sizeof(T) == 2 && G >= 2) {
     if (active && a.xq) {
       constexpr int KC = key_chunk(D);
@@ -263,29 +266,44 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
       static_assert(KC % DC == 0, "a lane's dims lie in one chunk");
       const int ch = (c * DC) / KC, x0 = (c * DC) % KC;
       const size_t wrow = ((size_t(seq) * n + i) * (D / KC) + ch) * (GW * KC) + x0;
+      uint32_t pq[GW][DC], pd[GW][DC];
+#pragma unroll
+      for (int m = 0; m < GW; ++m)
+#pragma unroll
+        for (int x = 0; x < DC; ++x) {
+          pq[m][x] = pack_h2(qv[2 * m][x], qv[2 * m + 1][x]);
+          pd[m][x] = pack_h2(dov[2 * m][x], dov[2 * m + 1][x]);
+        }
 #pragma unroll
       for (int hp = 0; hp < GW; ++hp) {
+        // the register pair holding head pair hp, and whether its even
+        // register holds the odd head
+        int msel = 0;
+        bool swap = false;
+#pragma unroll
+        for (int m = 0; m < GW; ++m) {
+          const int h = HS::head(c, 2 * m);
+          msel = (h >> 1) == hp ? m : msel;
+          swap = (h >> 1) == hp ? (h & 1) != 0 : swap;
+        }
+        const uint32_t sel = swap ? 0x01000302u : 0x03020100u;  // halves swapped or kept
         uint32_t wq[DC], wd[DC];
 #pragma unroll
         for (int x = 0; x < DC; ++x) {
-          float q0 = 0.f, q1 = 0.f, d0 = 0.f, d1 = 0.f;
+          uint32_t q_ = pq[0][x], d_ = pd[0][x];
 #pragma unroll
-          for (int j = 0; j < G; ++j) {
-            const int h = HS::head(c, j);
-            q0 = h == 2 * hp ? qv[j][x] : q0;
-            q1 = h == 2 * hp + 1 ? qv[j][x] : q1;
-            d0 = h == 2 * hp ? dov[j][x] : d0;
-            d1 = h == 2 * hp + 1 ? dov[j][x] : d1;
+          for (int m = 1; m < GW; ++m) {
+            q_ = msel == m ? pq[m][x] : q_;
+            d_ = msel == m ? pd[m][x] : d_;
           }
-          wq[x] = pack_h2(q0, q1);
-          wd[x] = pack_h2(d0, d1);
+          wq[x] = __builtin_amdgcn_perm(q_, q_, sel);
+          wd[x] = __builtin_amdgcn_perm(d_, d_, sel);
         }
         store_words<DC>(a.xq + wrow + hp * KC, wq);
         store_words<DC>(a.xd + wrow + hp * KC, wd);
       }
     }
   }
-
   if (active && HS::writer(c)) a.Dvec[(size_t(seq) * n + i) * G + own] = dvec;
   float dvh[G];
   HS::bcast(dvec, dvh);
