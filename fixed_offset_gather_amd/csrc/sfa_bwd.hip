@@ -593,6 +593,7 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   const int j = j0 + tid;
   const bool activej = j < n;
   const bool rope = PART == 0 && a.rope != nullptr;
+  const bool want_dd = a.need_dd != 0;  // dd partials are requested
 
   for (int t = tid; t < NW * a.n_rungs; t += KB) ddl[t] = 0.f;
 
@@ -905,14 +906,14 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
           load_words<KC>(rowp, xw);
           const float w0 = __uint_as_float(wts[0]);
           const float ww = wt * w0;
-          float xo = 0.f;
 #pragma unroll
-          for (int x = 0; x < KC; ++x) {
-            const float xf = __uint_as_float(xw[x]);
-            acc[x] = fmaf(ww, xf, acc[x]);
-            xo = fmaf(xf, own[x], xo);
+          for (int x = 0; x < KC; ++x) acc[x] = fmaf(ww, __uint_as_float(xw[x]), acc[x]);
+          if (want_dd) {  // uniform: the dd dot product only when dd is requested
+            float xo = 0.f;
+#pragma unroll
+            for (int x = 0; x < KC; ++x) xo = fmaf(__uint_as_float(xw[x]), own[x], xo);
+            part = w0 * xo;
           }
-          part = w0 * xo;
         } else {
           float y[KC];
           uint32_t xw[KC];
@@ -926,9 +927,10 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
             for (int x = 0; x < KC; ++x) y[x] = dot2_h(wts[hp], xw[x], y[x]);
           }
 #pragma unroll
-          for (int x = 0; x < KC; ++x) {
-            acc[x] = fmaf(wt, y[x], acc[x]);
-            part = fmaf(y[x], own[x], part);
+          for (int x = 0; x < KC; ++x) acc[x] = fmaf(wt, y[x], acc[x]);
+          if (want_dd) {
+#pragma unroll
+            for (int x = 0; x < KC; ++x) part = fmaf(y[x], own[x], part);
           }
         }
         ddacc += tap ? part : -part;
