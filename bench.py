@@ -144,6 +144,28 @@ def calibration_copy():
     del a, b
 
 
+def copy_bandwidth_gbs(reps=5):
+    """The box's plain device-to-device copy rate (1 GiB read and 1 GiB
+    written per copy, best of `reps`), outside any timed region: the HBM
+    rate a streaming kernel can reach here, beside the 8 TB/s peak."""
+    import torch
+    a = torch.empty(512 * 1024 * 1024, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    nbytes = 2 * a.numel() * a.element_size()
+    del a, b
+    return round(nbytes / best / 1e9, 1)
+
+
 def cpu_baseline(w, alpha, seqs):
     """The fp64 oracle on `seqs` sequences of the same step, one thread."""
     from threadpoolctl import threadpool_limits
@@ -556,6 +578,7 @@ def main():
         },
         "step_algorithmic_GBs": round(step_gbs, 1),
         "step_frac_of_hbm_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+        "hbm_copy_GBs": copy_bandwidth_gbs(),
         "kernels_avg_us": {k_: round(v_["avg_us"], 3) for k_, v_ in kern.items()},
         "roofline": roofline,
         "fwd_only": fwd_only,
