@@ -603,22 +603,22 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
   float m = neg_inf(), l = 0.f;
 
   for (int t0 = 0; t0 < cmax; t0 += ESC) {
+    // Branch-free over the lanes' different lists: an entry past the
+    // query's count or a padding entry reads row 0 (row 0 exists) and is
+    // masked by its logit, so p = 0 for it.  The list index is clamped to
+    // the width: the chunk can run past it when the width is not a
+    // multiple of ESC.
     float sl[ESC];
     int jj[ESC];
 #pragma unroll
     for (int j = 0; j < ESC; ++j) {
       const int t = t0 + j;
-      int key = (t < cnt) ? erow[t] : -1;
-      const bool valid = key >= 0 && key < n;
-      jj[j] = valid ? key : -1;
+      const int key = erow[min(t, a.width - 1)];
+      const bool valid = t < cnt && key >= 0 && key < n;
+      jj[j] = valid ? key : 0;
       float kt[DC];
-      if (valid) {
-        load_vec<DC>(Kseq + size_t(key) * kv_row, kt);
-        if (a.rope) rotate_pairs<DC, 1>(kt, a.rope + size_t(key) * D, c * DC);
-      } else {
-#pragma unroll
-        for (int x = 0; x < DC; ++x) kt[x] = 0.f;
-      }
+      load_vec<DC>(Kseq + size_t(jj[j]) * kv_row, kt);
+      if (a.rope) rotate_pairs<DC, 1>(kt, a.rope + size_t(jj[j]) * D, c * DC);
       const float mine = own_logit<G, LPQ, DC>(qv, kt, own);
       sl[j] = valid ? mine * a.scale_log2 : neg_inf();
     }
@@ -645,12 +645,7 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
 #pragma unroll
     for (int j = 0; j < ESC; ++j) {
       float vt[DC];
-      if (jj[j] >= 0) {
-        load_vec<DC>(Vseq + size_t(jj[j]) * kv_row, vt);
-      } else {
-#pragma unroll
-        for (int x = 0; x < DC; ++x) vt[x] = 0.f;
-      }
+      load_vec<DC>(Vseq + size_t(jj[j]) * kv_row, vt);  // p[j] = 0 for a masked entry
       float ph[G];
       Bcast<G, LPQ>::run(p[j], ph);
 #pragma unroll

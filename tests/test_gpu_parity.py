@@ -444,6 +444,28 @@ def test_edge_backward_multi_tile_ragged(dtype, hq, hkv, D, theta):
     _edge_bwd_check(case, edges, count, tol=TOL[dtype] if dtype == "bf16" else 2e-5)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("width,radius,draws", [(13, 2, 6), (7, 1, 3)])
+def test_edge_lists_width_not_a_multiple_of_the_chunk(dtype, width, radius, draws):
+    # The forward reads its lists in chunks of 4 entries; a width that is not
+    # a multiple of 4 ends the last chunk past the list (the index is clamped
+    # there) and the last query's list ends the buffer.
+    sfa = _sfa()
+    case = Case(2, 150, 8, 2, 64, dtype, seed=29, rope_theta=1e4)
+    edges, count = sfa.edges_powerlaw(150, radius, 0.8, draws, width, 5)
+    assert edges.shape == (150, width) and int(count.max()) <= width
+    o = sfa.fwd_edges(case.qd, case.kd, case.vd, torch.from_numpy(edges).to(DEV),
+                      torch.from_numpy(count).to(DEV), rope=case.rope)
+    torch.cuda.synchronize()
+    q, k, v, _ = case.f64()
+    ro, _ = ref.forward_edges(q, k, v, edges, count, 1e4)
+    if dtype == "bf16":
+        assert _excess(_np(o), ro, "bf16") <= 1e-2
+    else:
+        assert _maxerr(_np(o), ro) <= 1e-5
+    _edge_bwd_check(case, edges, count, tol=TOL[dtype] if dtype == "bf16" else 2e-5)
+
+
 def test_edge_backward_ctx2048_powerlaw_full_size_and_deterministic():
     sfa = _sfa()
     w = si.WORKLOADS["ctx2048_powerlaw"]
