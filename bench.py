@@ -578,7 +578,8 @@ def main():
         },
         "step_algorithmic_GBs": round(step_gbs, 1),
         "step_frac_of_hbm_peak": round(step_gbs / HBM_PEAK_GBS, 4),
-        "hbm_copy_GBs": copy_bandwidth_gbs(),
+        # (not in counter runs: its copies would join the calibration copy's)
+        "hbm_copy_GBs": None if args.calibrate_copy else copy_bandwidth_gbs(),
         "kernels_avg_us": {k_: round(v_["avg_us"], 3) for k_, v_ in kern.items()},
         "roofline": roofline,
         "fwd_only": fwd_only,
