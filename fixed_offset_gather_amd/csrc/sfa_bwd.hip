@@ -343,9 +343,9 @@ constexpr int key_block(int esize, int G, int D) {
 }
 constexpr int key_cap(int kb) { return kb + 48; }
 
-// bf16 key pass: two kernels of 128 keys per workgroup, one for dK (staging
-// Q) and one for dV (staging dO).  Words per staged row: the chunk of every
-// head as f16 head pairs, plus a 4-word pad against bank conflicts.
+// bf16 key pass: workgroups of 128 keys of two kinds in one launch, dK
+// (staging q~) and dV (staging dO).  Words per staged row: the chunk of
+// every head as f16 head pairs, plus a 4-word pad against bank conflicts.
 constexpr int kKeyBlockH16 = 128;
 constexpr int key_half_row_words(int G, int D) { return key_chunk(D) * ((G + 1) / 2) + 4; }
 
