@@ -154,6 +154,16 @@ def test_forward_multi_tile_ragged(dtype, hq, hkv, D, W, alpha):
     _fwd_check(case, W, lo, frac)
 
 
+@pytest.mark.parametrize("hq,hkv,D", [(4, 2, 64), (16, 2, 64), (8, 2, 32), (8, 1, 32)])
+def test_backward_packed_key_rows_group_shapes(hq, hkv, D):
+    # bf16 with two or more heads per KV head: the query pass writes the key
+    # pass's rows packed as f16 head pairs (8, 4 and 2 dims per lane, 1 to 4
+    # head pairs), which the key pass stages by copying
+    case = Case(2, 150, hq, hkv, D, "bf16", seed=37, rope_theta=1e4)
+    lo, frac = _sfa().offsets_fib(0.83)
+    _bwd_check(case, 6, lo, frac, 0.83, _sfa().base_fib(), tol=TOL["bf16"], grad_tol=1e-2)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("hq,hkv,D", [(8, 2, 64), (4, 4, 64), (2, 1, 32), (8, 1, 16)])
 @pytest.mark.parametrize("W,alpha", [(10, 0.713), (2, 1.0)])
