@@ -262,6 +262,28 @@ def _require(t, name, dtype=None, shape=None):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
 
 
+def _check_shapes(q, k, v=None, dout=None):
+    """Shapes and devices of the attention tensors, before any other check:
+    the C ABI takes raw pointers, so a K, V or dO smaller than Q implies
+    would be read (or written) past its end.  q [B, n, Hq, D]; k, v
+    [B, n, Hkv, D] with Hq a multiple of Hkv; dout like q."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-d: [B, n, H, D]")
+    B, n, hq, d = q.shape
+    hkv = k.shape[2]
+    if tuple(k.shape) != (B, n, hkv, d):
+        raise ValueError("k has shape %s, expected (%d, %d, Hkv, %d)" % (tuple(k.shape), B, n, d))
+    if hkv < 1 or hq % hkv:
+        raise ValueError("query heads %d are not a multiple of key/value heads %d" % (hq, hkv))
+    if v is not None and tuple(v.shape) != tuple(k.shape):
+        raise ValueError("v has shape %s, expected %s (like k)" % (tuple(v.shape), tuple(k.shape)))
+    if dout is not None and tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("dout has shape %s, expected %s (like q)" % (tuple(dout.shape), tuple(q.shape)))
+    for t, nm in ((k, "k"), (v, "v"), (dout, "dout")):
+        if t is not None and t.device != q.device:
+            raise ValueError("%s is on %s, q on %s" % (nm, t.device, q.device))
+
+
 class Problem:
     """Holds an ``sfa_attn`` and the host arrays it points to."""
 
@@ -291,10 +313,9 @@ def fwd(q, k, v, window=0, lo=None, frac=None, rope=None, scale=0.0, want_lse=Fa
     signed_offsets=True admits negative lo (later rows; SFA_FLAG_SIGNED_OFFSETS).
     """
     torch = _torch()
+    _check_shapes(q, k, v)
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, nm, q.dtype)
-    if k.shape != v.shape:
-        raise ValueError("k and v shapes differ")
     B, n, hq, d = q.shape
     pr = Problem(q, k, window, lo, frac, rope, scale, (SFA_FLAG_INTERP_KERNEL if interp_kernel else 0) |
                  (SFA_FLAG_SIGNED_OFFSETS if signed_offsets else 0))
@@ -311,6 +332,7 @@ def fwd(q, k, v, window=0, lo=None, frac=None, rope=None, scale=0.0, want_lse=Fa
 def fwd_edges(q, k, v, edges, count, rope=None, scale=0.0, want_lse=False, out=None):
     """Forward over per-query edge lists (device int32 [n, width], [n])."""
     torch = _torch()
+    _check_shapes(q, k, v)
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, nm, q.dtype)
     B, n, hq, d = q.shape
@@ -335,9 +357,11 @@ def bwd_workspace_bytes(q, k, window=0, lo=None, frac=None, rope=None, scale=0.0
 
 
 def bwd(q, k, v, lse, dout, window=0, lo=None, frac=None, rope=None, scale=0.0,
-        base=None, alpha=None, workspace=None, want_dd=True, signed_offsets=False):
-    """Backward: returns (dq, dk, dv, dd or None, dtheta or None)."""
+        base=None, alpha=None, workspace=None, want_dd=True, signed_offsets=False, out=None):
+    """Backward: returns (dq, dk, dv, dd or None, dtheta or None).  out:
+    optional (dq, dk, dv) tensors to write (like q, k, v)."""
     torch = _torch()
+    _check_shapes(q, k, v, dout)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _require(t, nm, q.dtype)
     B, n, hq, d = q.shape
@@ -346,7 +370,12 @@ def bwd(q, k, v, lse, dout, window=0, lo=None, frac=None, rope=None, scale=0.0,
     nb = _lib.sfa_bwd_workspace_bytes(pr.ref())
     if workspace is None:
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        for t, like, nm in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+            _require(t, nm, q.dtype, like.shape)
     nr = len(pr.lo)
     dd = torch.empty(max(nr, 1), dtype=torch.float32, device=q.device) if (want_dd and nr) else None
     dth = None
@@ -375,6 +404,7 @@ def bwd_edges(q, k, v, lse, dout, edges, count, inv, inv_count, rope=None, scale
     """Edge-list backward: returns (dq, dk, dv).  edges/count/inv/inv_count
     are device int32 tensors ([n, width], [n], [n, cap], [n])."""
     torch = _torch()
+    _check_shapes(q, k, v, dout)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _require(t, nm, q.dtype)
     B, n, hq, d = q.shape

@@ -332,12 +332,13 @@ extern "C" int sfa_bwd(const sfa_attn* a, const void* q, const void* k, const vo
                 ws_bytes);
   {
     ProfileScope ps("bwd_query", stream);
-    rc = hip_status(launch_bwd_query(p, t, q, k, v, lse, dout, dq, ws, stream), "sfa_bwd query launch");
+    rc = hip_status(launch_bwd_query(p, t, q, k, v, lse, dout, dq, ws, dd || dtheta, stream),
+                    "sfa_bwd query launch");
     if (rc) return rc;
   }
   {
     ProfileScope ps("bwd_key", stream);
-    rc = hip_status(launch_bwd_key(p, t, q, k, v, dout, dk, dv, ws, dd || dtheta, stream), "sfa_bwd key launch");
+    rc = hip_status(launch_bwd_key(p, t, q, k, v, dout, dk, dv, ws, stream), "sfa_bwd key launch");
     if (rc) return rc;
   }
   if (dd || dtheta) {

@@ -1,8 +1,9 @@
 // Backward kernels of libsfa (gfx950) for L = <O, dO> of the window plus
-// shared-offset forward ("Depth-Staggered Fibonacci Spacing for Sparse
-// Attention", gather paragraph: the interpolation between the floor and
-// floor-plus-one rows keeps a gradient to the offset distance, hence to
-// alpha and theta through the alpha parameterisation).
+// shared-offset forward.  Because every rung is a lerp of rows i-lo and
+// i-lo-1, the output is differentiable in the rung distance, and through
+// d_k = alpha f_k and the sigmoid map in theta ("Depth-Staggered Fibonacci
+// Spacing for Sparse Attention", gather paragraph and alpha
+// parameterisation).
 //
 // Launches on one stream, no atomics, fixed summation order:
 //
@@ -13,7 +14,13 @@
 //   accumulated as scale (sum p dp k~ - Dvec sum p k~), then rotated back to
 //   dQ.  The per-slot dot sums over a query's lanes are a reduce-scatter
 //   over the heads (HeadSlice).  p (0 where the slot has no row), dp and
-//   Dvec of every (query, slot, head) go to the workspace.
+//   Dvec of every (query, slot, head) go to the workspace.  The offset
+//   gradient is formed here too, from the fp32 rows and weights: for rung k
+//   and query head (i, h), dd_k gets scale dS (q~ . dK) + p (dO . dV) with
+//   dK = Kr[i-lo-1] - Kr[i-lo] and dV likewise; written as
+//   Y - Dvec X (Y = p (scale dp sd + vd), X = scale p sd) so that the
+//   per-rung values wait in registers until Dvec is known, then summed over
+//   the workgroup into one partial per (rung, workgroup).
 // bwd_key (key-centric transpose gather): key j receives from query j+lo
 //   (weight 1-frac) and j+lo+1 (weight frac) of every slot; those queries
 //   form contiguous ranges, so each lane gathers instead of scattering.
@@ -21,9 +28,9 @@
 //   with i-j fixed per (slot, tap), so unrotated Q rows are combined first
 //   and rotated once.  bf16: one launch of dK and dV workgroups, each
 //   staging half a query row into an LDS ring of rows that consecutive
-//   stages share.  Both also sum the per-block partials of dL/dd_k.
-// bwd_reduce: sums the dd partials in block order; dalpha = sum f_k dd_k;
-//   dtheta = (alpha - 1/2)(3/2 - alpha) dalpha.
+//   stages share.
+// bwd_reduce: sums the dd partials in block order (in double);
+//   dalpha = sum f_k dd_k; dtheta = (alpha - 1/2)(3/2 - alpha) dalpha.
 // The edge-list backward (bwd_edges_query, bwd_edges_key, further below)
 // does the same per query and per key over explicit lists.
 #include "sfa_device.h"
@@ -56,7 +63,8 @@ struct BwdArgs {
   const float* rope;
   int n, hq, hkv, nblk, tiles, S, n_rungs;
   int kcap;     // bwd_key: rows one stage may hold (dynamic LDS)
-  int need_dd;  // bwd_key: dd requested, so integer rungs also take their weight-0 second tap
+  int want_dd;  // bwd_query: dd requested
+  int r0;       // bwd_query: first rung whose dd this launch sums (a window of RPL x ND rungs)
   float scale, scale_log2;
 };
 
@@ -75,14 +83,29 @@ __device__ __forceinline__ float own_dot(const float (&a)[G][DC], const float (&
   return HeadSlice<G, LPQ>::reduce(part);
 }
 
-template <typename T, int D, int G, int LPQ, int CAP, int BQ>
-__global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable st) {
+// RPL: dd registers per lane.  The LPQ / G lanes of one (query, head) hold
+// bit-identical dot sums after the reduce-scatter; rung r of the launch's
+// window [a.r0, a.r0 + RPL * ND) is kept by the duplicate lane u = (r - r0)
+// % ND in register (r - r0) / ND.
+// The LDS of two workgroups fits a CU, and with G <= 4 their 16 waves fit
+// the register file when a lane stays within 128 VGPRs: ask for that.
+template <int G>
+constexpr int bwd_query_waves_per_eu() {
+  return G <= 4 ? 4 : 1;
+}
+template <typename T, int D, int G, int LPQ, int CAP, int BQ, int RPL>
+__global__ __launch_bounds__(BQ* LPQ) __attribute__((amdgpu_waves_per_eu(bwd_query_waves_per_eu<G>())))
+void bwd_query_kernel(BwdArgs a, SlotTable st) {
   constexpr int DC = D / LPQ;
   constexpr int KS = D + 4;
   constexpr int E = 16 / sizeof(T);
   constexpr int CPR = D / E;
   constexpr int NT = BQ * LPQ;
+  constexpr int ND = LPQ / G;       // duplicate lanes per (query, head)
+  constexpr int NWV = NT / 64;      // waves per workgroup
+  constexpr int RW_DD = RPL * ND;   // rungs whose dd one launch sums
   using HS = HeadSlice<G, LPQ>;
+  static_assert((ND & (ND - 1)) == 0 && NT % 64 == 0, "lane groups");
   // K and V rows of a stage in one LDS array, each led by a pad row:
   // [pad][K rows 0..CAP-1][pad][V rows 0..CAP-1].  Row r - 1 of a slot (its
   // interpolation partner, or a pad row when r = 0) is then never below the
@@ -132,6 +155,16 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
   }
   const float lse2 = active ? a.lse[(size_t(b) * a.hq + size_t(g) * G + own) * n + i] * kLog2e : 0.f;
   float dvec = 0.f;  // rowsum(dO * O) of the own head, as sum_slots p dp
+  // dd of the launch's rung window: X = scale p sd and Y = p (scale dp sd +
+  // vd) of this lane's rungs, combined with Dvec after the slot loop.
+  const bool want_dd = a.want_dd != 0;
+  const int ddu = c & (ND - 1);
+  float psum = 0.f;  // sum_slots p of the own head (1 up to the rounding of lse)
+  float xacc[RPL], yacc[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) xacc[r] = yacc[r] = 0.f;
+  // a slot whose dd this launch sums (uniform)
+  auto dd_slot = [&](int sj) { return want_dd && unsigned(st.rung[sj] - a.r0) < unsigned(RW_DD); };
 
   const size_t kv_row = size_t(a.hkv) * D;
   const T* Kseq = K + size_t(b) * n * kv_row + size_t(g) * D;
@@ -146,12 +179,13 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
   while (s < S) {
     const int lo0 = st.lo[s];
     if (lo0 > i_last) break;
-    int lomax = lo0 + (st.frac[s] > 0.f ? 1 : 0);
+    // interpolated slots and dd slots read their second row i - lo - 1
+    int lomax = lo0 + ((st.frac[s] > 0.f || dd_slot(s)) ? 1 : 0);
     int e = s + 1;
     while (e < S) {
       const int le = st.lo[e];
       if (le > i_last) break;
-      const int need = max(lomax, le + (st.frac[e] > 0.f ? 1 : 0));
+      const int need = max(lomax, le + ((st.frac[e] > 0.f || dd_slot(e)) ? 1 : 0));
       if (need - lo0 + BQ > CAP) break;
       lomax = need;
       ++e;
@@ -187,17 +221,26 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
       const float w = __int_as_float(wbits);
       const bool interp = wbits != 0;
       const float* const kp = lane_kv - lo * KS;  // K row r - 1
-      float kt[DC], vt[DC];
+      const bool dds = dd_slot(sj);
+      float kt[DC], vt[DC], dk[DC], dv[DC];
       load_vec<DC>(kp + KS, kt);
       load_vec<DC>(kp + KS + VOFF, vt);
-      if (interp) {
+      if (interp || dds) {
+        // dK, dV = row r - 1 minus row r: the lerp's slope and dd's factor
         float kb[DC], vb[DC];
         load_vec<DC>(kp, kb);
         load_vec<DC>(kp + VOFF, vb);
 #pragma unroll
         for (int x = 0; x < DC; ++x) {
-          kt[x] = fmaf(w, kb[x] - kt[x], kt[x]);
-          vt[x] = fmaf(w, vb[x] - vt[x], vt[x]);
+          dk[x] = kb[x] - kt[x];
+          dv[x] = vb[x] - vt[x];
+        }
+        if (interp) {
+#pragma unroll
+          for (int x = 0; x < DC; ++x) {
+            kt[x] = fmaf(w, dk[x], kt[x]);
+            vt[x] = fmaf(w, dv[x], vt[x]);
+          }
         }
       }
       float sp[G], dps[G];
@@ -214,6 +257,24 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
       }
       const float sdot = HS::reduce(sp);
       const float dp = HS::reduce(dps);
+      // dd slot: sd = q~ . dK and vd = dO . dV of the own head, fp32
+      float sd = 0.f, vd = 0.f;
+      if (dds) {
+        float sdp[G], vdp[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+          for (int x = 0; x < DC; ++x) {
+            s1 = fmaf(qv[j][x], dk[x], s1);
+            s2 = fmaf(dov[j][x], dv[x], s2);
+          }
+          sdp[j] = s1;
+          vdp[j] = s2;
+        }
+        sd = HS::reduce(sdp);
+        vd = HS::reduce(vdp);
+      }
       // The nearer row i - lo exists when mn <= i - lo <= n - 1, mn = 1 for
       // an interpolated slot (its farther row i - lo - 1 must exist too):
       // one unsigned compare and a select, no branch.  mn comes from integer
@@ -226,6 +287,7 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
       const float p = valid ? ex : 0.f;
       const float pdp = p * dp;
       dvec += pdp;
+      psum += p;
       if (active && HS::writer(c)) {  // p = 0 where the slot has no row for query i
         // The slot's plane bases stay scalar (global_store with an SGPR
         // base and the lane's 32-bit offset) instead of being folded into
@@ -247,6 +309,15 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
           acc_pd[j][x] = fmaf(pdh[j], kt[x], acc_pd[j][x]);
           acc_p[j][x] = fmaf(ph[j], kt[x], acc_p[j][x]);
         }
+      if (dds) {
+        const float X = active ? a.scale * p * sd : 0.f;
+        const float Y = active ? p * fmaf(a.scale * dp, sd, vd) : 0.f;
+        const int rr = st.rung[sj] - a.r0;
+        if (ddu == (rr & (ND - 1))) {
+          xacc[rr / ND] = X;
+          yacc[rr / ND] = Y;
+        }
+      }
     }
     s = e;
   }
@@ -305,6 +376,36 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
     }
   }
   if (active && HS::writer(c)) a.Dvec[(size_t(seq) * n + i) * G + own] = dvec;
+  if (want_dd) {
+    // sum_(query, head) of Y - Dvec X per rung over the workgroup: each
+    // (query, head) counts once (its duplicate lane u holds the rung), so
+    // the wave sums over the lane bits above ND, then the waves are added in
+    // order.  Fixed order: deterministic.  The weights are renormalised by
+    // l = sum p: the rounding of the forward's lse scales every p of a query
+    // by one common factor, which would otherwise enter each of the query's
+    // terms (dd is a sum of many terms of both signs, so that shared error
+    // does not cancel the way the terms do); with p / l the weights sum to
+    // one, as the exact softmax does.
+    __shared__ float ddw[NWV][RW_DD];
+    const int lane = tid & 63, wave = tid >> 6;
+    const float linv = psum > 0.f ? 1.f / psum : 0.f;
+    const float dvn = dvec * linv;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      float t = linv * fmaf(-dvn, xacc[r], yacc[r]);
+#pragma unroll
+      for (int m = ND; m < 64; m <<= 1) t += __shfl_xor(t, m);
+      if (lane < ND) ddw[wave][r * ND + lane] = t;
+    }
+    __syncthreads();
+    const int nr = min(a.n_rungs - a.r0, RW_DD);
+    for (int r = tid; r < nr; r += NT) {
+      float t = 0.f;
+#pragma unroll
+      for (int w_ = 0; w_ < NWV; ++w_) t += ddw[w_][r];
+      a.dd_part[size_t(a.r0 + r) * a.tiles + tile] = t;
+    }
+  }
   float dvh[G];
   HS::bcast(dvec, dvh);
   if (active) {
@@ -322,11 +423,8 @@ __global__ __launch_bounds__(BQ* LPQ) void bwd_query_kernel(BwdArgs a, SlotTable
 
 // Key-centric pass.  For key j and slot s (row pair i-lo, i-lo-1 of query
 // i): tap 0 is query j+lo (weight 1-frac), tap 1 is query j+lo+1 (weight
-// frac).  dS = scale p (dp - Dvec) is formed here from the stored p, dp and
-// Dvec.  The offset gradient dd_k = sum_i dK~.(Kr[i-lo-1] - Kr[i-lo]) +
-// dV~.(V[i-lo-1] - V[i-lo]) is gathered per key as well: key j meets each
-// rung once as the farther row (tap 1, sign +) and once as the nearer row
-// (tap 0, sign -), both taps taken even when frac = 0.
+// frac; only for an interpolated slot).  dS = scale p (dp - Dvec) is formed
+// here from the stored p, dp and Dvec.
 //
 // One workgroup per (sequence, block of KB keys, chunk of KC dims); one key
 // per lane.  The query rows a stage of slots needs, [j0 + lo_first,
@@ -353,9 +451,9 @@ constexpr int key_half_row_words(int G, int D) { return key_chunk(D) * ((G + 1) 
 // share the 160 KiB of LDS, but at least the block plus 12 rows (a window
 // of 10 and the interpolation tap in one stage) and at most the block plus
 // 64.
-inline int key_half_cap(int G, int D, int n_rungs) {
+inline int key_half_cap(int G, int D) {
   constexpr int kb = kKeyBlockH16, nw = kb / 64;
-  const int budget = 163840 * nw / 16 - nw * n_rungs * 4;
+  const int budget = 163840 * nw / 16;
   int cap = budget / (4 * key_half_row_words(G, D));
   if (cap < kb + 12) cap = kb + 12;
   if (cap > kb + 64) cap = kb + 64;
@@ -372,13 +470,10 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
   constexpr int RW = 2 * G * HW + 4;           // words per staged row (Q, dO, pad)
   constexpr int CH16 = KC * int(sizeof(T)) / 16;  // 16-byte pieces per head chunk
   constexpr int PPR = 2 * G * CH16;               // 16-byte pieces per row
-  constexpr int NW = KB / 64;
   static_assert(KC * sizeof(T) % 16 == 0, "16-byte pieces");
   __shared__ __align__(16) uint32_t Ws[KCAP * RW];
-  __shared__ float ddl[NW][SFA_MAX_OFFSETS];
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
   const int tile = xcd_tile(blockIdx.x, a.tiles);
   const int c = tile % NCH;
   const int rest = tile / NCH;
@@ -390,27 +485,16 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
   const int j = j0 + tid;
   const bool activej = j < n;
 
-  for (int t = tid; t < NW * SFA_MAX_OFFSETS; t += KB) (&ddl[0][0])[t] = 0.f;
-
   const T* __restrict__ Q = static_cast<const T*>(a.q);
   const T* __restrict__ dO = static_cast<const T*>(a.dout);
   const size_t ws_seq = size_t(seq) * a.S;
   const size_t kv_off = (size_t(b) * n + j) * size_t(a.hkv) * D + size_t(g) * D + c * KC;
 
-  float kj[KC], vj[KC];  // this key's own rows (unrotated K, V), for dd
-  if (activej) {
-    load_vec<KC>(static_cast<const T*>(a.k) + kv_off, kj);
-    load_vec<KC>(static_cast<const T*>(a.v) + kv_off, vj);
-  } else {
-#pragma unroll
-    for (int x = 0; x < KC; ++x) kj[x] = vj[x] = 0.f;
-  }
   float dk[KC], dv[KC];
 #pragma unroll
   for (int x = 0; x < KC; ++x) dk[x] = dv[x] = 0.f;
 
   const int S = st.count;
-  const int last_key = min(j0 + KB, n) - 1;
   int s = 0;
   while (s < S) {
     const int lo0 = st.lo[s];
@@ -461,7 +545,7 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
         for (int h = 0; h < G; ++h) pg[h] = dpg[h] = dvg[h] = 0.f;
       }
     };
-    auto taps_of = [&](int sj) { return (st.frac[sj] > 0.f || (a.need_dd && st.rung[sj] >= 0)) ? 2 : 1; };
+    auto taps_of = [&](int sj) { return st.frac[sj] > 0.f ? 2 : 1; };
 
     float pg[G], dpg[G], dvg[G];
     load_step(s, 0, pg, dpg, dvg);
@@ -477,7 +561,6 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
 
       const int lo = st.lo[sj];
       const float w = st.frac[sj];
-      const int rung = st.rung[sj];
       const int delta = lo + tap;
       const float wt = tap ? w : 1.f - w;
       const bool valid = step_valid(sj, tap);
@@ -512,13 +595,6 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
           dv[x] = fmaf(wt, yv[x], dv[x]);
         }
       }
-      if (rung >= 0) {
-        float part = 0.f;
-#pragma unroll
-        for (int x = 0; x < KC; ++x) part = fmaf(yk[x], kj[x], fmaf(yv[x], vj[x], part));
-        const float tot = wave_sum(tap ? part : -part);
-        if ((tid & 63) == 0) ddl[wave][rung] += tot;
-      }
       if (nsj < e) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -531,18 +607,10 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
       tap = ntap;
     }
     s = e;
-    (void)last_key;
   }
   if (activej) {
     store_vec<KC>(static_cast<T*>(a.dk) + kv_off, dk);
     store_vec<KC>(static_cast<T*>(a.dv) + kv_off, dv);
-  }
-  __syncthreads();
-  for (int r = tid; r < a.n_rungs; r += KB) {
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) acc += ddl[w][r];
-    a.dd_part[size_t(r) * a.tiles + tile] = acc;
   }
 }
 
@@ -550,11 +618,9 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
 // each stage half of a query row (one launch, bwd_key_h16_kernel below, runs
 // both).  PART 0 (dK) stages q~ = R(i) q of the
 // chunk (rotated while staging) and gathers yk~ = sum_h dS_h q~_h; dK~ =
-// sum w yk~ is rotated back once, dK = R(j)^T dK~, and the key term of dd_k
-// is yk~ . k~_j with k~_j = R(j) k_j (the relative rotation R(i - j) =
-// R(j)^T R(i) never has to be formed per step).  PART 1 (dV) stages dO and
-// gathers yv = sum_h p_h dO_h: dV += w yv, and the value term of dd_k is
-// yv . v_j.  A staged row holds the chunk of every head as f16 with the
+// sum w yk~ is rotated back once, dK = R(j)^T dK~ (the relative rotation
+// R(i - j) = R(j)^T R(i) never has to be formed per step).  PART 1 (dV)
+// stages dO and gathers yv = sum_h p_h dO_h: dV += w yv.  A staged row holds the chunk of every head as f16 with the
 // heads interleaved in pairs (word [hp][x] = (head 2hp, head 2hp+1) of dim
 // x), so each head sum is one v_dot2_f32_f16 per head pair and dim,
 // accumulated in fp32; dS and p enter as f16 pairs.  Half a row per
@@ -573,16 +639,13 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   constexpr int RW = key_half_row_words(G, D);
   constexpr int XH = KC / 8;       // 8-dim pieces per head chunk
   constexpr int PPR = GW * XH;     // staging pieces per row
-  constexpr int NW = KB / 64;
   constexpr int NQ = SMALL ? 1 : 3;  // VGPRs per slot-table column
   static_assert(KC % 8 == 0 && KB % PPR == 0, "8-dim pieces, whole rows per pass");
-  // Dynamic LDS: a.kcap staged rows of RW words, then NW x n_rungs dd sums.
+  // Dynamic LDS: a.kcap staged rows of RW words.
   extern __shared__ __align__(16) uint32_t key_smem[];
   uint32_t* Ws = key_smem;
-  float* ddl = reinterpret_cast<float*>(key_smem + size_t(a.kcap) * RW);
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
   const int c = tile % NCH;
   const int rest = tile / NCH;
   const int seq = rest / a.nblk;
@@ -593,22 +656,10 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   const int j = j0 + tid;
   const bool activej = j < n;
   const bool rope = PART == 0 && a.rope != nullptr;
-  const bool want_dd = a.need_dd != 0;  // dd partials are requested
-
-  for (int t = tid; t < NW * a.n_rungs; t += KB) ddl[t] = 0.f;
 
   const bf16_t* __restrict__ X = static_cast<const bf16_t*>(PART == 0 ? a.q : a.dout);
   const size_t kv_off = (size_t(b) * n + j) * size_t(a.hkv) * D + size_t(g) * D + c * KC;
 
-  // k~_j = R(j) k_j (dK) or v_j (dV): the dd term's partner row
-  float own[KC];
-  if (activej) {
-    load_vec<KC>(static_cast<const bf16_t*>(PART == 0 ? a.k : a.v) + kv_off, own);
-    if (rope) rotate_pairs<KC, 1>(own, a.rope + size_t(j) * D, c * KC);
-  } else {
-#pragma unroll
-    for (int x = 0; x < KC; ++x) own[x] = 0.f;
-  }
   float acc[KC];
 #pragma unroll
   for (int x = 0; x < KC; ++x) acc[x] = 0.f;
@@ -619,20 +670,16 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   // on lgkmcnt, and scalar loads return out of order).
   const int S = st.count;
   const int lane = tid & 63;
-  int vlo[NQ], vfr[NQ], vinfo[NQ];
+  int vlo[NQ], vfr[NQ], vtaps[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int sl = q * 64 + lane;
     const bool in = sl < S;
     const int sc = in ? sl : 0;
     const float fr = in ? st.frac[sc] : 0.f;
-    const int rg = in ? st.rung[sc] : -1;
     vlo[q] = in ? min(st.lo[sc], n) : n;
     vfr[q] = __float_as_int(fr);
-    // bits 0-15: rung + 1 (0 for a window slot); bit 16: a second tap (an
-    // interpolated rung, or any rung when dd is wanted: the weight-0 tap of
-    // an integer rung still carries its dd term)
-    vinfo[q] = (rg + 1) | ((in && (fr > 0.f || (a.need_dd && rg >= 0))) ? 0x10000 : 0);
+    vtaps[q] = fr > 0.f ? 2 : 1;  // an interpolated slot has a second tap
   }
   auto slot_i = [&](const int (&v)[NQ], int sj) {  // sj wave-uniform, < 64 * NQ
     if constexpr (SMALL) {
@@ -655,8 +702,10 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   const float* __restrict__ Pseq = a.P + size_t(seq) * a.S * n * G;
   const float* __restrict__ dPseq = a.dP + size_t(seq) * a.S * n * G;
   const float* __restrict__ Dseq = a.Dvec + size_t(seq) * n * G;
-  // the prefetch cursor: step (fs, ft) and its slot's min(lo, n) and taps
+  // the prefetch cursor: step (fs, ft) and its slot's min(lo, n), taps and
+  // fraction
   int fs = 0, ft = 0, flo = 0, ftaps = 1;
+  float fw = 0.f;
   // The three loads share the lane's 32-bit byte offset i * G * 4 from
   // uniform bases (the slot's planes of p and dp, and Dvec), so the address
   // arithmetic is scalar except for that offset.
@@ -673,17 +722,23 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
       load_global_at<G>(vb, ioff, raw[2]);
     }
   };
-  // f16 weight pairs of the cursor's step: dS = scale p (dp - Dvec) for dK,
-  // p for dV; zero for a masked step.
+  // f16 weight pairs of the cursor's step, times its tap weight wt (1 - frac
+  // for the nearer row, frac for the farther one): wt dS, dS = scale p (dp -
+  // Dvec), for dK, wt p for dV; zero for a masked step.
   auto convert = [&](const float (&raw)[NR][G], uint32_t (&wts)[GW]) {
     const bool valid = fs < S && unsigned(j + flo + ft) < unsigned(n);
+    const float wt = ft ? fw : 1.f - fw;
+    const float ws = PART == 0 ? a.scale * wt : wt;
 #pragma unroll
     for (int hp = 0; hp < GW; ++hp) {
       const int h0 = 2 * hp, h1 = 2 * hp + 1 < G ? 2 * hp + 1 : 2 * hp;
       float w0 = raw[0][h0], w1 = 2 * hp + 1 < G ? raw[0][h1] : 0.f;
       if constexpr (PART == 0) {
-        w0 = a.scale * w0 * (raw[1][h0] - raw[2][h0]);
-        w1 = a.scale * w1 * (raw[1][h1] - raw[2][h1]);
+        w0 = ws * w0 * (raw[1][h0] - raw[2][h0]);
+        w1 = ws * w1 * (raw[1][h1] - raw[2][h1]);
+      } else {
+        w0 *= ws;
+        w1 *= ws;
       }
       const uint32_t pk = G == 1 ? __float_as_uint(w0) : pack_h2(w0, w1);
       wts[hp] = valid ? pk : 0u;
@@ -698,7 +753,8 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
       ft = 0;
       if (fs < S) {
         flo = slot_i(vlo, fs);
-        ftaps = (slot_i(vinfo, fs) >> 16) + 1;
+        ftaps = slot_i(vtaps, fs);
+        fw = __int_as_float(slot_i(vfr, fs));
       }
     }
   };
@@ -713,7 +769,8 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   float raw[NR][G];
   if (S > 0) {
     flo = slot_i(vlo, 0);
-    ftaps = (slot_i(vinfo, 0) >> 16) + 1;
+    ftaps = slot_i(vtaps, 0);
+    fw = __int_as_float(slot_i(vfr, 0));
     load_step(raw);
     convert(raw, wts);
     advance();
@@ -878,18 +935,13 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
 
     for (int sj = s; sj < e; ++sj) {
       const int lo = slot_i(vlo, sj);
-      const float w = __int_as_float(slot_i(vfr, sj));
-      const int info = slot_i(vinfo, sj);
-      const int rung = (info & 0xffff) - 1;
-      const int ntaps = (info >> 16) + 1;
-      float ddacc = 0.f;
+      const int ntaps = slot_i(vtaps, sj);
       for (int tap = 0; tap < ntaps; ++tap) {
         const int delta = lo + tap;
-        const float wt = tap ? w : 1.f - w;
         // Query j + delta; the query pass stored p = 0 where the slot has no
         // row for it.  Masked steps read ring slot 0 with zero weights.
-        // Window slots run the same arithmetic with weight 1; their dd sum is
-        // never stored.  One straight-line body keeps the registers put.
+        // The tap weight (1 - frac or frac) is already in the step's
+        // weights.  One straight-line body keeps the registers put.
         // Ring slot of query j + delta: tid + soff (soff uniform), wrapped
         // once past kcap; as a byte offset, the lane's tid * RW * 4 plus a
         // scalar term, minus the ring size where tid >= kcap - soff.
@@ -899,41 +951,23 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
         const unsigned roff = tid_b + unsigned(soff * RW * 4) - wrap;
         const uint32_t* rowp = reinterpret_cast<const uint32_t*>(
             reinterpret_cast<const char*>(Ws) + (valid ? roff : 0u));
-        float part = 0.f;
         if constexpr (G == 1) {
-          // y = w0 x: acc += (wt w0) x, and y . own = w0 (x . own)
+          // acc += (wt w0) x
           uint32_t xw[KC];
           load_words<KC>(rowp, xw);
           const float w0 = __uint_as_float(wts[0]);
-          const float ww = wt * w0;
 #pragma unroll
-          for (int x = 0; x < KC; ++x) acc[x] = fmaf(ww, __uint_as_float(xw[x]), acc[x]);
-          if (want_dd) {  // uniform: the dd dot product only when dd is requested
-            float xo = 0.f;
-#pragma unroll
-            for (int x = 0; x < KC; ++x) xo = fmaf(__uint_as_float(xw[x]), own[x], xo);
-            part = w0 * xo;
-          }
+          for (int x = 0; x < KC; ++x) acc[x] = fmaf(w0, __uint_as_float(xw[x]), acc[x]);
         } else {
-          float y[KC];
+          // acc += sum over head pairs of dot2((wt w_2hp, wt w_2hp+1), x)
           uint32_t xw[KC];
-          load_words<KC>(rowp, xw);
 #pragma unroll
-          for (int x = 0; x < KC; ++x) y[x] = dot2_h(wts[0], xw[x], 0.f);
-#pragma unroll
-          for (int hp = 1; hp < GW; ++hp) {
+          for (int hp = 0; hp < GW; ++hp) {
             load_words<KC>(rowp + hp * KC, xw);
 #pragma unroll
-            for (int x = 0; x < KC; ++x) y[x] = dot2_h(wts[hp], xw[x], y[x]);
-          }
-#pragma unroll
-          for (int x = 0; x < KC; ++x) acc[x] = fmaf(wt, y[x], acc[x]);
-          if (want_dd) {
-#pragma unroll
-            for (int x = 0; x < KC; ++x) part = fmaf(y[x], own[x], part);
+            for (int x = 0; x < KC; ++x) acc[x] = dot2_h(wts[hp], xw[x], acc[x]);
           }
         }
-        ddacc += tap ? part : -part;
 
         // weights of the next step, then the loads of the one after it
         convert(raw, wts);
@@ -941,24 +975,12 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
         advance();
         load_step(raw);
       }
-      if (rung >= 0) {
-        const float tot = wave_sum(ddacc);
-        if ((tid & 63) == 0) ddl[wave * a.n_rungs + rung] += tot;
-      }
     }
     s = e;
   }
   if (activej) {
     if (rope) rotate_pairs<KC, -1>(acc, a.rope + size_t(j) * D, c * KC);  // dK = R(j)^T dK~
     store_vec<KC>(static_cast<bf16_t*>(PART == 0 ? a.dk : a.dv) + kv_off, acc);
-  }
-  __syncthreads();
-  // dd partials: [rung][2 * tiles], the dK half first
-  for (int r = tid; r < a.n_rungs; r += KB) {
-    float t_ = 0.f;
-#pragma unroll
-    for (int w_ = 0; w_ < NW; ++w_) t_ += ddl[w_ * a.n_rungs + r];
-    a.dd_part[size_t(r) * (2 * a.tiles) + PART * a.tiles + tile] = t_;
   }
 }
 
@@ -984,19 +1006,20 @@ struct ReduceArgs {
   float base[SFA_MAX_OFFSETS];
 };
 
-// One workgroup of 16 waves.  The partials are stored rung-major
-// ([rung][block]), so wave w reduces rungs w, w+16, ... with coalesced
-// loads: lane l adds the partials of blocks l, l+64, ... in block order,
-// then the wave adds its 64 lanes in a fixed DPP/shuffle tree.  The result
-// does not depend on timing.
+// One workgroup of 16 waves.  The partials (one per query-pass workgroup)
+// are stored rung-major ([rung][block]), so wave w reduces rungs w, w+16,
+// ... with coalesced loads: lane l adds the partials of blocks l, l+64, ...
+// in block order, then the wave adds its 64 lanes in a fixed shuffle tree,
+// all in double (a dd_k is a sum over every query and head of the batch,
+// often a near cancellation).  The result does not depend on timing.
 constexpr int kReduceThreads = 1024;
 
 __global__ __launch_bounds__(kReduceThreads) void bwd_reduce_kernel(ReduceArgs a) {
-  __shared__ float sdd[SFA_MAX_OFFSETS];
+  __shared__ double sdd[SFA_MAX_OFFSETS];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   for (int r = wave; r < a.n_rungs; r += kReduceThreads / 64) {
-    float acc = 0.f;
+    double acc = 0.0;
     const float* row = a.dd_part + size_t(r) * a.blocks;
     int blk = lane;
     for (; blk + 7 * 64 < a.blocks; blk += 8 * 64) {
@@ -1004,19 +1027,20 @@ __global__ __launch_bounds__(kReduceThreads) void bwd_reduce_kernel(ReduceArgs a
 #pragma unroll
       for (int u = 0; u < 8; ++u) x[u] = row[blk + u * 64];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc += x[u];
+      for (int u = 0; u < 8; ++u) acc += double(x[u]);
     }
-    for (; blk < a.blocks; blk += 64) acc += row[blk];
-    const float tot = wave_sum(acc);
+    for (; blk < a.blocks; blk += 64) acc += double(row[blk]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) acc += __shfl_xor(acc, m);
     if (lane == 0) {
-      sdd[r] = tot;
-      if (a.dd) a.dd[r] = tot;
+      sdd[r] = acc;
+      if (a.dd) a.dd[r] = float(acc);
     }
   }
   __syncthreads();
   if (threadIdx.x == 0 && a.dtheta) {
     double da = 0.0;
-    for (int r = 0; r < a.n_rungs; ++r) da += double(a.base[r]) * double(sdd[r]);
+    for (int r = 0; r < a.n_rungs; ++r) da += double(a.base[r]) * sdd[r];
     a.dtheta[0] = float((a.alpha - 0.5) * (1.5 - a.alpha) * da);
   }
 }
@@ -1076,15 +1100,41 @@ BwdArgs make_args(const Problem& p, const SlotTable& t, const BwdWorkspace& ws) 
   return a;
 }
 
+// dd registers per lane of bwd_query: the small variant holds 16 rungs
+// (the Fibonacci and power-of-2 bases), the large one 16 x ND (ND = LPQ / G
+// duplicate lanes per query head); more rungs take one launch per window of
+// 16 x ND (every launch writes the same dQ and workspace, and the dd
+// partials of its own rungs).
+template <int D, int G>
+constexpr int bwd_rpl_small() {
+  constexpr int nd = bwd_lpq<D, G>() / G;
+  return nd >= 16 ? 1 : 16 / nd;
+}
+constexpr int kRplLarge = 16;
+
 template <typename T, int D, int G>
 int launch_query_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
   constexpr int LPQ = bwd_lpq<D, G>();
   constexpr int BQ = bwd_bq<G>();
+  constexpr int ND = LPQ / G;
+  constexpr int RS = bwd_rpl_small<D, G>();
   BwdArgs a = a0;
   a.nblk = (a.n + BQ - 1) / BQ;
   a.tiles = a.nblk * (a0.tiles / a0.nblk);
-  hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, kCap, BQ>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
-  return int(hipGetLastError());
+  const bool dd = a.want_dd && t.n_rungs > 0;
+  a.want_dd = dd ? 1 : 0;
+  a.r0 = 0;
+  if (!dd || t.n_rungs <= RS * ND) {
+    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, kCap, BQ, RS>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+    return int(hipGetLastError());
+  }
+  for (int r0 = 0; r0 < t.n_rungs; r0 += kRplLarge * ND) {
+    a.r0 = r0;
+    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, kCap, BQ, kRplLarge>), dim3(a.tiles), dim3(BQ * LPQ), 0, st,
+                       a, t);
+    if (hipError_t e = hipGetLastError()) return int(e);
+  }
+  return 0;
 }
 
 template <typename T, int D, int G>
@@ -1094,8 +1144,8 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
     constexpr int KB = kKeyBlockH16;
     a.nblk = (a.n + KB - 1) / KB;
     a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk(D));
-    a.kcap = key_half_cap(G, D, t.n_rungs);
-    const size_t lds = (size_t(a.kcap) * key_half_row_words(G, D) + size_t(KB / 64) * t.n_rungs) * 4;
+    a.kcap = key_half_cap(G, D);
+    const size_t lds = size_t(a.kcap) * key_half_row_words(G, D) * 4;
     const bool small = t.count <= 64;
     if (small)
       hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, true>), dim3(2 * a.tiles), dim3(KB), lds, st, a, t);
@@ -1373,11 +1423,10 @@ size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, Bw
   auto al = [](size_t e) { return (e + 63) & ~size_t(63); };  // 256-byte aligned sections
   const size_t pe = al(size_t(p.B) * p.hkv * t.count * size_t(p.n) * p.G);  // floats per array
   const size_t de = al(size_t(p.B) * p.hkv * size_t(p.n) * p.G);
-  // dd partials per rung: one per key-pass workgroup (bf16: the dK and the
-  // dV kernel each have one per tile)
+  // dd partials per rung: one per query-pass workgroup
   const bool h16 = p.dtype == SFA_BF16;
-  const int kb = h16 ? kKeyBlockH16 : key_block(4, p.G, p.D);
-  ws->blocks = ((p.n + kb - 1) / kb) * p.B * p.hkv * (p.D / key_chunk(p.D)) * (h16 ? 2 : 1);
+  const int bq = p.G >= 4 ? bwd_bq<4>() : bwd_bq<1>();
+  ws->blocks = ((p.n + bq - 1) / bq) * p.B * p.hkv;
   const size_t dd_e = al(size_t(ws->blocks) * (t.n_rungs > 0 ? t.n_rungs : 1));
   // packed key-pass rows (bf16, G >= 2): D * G / 2 words per (sequence, row)
   const size_t xe = (h16 && p.G >= 2) ? al(size_t(p.B) * p.hkv * size_t(p.n) * p.D * (p.G / 2)) : 0;
@@ -1393,8 +1442,10 @@ size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, Bw
 }
 
 int launch_bwd_query(const Problem& p, const SlotTable& t, const void* q, const void* k, const void* v,
-                     const float* lse, const void* dout, void* dq, const BwdWorkspace& ws, void* stream) {
+                     const float* lse, const void* dout, void* dq, const BwdWorkspace& ws, bool want_dd,
+                     void* stream) {
   BwdArgs a = make_args(p, t, ws);
+  a.want_dd = want_dd ? 1 : 0;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -1406,9 +1457,8 @@ int launch_bwd_query(const Problem& p, const SlotTable& t, const void* q, const 
 }
 
 int launch_bwd_key(const Problem& p, const SlotTable& t, const void* q, const void* k, const void* v,
-                   const void* dout, void* dk, void* dv, const BwdWorkspace& ws, bool need_dd, void* stream) {
+                   const void* dout, void* dk, void* dv, const BwdWorkspace& ws, void* stream) {
   BwdArgs a = make_args(p, t, ws);
-  a.need_dd = need_dd ? 1 : 0;
   a.q = q;
   a.k = k;
   a.v = v;

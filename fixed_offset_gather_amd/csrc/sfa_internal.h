@@ -51,7 +51,7 @@ struct BwdWorkspace {
   float* p;        // [B][Hkv][S][n][G] softmax probabilities (0 where a slot has no row)
   float* dp;       // [B][Hkv][S][n][G] dO . v~
   float* dvec;     // [B][Hkv][n][G] rowsum(dO * O) = sum_slots p dp
-  float* dd_part;  // [n_rungs][blocks] per-block partial sums of dL/dd_k
+  float* dd_part;  // [n_rungs][blocks] per-block partial sums of dL/dd_k (one per query-pass workgroup)
   // bf16 with G >= 2: the query pass's rows for the key pass, as f16 head
   // pairs in the key pass's LDS row layout, [B][Hkv][n][D/16][G/2][16] words
   // (word = heads (2hp, 2hp+1) of one dim): q rotated by its own position,
@@ -76,10 +76,10 @@ int launch_bwd_edges(const Problem& p, const int32_t* edges, const int32_t* coun
 int launch_bwd_query(const Problem& p, const SlotTable& t, const void* q,
                      const void* k, const void* v, const float* lse,
                      const void* dout, void* dq, const BwdWorkspace& ws,
-                     void* stream);
+                     bool want_dd, void* stream);
 int launch_bwd_key(const Problem& p, const SlotTable& t, const void* q,
                    const void* k, const void* v, const void* dout, void* dk,
-                   void* dv, const BwdWorkspace& ws, bool need_dd, void* stream);
+                   void* dv, const BwdWorkspace& ws, void* stream);
 int launch_bwd_reduce(const SlotTable& t, const BwdWorkspace& ws,
                       const float* base_f, double alpha, float* dd,
                       float* dtheta, void* stream);

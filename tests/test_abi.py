@@ -172,9 +172,9 @@ def test_bwd_validation_and_workspace_size():
     al = lambda e: (e + 63) // 64 * 64
     pe = al(2 * 2 * S * 100 * 4)          # p and dp: [B][Hkv][S][n][G]
     de = al(2 * 2 * 100 * 4)              # Dvec: [B][Hkv][n][G]
-    # dd partials: one per key-pass tile (128-key blocks x B x Hkv x 16-dim
-    # chunks) from each of the bf16 dK and dV halves
-    blocks = 1 * 2 * 2 * 4 * 2
+    # dd partials: one per query-pass workgroup (32-query blocks at 4 heads
+    # per KV head, x B x Hkv)
+    blocks = 4 * 2 * 2
     dd = al(blocks * 15)
     # packed key-pass rows of q and dO (bf16, G >= 2): D * G / 2 words per row
     xe = al(2 * 2 * 100 * 64 * 2)
@@ -286,3 +286,54 @@ def test_profile_controls_without_launches():
     sfa.profile_reset()
     assert sfa.profile_read("bwd_query") == (0.0, 0)
     sfa.profile_enable(False, only=None)
+
+
+def _cpu(shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.float32)
+
+
+@pytest.mark.parametrize("which,shape", [
+    ("k", (2, 50, 2, 32)),    # k shorter than q's sequence
+    ("k", (1, 64, 2, 32)),    # k with fewer batch entries
+    ("k", (2, 64, 2, 16)),    # k with another head dim
+    ("k", (2, 64, 3, 32)),    # query heads not a multiple of key heads
+    ("v", (2, 64, 2, 16)),    # v unlike k
+    ("v", (2, 63, 2, 32)),
+])
+def test_binding_rejects_mismatched_kv_shapes(which, shape):
+    # A K or V smaller than Q implies would be read past its end by the
+    # kernels (raw pointers); the binding refuses it before any device use.
+    q, k, v = _cpu((2, 64, 8, 32)), _cpu((2, 64, 2, 32)), _cpu((2, 64, 2, 32))
+    bad = _cpu(shape)
+    k_, v_ = (bad, v) if which == "k" else (k, bad)
+    lo, fr = sfa.offsets_fib(1.0)
+    with pytest.raises(ValueError):
+        sfa.fwd(q, k_, v_, 4, lo, fr)
+    with pytest.raises(ValueError):
+        sfa.bwd(q, k_, v_, _cpu((2, 8, 64)), q, 4, lo, fr)
+    e, c = _cpu((64, 8)), _cpu((64,))
+    with pytest.raises(ValueError):
+        sfa.fwd_edges(q, k_, v_, e, c)
+    with pytest.raises(ValueError):
+        sfa.bwd_edges(q, k_, v_, _cpu((2, 8, 64)), q, e, c, e, c)
+
+
+@pytest.mark.parametrize("shape", [(2, 64, 8, 16), (2, 63, 8, 32), (1, 64, 8, 32), (2, 64, 4, 32)])
+def test_binding_rejects_mismatched_dout(shape):
+    q, k = _cpu((2, 64, 8, 32)), _cpu((2, 64, 2, 32))
+    lo, fr = sfa.offsets_fib(1.0)
+    with pytest.raises(ValueError):
+        sfa.bwd(q, k, k, _cpu((2, 8, 64)), _cpu(shape), 4, lo, fr)
+    e, c = _cpu((64, 8)), _cpu((64,))
+    with pytest.raises(ValueError):
+        sfa.bwd_edges(q, k, k, _cpu((2, 8, 64)), _cpu(shape), e, c, e, c)
+
+
+def test_binding_rejects_tensors_on_different_devices():
+    import torch
+    q, k = _cpu((1, 8, 2, 16)), _cpu((1, 8, 1, 16))
+    meta = torch.zeros((1, 8, 1, 16), dtype=torch.float32, device="meta")
+    lo, fr = sfa.offsets_fib(1.0)
+    with pytest.raises(ValueError):
+        sfa.fwd(q, k, meta, 0, lo, fr)
