@@ -43,6 +43,7 @@ SFA_FLAG_INTERP_KERNEL = 1
 SFA_FLAG_SIGNED_OFFSETS = 2
 MAX_OFFSETS = 128
 MAX_SLOTS = 192
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 SCHEDULES = {"fixed": 0, "linear": 1, "coprime": 2}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -91,6 +92,8 @@ _sig("sfa_fwd_edges", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _c.c_int, _vp, _
 _sig("sfa_bwd_workspace_bytes", _c.c_size_t, [_c.POINTER(SfaAttn)])
 _sig("sfa_bwd", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _vp, _i32p, _c.c_double, _vp, _vp, _c.c_size_t, _vp])
+_sig("sfa_bwd_noalloc", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _i32p, _c.c_double, _vp, _vp])
 _sig("sfa_bwd_edges_workspace_bytes", _c.c_size_t, [_c.POINTER(SfaAttn), _c.c_int])
 _sig("sfa_bwd_edges", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _c.c_int, _vp, _vp, _c.c_int, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _c.c_size_t, _vp])

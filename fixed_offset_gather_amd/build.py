@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsfa.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["sfa_api.hip", "sfa_fwd.hip", "sfa_bwd.hip"]
+HIP_SOURCES = ["sfa_api.hip", "sfa_fwd.hip", "sfa_bwd.hip", "sfa_noalloc.hip"]
 CXX_SOURCES = ["sfa_producers.cpp"]
 
 # Packed FP32 instructions are disabled for all device code.  The tied

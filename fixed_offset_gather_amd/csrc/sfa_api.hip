@@ -285,8 +285,7 @@ extern "C" int sfa_bwd_edges(const sfa_attn* a, const int32_t* edges, const int3
                     "sfa_bwd_edges launch");
 }
 
-extern "C" size_t sfa_bwd_workspace_bytes(const sfa_attn* a) {
-  clear_error();
+size_t sfa::bwd_workspace_bytes(const sfa_attn* a) {
   Problem p;
   if (validate_problem(a, &p)) return 0;
   SlotTable t;
@@ -295,17 +294,22 @@ extern "C" size_t sfa_bwd_workspace_bytes(const sfa_attn* a) {
   return bwd_workspace_layout(p, t, nullptr, &ws);
 }
 
-extern "C" int sfa_bwd(const sfa_attn* a, const void* q, const void* k, const void* v,
-                       const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dd,
-                       const int32_t* base, double alpha, float* dtheta, void* workspace,
-                       size_t ws_bytes, void* stream) {
+extern "C" size_t sfa_bwd_workspace_bytes(const sfa_attn* a) {
   clear_error();
+  return bwd_workspace_bytes(a);
+}
+
+namespace sfa {
+
+int bwd_impl(const sfa_attn* a, const void* q, const void* k, const void* v, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, float* dd, const int32_t* base, double alpha, float* dtheta,
+             void* workspace, size_t ws_bytes, void* stream, const char* fn) {
   Problem p;
   int rc = validate_problem(a, &p);
   if (rc) return rc;
   if (dtheta) {
-    if (p.n_off > 0 && !base) return fail(SFA_ERR_ARG, "sfa_bwd: dtheta needs the base rungs");
-    if (!std::isfinite(alpha)) return fail(SFA_ERR_ARG, "sfa_bwd: alpha must be finite");
+    if (p.n_off > 0 && !base) return fail(SFA_ERR_ARG, "%s: dtheta needs the base rungs", fn);
+    if (!std::isfinite(alpha)) return fail(SFA_ERR_ARG, "%s: alpha must be finite", fn);
   }
   SlotTable t;
   build_slots(a, &t);
@@ -317,33 +321,40 @@ extern "C" int sfa_bwd(const sfa_attn* a, const void* q, const void* k, const vo
     // Nothing to sum: the reduce kernel over zero blocks writes zero dd/dtheta.
     if (!dd && !dtheta) return SFA_OK;
     ProfileScope ps("bwd_reduce", stream);
-    return hip_status(launch_bwd_reduce(t, ws, base_f, alpha, dd, dtheta, stream), "sfa_bwd reduce launch");
+    return hip_status(launch_bwd_reduce(t, ws, base_f, alpha, dd, dtheta, stream), "bwd reduce launch");
   }
-  if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv)
-    return fail(SFA_ERR_ARG, "sfa_bwd: NULL tensor");
+  if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv) return fail(SFA_ERR_ARG, "%s: NULL tensor", fn);
   const void* ptrs[] = {q, k, v, lse, dout, dq, dk, dv};
   for (const void* x : ptrs)
-    if (!aligned16(x)) return fail(SFA_ERR_ARG, "sfa_bwd: tensors must be 16-byte aligned");
-  if (dd && (reinterpret_cast<uintptr_t>(dd) & 3u)) return fail(SFA_ERR_ARG, "sfa_bwd: dd misaligned");
-  if (dtheta && (reinterpret_cast<uintptr_t>(dtheta) & 3u))
-    return fail(SFA_ERR_ARG, "sfa_bwd: dtheta misaligned");
+    if (!aligned16(x)) return fail(SFA_ERR_ARG, "%s: tensors must be 16-byte aligned", fn);
+  if (dd && (reinterpret_cast<uintptr_t>(dd) & 3u)) return fail(SFA_ERR_ARG, "%s: dd misaligned", fn);
+  if (dtheta && (reinterpret_cast<uintptr_t>(dtheta) & 3u)) return fail(SFA_ERR_ARG, "%s: dtheta misaligned", fn);
   if (!workspace || ws_bytes < need || !aligned16(workspace))
-    return fail(SFA_ERR_CAPACITY, "sfa_bwd: workspace needs %zu bytes (16-byte aligned), got %zu", need,
-                ws_bytes);
+    return fail(SFA_ERR_CAPACITY, "%s: workspace needs %zu bytes (16-byte aligned), got %zu", fn, need, ws_bytes);
   {
     ProfileScope ps("bwd_query", stream);
-    rc = hip_status(launch_bwd_query(p, t, q, k, v, lse, dout, dq, ws, dd || dtheta, stream),
-                    "sfa_bwd query launch");
+    rc = hip_status(launch_bwd_query(p, t, q, k, v, lse, dout, dq, ws, dd || dtheta, stream), "bwd query launch");
     if (rc) return rc;
   }
   {
     ProfileScope ps("bwd_key", stream);
-    rc = hip_status(launch_bwd_key(p, t, q, k, v, dout, dk, dv, ws, stream), "sfa_bwd key launch");
+    rc = hip_status(launch_bwd_key(p, t, q, k, v, dout, dk, dv, ws, stream), "bwd key launch");
     if (rc) return rc;
   }
   if (dd || dtheta) {
     ProfileScope ps("bwd_reduce", stream);
-    rc = hip_status(launch_bwd_reduce(t, ws, base_f, alpha, dd, dtheta, stream), "sfa_bwd reduce launch");
+    rc = hip_status(launch_bwd_reduce(t, ws, base_f, alpha, dd, dtheta, stream), "bwd reduce launch");
   }
   return rc;
+}
+
+}  // namespace sfa
+
+extern "C" int sfa_bwd(const sfa_attn* a, const void* q, const void* k, const void* v,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv, float* dd,
+                       const int32_t* base, double alpha, float* dtheta, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  clear_error();
+  return bwd_impl(a, q, k, v, lse, dout, dq, dk, dv, dd, base, alpha, dtheta, workspace, ws_bytes, stream,
+                  "sfa_bwd");
 }

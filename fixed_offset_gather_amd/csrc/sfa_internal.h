@@ -84,6 +84,15 @@ int launch_bwd_reduce(const SlotTable& t, const BwdWorkspace& ws,
                       const float* base_f, double alpha, float* dd,
                       float* dtheta, void* stream);
 
+// sfa_bwd's validation and launches with the workspace given; shared by the
+// entry points that bring their own workspace and the one that uses the
+// library's static scratch (fn names the caller in error messages).
+int bwd_impl(const sfa_attn* a, const void* q, const void* k, const void* v, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, float* dd, const int32_t* base, double alpha, float* dtheta,
+             void* workspace, size_t ws_bytes, void* stream, const char* fn);
+// Workspace bytes sfa_bwd needs (0 after recording the error on bad input).
+size_t bwd_workspace_bytes(const sfa_attn* a);
+
 // Event-pair bracketing for sfa_profile_*; no-ops while profiling is off.
 struct ProfileScope {
   ProfileScope(const char* name, void* stream);

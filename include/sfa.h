@@ -287,6 +287,26 @@ int sfa_bwd(const sfa_attn* a, const void* q, const void* k, const void* v,
             float* dd, const int32_t* base, double alpha, float* dtheta,
             void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * sfa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * sfa_bwd (bit-identical outputs); the workspace is the library's static
+ * device scratch of SFA_NOALLOC_SCRATCH_BYTES, one copy per device, taken
+ * when the library's device code is first used on that device and held until
+ * the process ends.  Allocates nothing.  A problem whose sfa_bwd_workspace_bytes
+ * exceeds SFA_NOALLOC_SCRATCH_BYTES returns SFA_ERR_CAPACITY before any HIP
+ * call (the page-1 learned-alpha step, 32 x 1024 tokens at 8/2 heads, needs
+ * about 122 MB).  Calls that overlap on one device share the scratch and race:
+ * serialise them (one stream, or events).  The first call on a device looks up
+ * that device's copy with hipGetSymbolAddress.
+ */
+#define SFA_NOALLOC_SCRATCH_BYTES (128ull * 1024 * 1024)
+int sfa_bwd_noalloc(const sfa_attn* a, const void* q, const void* k, const void* v,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    float* dd, const int32_t* base, double alpha, float* dtheta,
+                    void* stream);
+
 /* ------------------------------------------------------------------ */
 /* Kernel timing (measurement support; off by default)                  */
 /* ------------------------------------------------------------------ */

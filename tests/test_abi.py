@@ -337,3 +337,21 @@ def test_binding_rejects_tensors_on_different_devices():
     lo, fr = sfa.offsets_fib(1.0)
     with pytest.raises(ValueError):
         sfa.fwd(q, k, meta, 0, lo, fr)
+
+
+def test_noalloc_rejects_oversize_and_invalid_before_any_device_call():
+    # The scratch holds SFA_NOALLOC_SCRATCH_BYTES; a larger workspace need is
+    # refused with SFA_ERR_CAPACITY, an invalid problem with its own code,
+    # both before any HIP call (this runs without a GPU).
+    lib = sfa.library()
+    lo, frac = sfa.offsets_fib(0.8)
+    big = _prob(batch=64, seqlen=1024, lo=lo, frac=frac, window=10)
+    assert lib.sfa_bwd_workspace_bytes(ctypes.byref(big)) > sfa.NOALLOC_SCRATCH_BYTES
+    base = sfa.base_fib()
+    bp = base.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    args = [FAKE] * 9
+    rc = lib.sfa_bwd_noalloc(ctypes.byref(big), *args, bp, 0.8, FAKE, None)
+    assert rc == sfa.SFA_ERR_CAPACITY
+    assert b"static scratch" in lib.sfa_last_error()
+    rc = lib.sfa_bwd_noalloc(ctypes.byref(_prob(head_dim=48)), *args, bp, 0.8, FAKE, None)
+    assert rc == sfa.SFA_ERR_UNSUPPORTED
