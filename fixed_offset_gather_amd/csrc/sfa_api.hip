@@ -78,17 +78,17 @@ int build_slots(const sfa_attn* a, SlotTable* t, bool merge) {
   t->n_rungs = a->n_off;
   int c = 0;
   for (size_t s = 0; s < v.size(); ++s) {
-    if (merge && c > 0 && t->lo[c - 1] == v[s].lo && t->frac[c - 1] == v[s].frac) {
-      t->mult[c - 1] += 1.f;
-      t->rung[c - 1] = -1;
+    if (merge && c > 0 && t->s[c - 1].lo == v[s].lo && t->s[c - 1].frac == v[s].frac) {
+      t->s[c - 1].mult += 1.f;
+      t->s[c - 1].rung = -1;
       continue;
     }
-    t->lo[c] = v[s].lo;
+    t->s[c].lo = v[s].lo;
     // Kernels test frac != 0 on its bit pattern (a scalar compare), so a
     // zero fraction is stored as +0.
-    t->frac[c] = v[s].frac == 0.f ? 0.f : v[s].frac;
-    t->mult[c] = 1.f;
-    t->rung[c] = v[s].rung;
+    t->s[c].frac = v[s].frac == 0.f ? 0.f : v[s].frac;
+    t->s[c].mult = 1.f;
+    t->s[c].rung = v[s].rung;
     ++c;
   }
   t->count = c;

@@ -164,7 +164,7 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
 #pragma unroll
   for (int r = 0; r < RPL; ++r) xacc[r] = yacc[r] = 0.f;
   // a slot whose dd this launch sums (uniform)
-  auto dd_slot = [&](int sj) { return want_dd && unsigned(st.rung[sj] - a.r0) < unsigned(RW_DD); };
+  auto dd_of = [&](const Slot& x) { return want_dd && unsigned(x.rung - a.r0) < unsigned(RW_DD); };
 
   const size_t kv_row = size_t(a.hkv) * D;
   const T* Kseq = K + size_t(b) * n * kv_row + size_t(g) * D;
@@ -177,15 +177,17 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
   int s = 0;
   const int S = st.count;
   while (s < S) {
-    const int lo0 = st.lo[s];
+    const Slot s0 = st.s[s];  // one 16-byte scalar load per slot record
+    const int lo0 = s0.lo;
     if (lo0 > i_last) break;
     // interpolated slots and dd slots read their second row i - lo - 1
-    int lomax = lo0 + ((st.frac[s] > 0.f || dd_slot(s)) ? 1 : 0);
+    int lomax = lo0 + ((s0.frac > 0.f || dd_of(s0)) ? 1 : 0);
     int e = s + 1;
     while (e < S) {
-      const int le = st.lo[e];
+      const Slot se = st.s[e];
+      const int le = se.lo;
       if (le > i_last) break;
-      const int need = max(lomax, le + ((st.frac[e] > 0.f || dd_slot(e)) ? 1 : 0));
+      const int need = max(lomax, le + ((se.frac > 0.f || dd_of(se)) ? 1 : 0));
       if (need - lo0 + BQ > CAP) break;
       lomax = need;
       ++e;
@@ -214,14 +216,15 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
     // K row r - 1 of the slot at lo = 0; a slot's rows are lo rows earlier.
     const float* const lane_kv = Ks + (i - r0 - 1) * KS + c * DC;
     for (int sj = s; sj < e; ++sj) {
-      const int lo = st.lo[sj];
+      const Slot cur = st.s[sj];  // one 16-byte scalar load
+      const int lo = cur.lo;
       // frac is +0 or positive: its bit pattern, read as an integer, decides
       // interpolation with a scalar compare.
-      const int wbits = reinterpret_cast<const int*>(st.frac)[sj];
+      const int wbits = __float_as_int(cur.frac);
       const float w = __int_as_float(wbits);
       const bool interp = wbits != 0;
       const float* const kp = lane_kv - lo * KS;  // K row r - 1
-      const bool dds = dd_slot(sj);
+      const bool dds = dd_of(cur);
       float kt[DC], vt[DC], dk[DC], dv[DC];
       load_vec<DC>(kp + KS, kt);
       load_vec<DC>(kp + KS + VOFF, vt);
@@ -312,7 +315,7 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
       if (dds) {
         const float X = active ? a.scale * p * sd : 0.f;
         const float Y = active ? p * fmaf(a.scale * dp, sd, vd) : 0.f;
-        const int rr = st.rung[sj] - a.r0;
+        const int rr = cur.rung - a.r0;
         if (ddu == (rr & (ND - 1))) {
           xacc[rr / ND] = X;
           yacc[rr / ND] = Y;
@@ -445,7 +448,17 @@ constexpr int key_cap(int kb) { return kb + 48; }
 // (staging q~) and dV (staging dO).  Words per staged row: the chunk of
 // every head as f16 head pairs, plus a 4-word pad against bank conflicts.
 constexpr int kKeyBlockH16 = 128;
-constexpr int key_half_row_words(int G, int D) { return key_chunk(D) * ((G + 1) / 2) + 4; }
+// Dims per bf16 key-pass tile (and per chunk of the packed rows the query
+// pass writes).  32-dim tiles at one head per KV head were measured slower
+// (Christoffel key pass 199 -> 263 us).
+constexpr int key_chunk_h16(int D, int G) { return key_chunk(D); }
+// Words per staged row: the chunk of every head as f16 head pairs (G >= 2,
+// one half of the pass per workgroup), or with one head per KV head the fp32
+// chunks of q~ and dO together (both halves in one workgroup); plus a 4-word
+// pad.
+constexpr int key_half_row_words(int G, int D) {
+  return G == 1 ? 2 * key_chunk_h16(D, G) + 4 : key_chunk_h16(D, G) * ((G + 1) / 2) + 4;
+}
 
 // Rows per stage of a bf16 key-pass half.  As many as let 16 waves per CU
 // share the 160 KiB of LDS, but at least the block plus 12 rows (a window
@@ -497,12 +510,12 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
   const int S = st.count;
   int s = 0;
   while (s < S) {
-    const int lo0 = st.lo[s];
+    const int lo0 = st.s[s].lo;
     if (j0 + lo0 > n - 1) break;  // no query at this distance for any key of the block
     int lomax = lo0;
     int e = s;
     while (e < S) {
-      const int le = st.lo[e];
+      const int le = st.s[e].lo;
       if (j0 + le > n - 1 || le - lo0 + KB + 1 > KCAP) break;
       lomax = le;
       ++e;
@@ -529,13 +542,13 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
     // (slot, tap) steps of this stage, with the workspace loads of the next
     // step issued before the current one is consumed.
     auto step_valid = [&](int sj, int tap) {
-      const float w = st.frac[sj];
-      const int i = j + st.lo[sj] + tap;
+      const float w = st.s[sj].frac;
+      const int i = j + st.s[sj].lo + tap;
       return activej && i >= 0 && i < n && (tap == 1 || j > 0 || w == 0.f);
     };
     auto load_step = [&](int sj, int tap, float (&pg)[G], float (&dpg)[G], float (&dvg)[G]) {
       if (step_valid(sj, tap)) {
-        const int i = j + st.lo[sj] + tap;
+        const int i = j + st.s[sj].lo + tap;
         const size_t widx = ((ws_seq + sj) * n + i) * G;
         load_vec<G>(a.P + widx, pg);
         load_vec<G>(a.dP + widx, dpg);
@@ -545,7 +558,7 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
         for (int h = 0; h < G; ++h) pg[h] = dpg[h] = dvg[h] = 0.f;
       }
     };
-    auto taps_of = [&](int sj) { return st.frac[sj] > 0.f ? 2 : 1; };
+    auto taps_of = [&](int sj) { return st.s[sj].frac > 0.f ? 2 : 1; };
 
     float pg[G], dpg[G], dvg[G];
     load_step(s, 0, pg, dpg, dvg);
@@ -559,8 +572,8 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
       float pn[G], dpn[G], dvn[G];
       if (nsj < e) load_step(nsj, ntap, pn, dpn, dvn);
 
-      const int lo = st.lo[sj];
-      const float w = st.frac[sj];
+      const int lo = st.s[sj].lo;
+      const float w = st.s[sj].frac;
       const int delta = lo + tap;
       const float wt = tap ? w : 1.f - w;
       const bool valid = step_valid(sj, tap);
@@ -625,21 +638,29 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
 // x), so each head sum is one v_dot2_f32_f16 per head pair and dim,
 // accumulated in fp32; dS and p enter as f16 pairs.  Half a row per
 // workgroup halves the LDS and registers per wave, so four waves share a
-// SIMD.  With
-// one head per KV head (G = 1) a pair would leave half of every f16 word
-// empty, so there the staged words hold the fp32 rows and the weights stay
-// fp32: one FMA per dim and step instead of a dot2 doing one useful MAC.
-// SMALL: at most 64 slots (one VGPR per slot-table column).
+// SIMD.  With one head per KV head (G = 1) a pair would leave half of every
+// f16 word empty, so there the staged words hold the fp32 rows and the
+// weights stay fp32 (one FMA per dim and step instead of a dot2 doing one
+// useful MAC), and PART 2 does both halves in one workgroup: a step is then
+// 32 FMAs (dK and dV) for one set of per-step bookkeeping (slot cursor,
+// weight loads, ring address), which is scalar work that otherwise bounds
+// the pass (more SALU than VALU instructions per wave with the halves
+// apart).  SMALL: at most 64 slots (one VGPR per slot-table column).
 template <int D, int G, int PART, bool SMALL>
 __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable& st, const int tile) {
   constexpr int KB = kKeyBlockH16;
-  constexpr int KC = key_chunk(D);
+  constexpr int KC = key_chunk_h16(D, G);
   constexpr int NCH = D / KC;
   constexpr int GW = (G + 1) / 2;  // head pairs
   constexpr int RW = key_half_row_words(G, D);
   constexpr int XH = KC / 8;       // 8-dim pieces per head chunk
-  constexpr int PPR = GW * XH;     // staging pieces per row
+  constexpr bool BOTH = PART == 2;  // dK and dV in one workgroup (G = 1)
+  static_assert(!BOTH || G == 1, "both halves only with one head per KV head");
+  constexpr int PPR = (BOTH ? 2 : GW) * XH;  // staging pieces per row
   constexpr int NQ = SMALL ? 1 : 3;  // VGPRs per slot-table column
+  // steps of weight loads in flight (2 and 4 were measured slower: the key
+  // pass is not bound by their latency)
+  constexpr int PF = 1;
   static_assert(KC % 8 == 0 && KB % PPR == 0, "8-dim pieces, whole rows per pass");
   // Dynamic LDS: a.kcap staged rows of RW words.
   extern __shared__ __align__(16) uint32_t key_smem[];
@@ -655,14 +676,16 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   const int j0 = blk * KB;
   const int j = j0 + tid;
   const bool activej = j < n;
-  const bool rope = PART == 0 && a.rope != nullptr;
+  const bool rope = PART != 1 && a.rope != nullptr;
 
-  const bf16_t* __restrict__ X = static_cast<const bf16_t*>(PART == 0 ? a.q : a.dout);
+  const bf16_t* __restrict__ X = static_cast<const bf16_t*>(PART == 1 ? a.dout : a.q);
   const size_t kv_off = (size_t(b) * n + j) * size_t(a.hkv) * D + size_t(g) * D + c * KC;
 
-  float acc[KC];
+  float acc[KC], accv[BOTH ? KC : 1];  // dK~ (or dV), and dV for BOTH
 #pragma unroll
   for (int x = 0; x < KC; ++x) acc[x] = 0.f;
+#pragma unroll
+  for (int x = 0; x < (BOTH ? KC : 1); ++x) accv[x] = 0.f;
 
   // The slot table lives in VGPRs for the loops (lane l holds slot l, then
   // l + 64 and l + 128) and is read with v_readlane: no scalar memory access
@@ -676,8 +699,8 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
     const int sl = q * 64 + lane;
     const bool in = sl < S;
     const int sc = in ? sl : 0;
-    const float fr = in ? st.frac[sc] : 0.f;
-    vlo[q] = in ? min(st.lo[sc], n) : n;
+    const float fr = in ? st.s[sc].frac : 0.f;
+    vlo[q] = in ? min(st.s[sc].lo, n) : n;
     vfr[q] = __float_as_int(fr);
     vtaps[q] = fr > 0.f ? 2 : 1;  // an interpolated slot has a second tap
   }
@@ -698,7 +721,8 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   // query pass wrote (a slot is only reached while j0 + lo <= n - 1).  A
   // step past the end reloads the last slot's rows; masked steps get zero
   // weights in convert().
-  constexpr int NR = PART == 0 ? 3 : 1;
+  constexpr int NR = PART == 1 ? 1 : 3;
+  constexpr int NWT = BOTH ? 2 : GW;  // weight words per step
   const float* __restrict__ Pseq = a.P + size_t(seq) * a.S * n * G;
   const float* __restrict__ dPseq = a.dP + size_t(seq) * a.S * n * G;
   const float* __restrict__ Dseq = a.Dvec + size_t(seq) * n * G;
@@ -706,42 +730,55 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   // fraction
   int fs = 0, ft = 0, flo = 0, ftaps = 1;
   float fw = 0.f;
+  // A queue entry: the loads of one (slot, tap) step and its weight factor,
+  // the tap weight wt (1 - frac for the nearer row, frac for the farther
+  // one) times the scale for dK, and 0 for a masked step.
+  struct QE {
+    float raw[NR][G];
+    float ws;
+  };
   // The three loads share the lane's 32-bit byte offset i * G * 4 from
   // uniform bases (the slot's planes of p and dp, and Dvec), so the address
   // arithmetic is scalar except for that offset.
-  auto load_step = [&](float (&raw)[NR][G]) {
+  auto load_step = [&](QE& q) {
     const int sc = fs < S ? fs : S - 1;
     const int i = min(max(j + flo + ft, 0), n - 1);
     const unsigned ioff = unsigned(i) * unsigned(G * 4);
     const float* pb = uniform_ptr(Pseq + size_t(sc) * n * G);
-    load_global_at<G>(pb, ioff, raw[0]);
-    if constexpr (PART == 0) {
+    load_global_at<G>(pb, ioff, q.raw[0]);
+    if constexpr (PART != 1) {
       const float* db = uniform_ptr(dPseq + size_t(sc) * n * G);
       const float* vb = uniform_ptr(Dseq);
-      load_global_at<G>(db, ioff, raw[1]);
-      load_global_at<G>(vb, ioff, raw[2]);
+      load_global_at<G>(db, ioff, q.raw[1]);
+      load_global_at<G>(vb, ioff, q.raw[2]);
     }
-  };
-  // f16 weight pairs of the cursor's step, times its tap weight wt (1 - frac
-  // for the nearer row, frac for the farther one): wt dS, dS = scale p (dp -
-  // Dvec), for dK, wt p for dV; zero for a masked step.
-  auto convert = [&](const float (&raw)[NR][G], uint32_t (&wts)[GW]) {
     const bool valid = fs < S && unsigned(j + flo + ft) < unsigned(n);
     const float wt = ft ? fw : 1.f - fw;
-    const float ws = PART == 0 ? a.scale * wt : wt;
+    q.ws = valid ? wt : 0.f;
+  };
+  // f16 weight pairs of a queued step (G = 1: one fp32 weight): ws dS, dS =
+  // p (dp - Dvec), for dK, ws p for dV.  Every loaded value is finite (a
+  // clamped row the query pass wrote), so a masked step's ws = 0 gives 0.
+  auto convert = [&](const QE& q, uint32_t (&wts)[NWT]) {
+    if constexpr (BOTH) {
+      const float p = q.ws * q.raw[0][0];
+      wts[0] = __float_as_uint(a.scale * p * (q.raw[1][0] - q.raw[2][0]));
+      wts[1] = __float_as_uint(p);
+    } else {
+      const float ws = PART == 0 ? a.scale * q.ws : q.ws;
 #pragma unroll
-    for (int hp = 0; hp < GW; ++hp) {
-      const int h0 = 2 * hp, h1 = 2 * hp + 1 < G ? 2 * hp + 1 : 2 * hp;
-      float w0 = raw[0][h0], w1 = 2 * hp + 1 < G ? raw[0][h1] : 0.f;
-      if constexpr (PART == 0) {
-        w0 = ws * w0 * (raw[1][h0] - raw[2][h0]);
-        w1 = ws * w1 * (raw[1][h1] - raw[2][h1]);
-      } else {
-        w0 *= ws;
-        w1 *= ws;
+      for (int hp = 0; hp < GW; ++hp) {
+        const int h0 = 2 * hp, h1 = 2 * hp + 1 < G ? 2 * hp + 1 : 2 * hp;
+        float w0 = q.raw[0][h0], w1 = 2 * hp + 1 < G ? q.raw[0][h1] : 0.f;
+        if constexpr (PART == 0) {
+          w0 = ws * w0 * (q.raw[1][h0] - q.raw[2][h0]);
+          w1 = ws * w1 * (q.raw[1][h1] - q.raw[2][h1]);
+        } else {
+          w0 *= ws;
+          w1 *= ws;
+        }
+        wts[hp] = G == 1 ? __float_as_uint(w0) : pack_h2(w0, w1);
       }
-      const uint32_t pk = G == 1 ? __float_as_uint(w0) : pack_h2(w0, w1);
-      wts[hp] = valid ? pk : 0u;
     }
   };
   // advance the cursor one step; it stays at (S, 0) once past the end
@@ -760,21 +797,24 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   };
 
   // Software pipeline along the (slot, tap) sequence, straight across stage
-  // boundaries: wts holds the f16 weights of the step being computed and raw
-  // the loads of the cursor's step, the one after it.  The end of each step
-  // converts those into the next weights and only then reuses the registers
-  // for the loads of the step after that, so every load has a whole step to
-  // arrive.
-  uint32_t wts[GW] = {};
-  float raw[NR][G];
+  // boundaries: wts holds the weights of the step being computed and the
+  // queue the loads of the PF steps after it (the cursor is the last of
+  // them).  The end of each step converts the queue's head into the next
+  // weights, shifts the queue and loads the step PF ahead, so every load has
+  // PF steps to arrive.
+  uint32_t wts[NWT] = {};
+  QE que[PF];
   if (S > 0) {
     flo = slot_i(vlo, 0);
     ftaps = slot_i(vtaps, 0);
     fw = __int_as_float(slot_i(vfr, 0));
-    load_step(raw);
-    convert(raw, wts);
-    advance();
-    load_step(raw);
+    load_step(que[0]);
+    convert(que[0], wts);
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      advance();
+      load_step(que[k]);
+    }
   }
   // The staged rows form a ring in LDS: query j0 + q sits in slot
   // (q - q0) mod kcap, q0 the first stage's first row.  Stages run in
@@ -861,17 +901,19 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
       // G = 1: fp32 words, converted here; dK rows are rotated by their own
       // position, R(i) q, on the way.  Batches of SB pieces: all their
       // global loads are issued before the first conversion.
-      constexpr int SB = PART == 0 ? 2 : 4;  // dK also holds rotary rows
+      constexpr int SB = PART == 1 ? 4 : 2;  // dK also holds rotary rows
       constexpr int RSTEP = KB / PPR;
       const int pc = tid % PPR;
-      const int hp = pc / XH;
+      const int hp = pc / XH;  // head pair; with BOTH: 0 stages q~, 1 dO
       const int xh = pc % XH;
-      const bool pair = 2 * hp + 1 < G;
+      const bool pair = !BOTH && 2 * hp + 1 < G;
+      const bool rot = rope && !(BOTH && hp == 1);  // q~ rows are rotated, dO rows not
+      const bf16_t* __restrict__ Xs = BOTH ? static_cast<const bf16_t*>(hp ? a.dout : a.q) : X;
       const size_t rstride = size_t(a.hq) * D;
       // addresses from signed row indices: rows < 0 with negative offsets
       const int rn = j0 + fnew;                   // query of the first new row
       const int64_t grow0 = int64_t(b) * n + rn;  // its global row
-      const size_t col = (size_t(g) * G + 2 * hp) * D + c * KC + xh * 8;
+      const size_t col = (size_t(g) * G + (BOTH ? 0 : 2 * hp)) * D + c * KC + xh * 8;
       uint32_t* dst0 = Ws + hp * KC + xh * 8;
       for (int row0 = tid / PPR; row0 < nnew; row0 += SB * RSTEP) {
         uint4 u0[SB], u1[SB];
@@ -884,10 +926,10 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
           // rows before the sequence (negative offsets) are staged as zeros;
           // masked steps read ring slot 0 with zero weights
           if (row < nnew && rn + row >= 0) {
-            const bf16_t* src = X + size_t(grow0 + row) * rstride + col;
+            const bf16_t* src = Xs + size_t(grow0 + row) * rstride + col;
             u0[u] = *reinterpret_cast<const uint4*>(src);
             if (pair) u1[u] = *reinterpret_cast<const uint4*>(src + D);
-            if (rope) {
+            if (rot) {
               const float* rp = a.rope + size_t(rn + row) * D + c * KC + xh * 8;
               ra[u] = *reinterpret_cast<const float4*>(rp);
               rb[u] = *reinterpret_cast<const float4*>(rp + 4);
@@ -907,7 +949,7 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
               // dims 2x, 2x + 1 of both heads: one rotation pair each
               float a0 = bf16_lo(e0[x]), b0 = bf16_hi(e0[x]);
               float a1 = bf16_lo(e1[x]), b1 = bf16_hi(e1[x]);
-              if (PART == 0) {
+              if (PART != 1) {  // rows that are not rotated carry the identity (cos 1, sin 0)
                 const float c_ = cs[2 * x], s_ = cs[2 * x + 1];
                 const float ra0 = a0 * c_ - b0 * s_, rb0 = a0 * s_ + b0 * c_;
                 const float ra1 = a1 * c_ - b1 * s_, rb1 = a1 * s_ + b1 * c_;
@@ -951,7 +993,18 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
         const unsigned roff = tid_b + unsigned(soff * RW * 4) - wrap;
         const uint32_t* rowp = reinterpret_cast<const uint32_t*>(
             reinterpret_cast<const char*>(Ws) + (valid ? roff : 0u));
-        if constexpr (G == 1) {
+        if constexpr (BOTH) {
+          // dK~ += (wt dS) q~ and dV += (wt p) dO
+          uint32_t xq[KC], xd[KC];
+          load_words<KC>(rowp, xq);
+          load_words<KC>(rowp + KC, xd);
+          const float wk = __uint_as_float(wts[0]), wv = __uint_as_float(wts[1]);
+#pragma unroll
+          for (int x = 0; x < KC; ++x) {
+            acc[x] = fmaf(wk, __uint_as_float(xq[x]), acc[x]);
+            accv[x] = fmaf(wv, __uint_as_float(xd[x]), accv[x]);
+          }
+        } else if constexpr (G == 1) {
           // acc += (wt w0) x
           uint32_t xw[KC];
           load_words<KC>(rowp, xw);
@@ -969,18 +1022,21 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
           }
         }
 
-        // weights of the next step, then the loads of the one after it
-        convert(raw, wts);
+        // weights of the next step, then the loads of the step PF ahead
+        convert(que[0], wts);
+#pragma unroll
+        for (int k = 0; k + 1 < PF; ++k) que[k] = que[k + 1];
         __builtin_amdgcn_sched_barrier(0);
         advance();
-        load_step(raw);
+        load_step(que[PF - 1]);
       }
     }
     s = e;
   }
   if (activej) {
     if (rope) rotate_pairs<KC, -1>(acc, a.rope + size_t(j) * D, c * KC);  // dK = R(j)^T dK~
-    store_vec<KC>(static_cast<bf16_t*>(PART == 0 ? a.dk : a.dv) + kv_off, acc);
+    store_vec<KC>(static_cast<bf16_t*>(PART == 1 ? a.dv : a.dk) + kv_off, acc);
+    if constexpr (BOTH) store_vec<KC>(static_cast<bf16_t*>(a.dv) + kv_off, accv);
   }
 }
 
@@ -990,11 +1046,15 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
 // pass 146 -> 137 us, Christoffel 298 -> 266 us against two launches).
 template <int D, int G, bool SMALL>
 __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_h16_kernel(BwdArgs a, SlotTable st) {
-  const int t2 = xcd_tile(blockIdx.x, 2 * a.tiles);
-  if (t2 < a.tiles)
-    key_half_body<D, G, 0, SMALL>(a, st, t2);
-  else
-    key_half_body<D, G, 1, SMALL>(a, st, t2 - a.tiles);
+  if constexpr (G == 1) {
+    key_half_body<D, 1, 2, SMALL>(a, st, xcd_tile(blockIdx.x, a.tiles));  // both halves
+  } else {
+    const int t2 = xcd_tile(blockIdx.x, 2 * a.tiles);
+    if (t2 < a.tiles)
+      key_half_body<D, G, 0, SMALL>(a, st, t2);
+    else
+      key_half_body<D, G, 1, SMALL>(a, st, t2 - a.tiles);
+  }
 }
 
 struct ReduceArgs {
@@ -1143,14 +1203,15 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
     constexpr int KB = kKeyBlockH16;
     a.nblk = (a.n + KB - 1) / KB;
-    a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk(D));
+    a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk_h16(D, G));
     a.kcap = key_half_cap(G, D);
     const size_t lds = size_t(a.kcap) * key_half_row_words(G, D) * 4;
     const bool small = t.count <= 64;
+    const int grid = G == 1 ? a.tiles : 2 * a.tiles;  // G = 1: both halves in each workgroup
     if (small)
-      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, true>), dim3(2 * a.tiles), dim3(KB), lds, st, a, t);
+      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, true>), dim3(grid), dim3(KB), lds, st, a, t);
     else
-      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, false>), dim3(2 * a.tiles), dim3(KB), lds, st, a, t);
+      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, false>), dim3(grid), dim3(KB), lds, st, a, t);
   } else {
     constexpr int KB = key_block(sizeof(T), G, D);
     a.nblk = (a.n + KB - 1) / KB;

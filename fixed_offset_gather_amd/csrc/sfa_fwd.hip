@@ -108,9 +108,9 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
   __shared__ float s_w[SFA_MAX_SLOTS];
   __shared__ float s_mult[SFA_MAX_SLOTS];
   for (int t = threadIdx.x; t < st.count; t += blockDim.x) {
-    s_lo[t] = st.lo[t];
-    s_w[t] = st.frac[t];
-    s_mult[t] = st.mult[t];
+    s_lo[t] = st.s[t].lo;
+    s_w[t] = st.s[t].frac;
+    s_mult[t] = st.s[t].mult;
   }
   __syncthreads();
 
@@ -146,14 +146,14 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
   int s = 0;
   const int S = st.count;
   while (s < S) {
-    const int lo0 = st.lo[s];
+    const int lo0 = st.s[s].lo;
     if (lo0 > i_last) break;  // this slot and all later ones are masked for the block
-    int lomax = lo0 + ((INTERP && st.frac[s] > 0.f) ? 1 : 0);
+    int lomax = lo0 + ((INTERP && st.s[s].frac > 0.f) ? 1 : 0);
     int e = s + 1;
     while (e < S) {
-      const int le = st.lo[e];
+      const int le = st.s[e].lo;
       if (le > i_last) break;
-      const int need = max(lomax, le + ((INTERP && st.frac[e] > 0.f) ? 1 : 0));
+      const int need = max(lomax, le + ((INTERP && st.s[e].frac > 0.f) ? 1 : 0));
       if (need - lo0 + BQ > CAP) break;
       lomax = need;
       ++e;
@@ -333,9 +333,9 @@ __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Sl
   __shared__ int s_wb[SFA_MAX_SLOTS];
   __shared__ float s_mult[SFA_MAX_SLOTS];
   for (int t = threadIdx.x; t < st.count; t += blockDim.x) {
-    s_lo[t] = st.lo[t];
-    s_wb[t] = __float_as_int(st.frac[t]);
-    s_mult[t] = st.mult[t];
+    s_lo[t] = st.s[t].lo;
+    s_wb[t] = __float_as_int(st.s[t].frac);
+    s_mult[t] = st.s[t].mult;
   }
   __syncthreads();
 
@@ -373,14 +373,14 @@ __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Sl
   int s = 0;
   const int S = st.count;
   while (s < S) {
-    const int lo0 = st.lo[s];
+    const int lo0 = st.s[s].lo;
     if (lo0 > i_last) break;
-    int lomax = lo0 + ((INTERP && st.frac[s] > 0.f) ? 1 : 0);
+    int lomax = lo0 + ((INTERP && st.s[s].frac > 0.f) ? 1 : 0);
     int e = s + 1;
     while (e < S) {
-      const int le = st.lo[e];
+      const int le = st.s[e].lo;
       if (le > i_last) break;
-      const int need = max(lomax, le + ((INTERP && st.frac[e] > 0.f) ? 1 : 0));
+      const int need = max(lomax, le + ((INTERP && st.s[e].frac > 0.f) ? 1 : 0));
       if (need - lo0 + BQH > CAP) break;
       lomax = need;
       ++e;
@@ -726,7 +726,7 @@ void launch_fwd_offsets_i(const SlotTable& t, const FwdArgs& a0, hipStream_t st)
 template <typename T, int D, int G>
 int launch_fwd_offsets_t(const Problem& p, const SlotTable& t, const FwdArgs& a, hipStream_t st) {
   bool interp = (p.flags & SFA_FLAG_INTERP_KERNEL) != 0;
-  for (int s = 0; s < t.count && !interp; ++s) interp = t.frac[s] > 0.f;
+  for (int s = 0; s < t.count && !interp; ++s) interp = t.s[s].frac > 0.f;
   if (interp)
     launch_fwd_offsets_i<T, D, G, true>(t, a, st);
   else

@@ -14,17 +14,22 @@ void clear_error();
 
 // Slot table handed to the shared-offset kernels by value.  Slots are the
 // window distances 0..W and the offsets, sorted by ascending lo (stable, the
-// window first on ties); rung[s] is the caller's offset index or -1.  With
+// window first on ties); rung is the caller's offset index or -1.  With
 // merging (forward only), slots naming the same (lo, frac) become one entry
-// of multiplicity mult[s]: its softmax weight is mult * exp(logit), exactly
-// the sum of the identical slots.
+// of multiplicity mult: its softmax weight is mult * exp(logit), exactly
+// the sum of the identical slots.  One 16-byte record per slot, so a kernel
+// reads a slot with one scalar load.
+struct Slot {
+  int32_t lo;
+  float frac;  // +0 for an integer slot (kernels test the bit pattern)
+  float mult;
+  int32_t rung;
+};
 struct SlotTable {
   int32_t count;
   int32_t n_rungs;
-  int32_t lo[SFA_MAX_SLOTS];
-  float frac[SFA_MAX_SLOTS];
-  float mult[SFA_MAX_SLOTS];
-  int32_t rung[SFA_MAX_SLOTS];  // 32-bit: kernels read it with scalar loads
+  int32_t pad_[2];
+  Slot s[SFA_MAX_SLOTS];
 };
 
 // Kernel launch parameters derived from sfa_attn after validation.
