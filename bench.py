@@ -6,7 +6,8 @@ alpha: the rung offsets for alpha (host producer), the forward over the
 window plus the 15 interpolated Fibonacci rungs (with LSE), and the backward
 (dQ, dK, dV, dd and dtheta).  Shape: 32 sequences x 1024 tokens (32,768
 tokens per batch), 8 query heads over 2 key/value heads, head dim 64, window
-10, RoPE 1e4, bf16 tensors with fp32 arithmetic.  Inputs are seeded N(0,1)
+10, RoPE 1e4, bf16 tensors; products on f16 operands in the forward and the
+key pass, on fp32 in the query pass, every sum in fp32.  Inputs are seeded N(0,1)
 and rotate over four resident sets (336 MB, more than the 256 MB Infinity
 Cache) so HBM, not the cache, serves them.
 
@@ -47,24 +48,30 @@ def log(*a):
 VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (packed FMA counted)
 
 
-def algorithmic_flops(B, n, hq, hkv, D, S, n_interp):
+def algorithmic_flops(B, n, hq, hkv, D, S, n_interp, n_dd=0):
     """FLOPs each kernel must do by definition, per launch: 2 S D per
     query-head for every dot product or weighted sum over the S slots (forward:
     logits and the value sum; query pass: logits, dp and dq; each key-pass
     pass: dK and dV), plus 6 D per (KV head, query, interpolated rung) for the
-    row interpolation (the key pass interpolates both its gathers)."""
+    row interpolation (the key pass interpolates both its gathers), plus, for
+    the offset gradient, 4 D per query-head and rung (q~ . dK and dO . dV)."""
     qh = B * n * hq
     lerp = 6 * D * n_interp * B * n * hkv
     return {
         "fwd_offsets": 4 * S * D * qh + lerp,
-        "bwd_query": 6 * S * D * qh + lerp,
+        "bwd_query": 6 * S * D * qh + lerp + 4 * D * n_dd * qh,
         "bwd_key": 4 * S * D * qh + 2 * lerp,
         "bwd_reduce": 0,
     }
 
 
 def algorithmic_bytes(B, n, hq, hkv, D, esize):
-    """Bytes each kernel must move by definition (every tensor once)."""
+    """Bytes each kernel must move by definition (every tensor once).
+
+    "step" is the metric's count for a training step: the forward reads Q, K,
+    V and writes O and LSE; the backward reads Q, K, V, O, dO and LSE and
+    writes dQ, dK and dV.  "step_without_o" leaves out the backward's read of
+    O, which this backward does not need (rowsum(dO * O) is recomputed)."""
     q = B * n * hq * D * esize
     kv = B * n * hkv * D * esize
     lse = B * n * hq * 4
@@ -77,7 +84,8 @@ def algorithmic_bytes(B, n, hq, hkv, D, esize):
         "bwd_key": 2 * q + 2 * kv + 2 * kv,
         "bwd_reduce": 0,
         # the step: forward + backward, each tensor once per pass
-        "step": (q + 2 * kv + q + lse) + (q + 2 * kv + q + lse + q + 2 * kv),
+        "step": (q + 2 * kv + q + lse) + (q + 2 * kv + q + q + lse + q + 2 * kv),
+        "step_without_o": (q + 2 * kv + q + lse) + (q + 2 * kv + q + lse + q + 2 * kv),
         # forward without LSE
         "fwd_only": q + 2 * kv + q,
     }
@@ -337,6 +345,26 @@ def main():
     esize = 2
     ab = algorithmic_bytes(B, n, hq, hkv, D, esize)
     step_gbs = ab["step"] / (ms_per_step * 1e-3) / 1e9
+
+    # Median of event-timed steps (torch's events on the stream the library
+    # launches on), at least 100 of them, beside the wall-clock mean above.
+    nev = max(100, args.steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
+    torch.cuda.synchronize()
+    for t in range(nev):
+        evs[t][0].record()
+        step(t)
+        evs[t][1].record()
+    torch.cuda.synchronize()
+    step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    step_events = {
+        "iterations": nev,
+        "median_ms": round(step_ms[nev // 2], 5),
+        "p10_ms": round(step_ms[nev // 10], 5),
+        "p90_ms": round(step_ms[(9 * nev) // 10], 5),
+        "median_queries_per_s": round(B * n / (step_ms[nev // 2] * 1e-3), 1),
+        "median_algorithmic_GBs": round(ab["step"] / (step_ms[nev // 2] * 1e-3) / 1e9, 1),
+    }
     log("kernel avg us:", {k_: round(v_["avg_us"], 2) for k_, v_ in kern.items()},
         "step ms %.4f" % ms_per_step, "%s in the timed region %.2f us" % (dom, dom_us))
 
@@ -356,7 +384,7 @@ def main():
     # intensity the backward kernels sit above the machine balance
     # (157.3 TFLOP/s / 8 TB/s), so this is the roofline that binds them.
     n_interp = sum(1 for f_ in frac if f_ > 0.0)
-    af = algorithmic_flops(B, n, hq, hkv, D, W + 1 + len(lo), n_interp)
+    af = algorithmic_flops(B, n, hq, hkv, D, W + 1 + len(lo), n_interp, n_dd=len(lo))
     dom_tf = af[dom] / (dom_us * 1e-6) / 1e12
     roofline["alu"] = {
         "achieved": round(dom_tf, 2),
@@ -459,11 +487,56 @@ def main():
     log("length extrapolation us:", {k_: (v_["integer"]["avg_us"], v_["learned"]["avg_us"])
                                      for k_, v_ in lengths.items()})
 
+    # The staggered page-1 forward over 16 layers: W in {6, 8, 10, 12} with
+    # the coprime schedule (16 alphas each), the power-of-2 base at W = 8
+    # under the same schedule and the plain alpha = 1 control: 81 calls.
+    ws_ = si.WORKLOADS["page1_staggered"]
+    c2 = []
+    for W_ in ws_["windows"]:
+        for layer in range(ws_["layers"]):
+            c2.append((W_, "fib", sfa.stagger_alpha("coprime", layer, ws_["layers"], ws_["stride"])))
+    for layer in range(ws_["layers"]):
+        c2.append((8, "pow2", sfa.stagger_alpha("coprime", layer, ws_["layers"], ws_["stride"])))
+    c2.append((8, "pow2", 1.0))
+    c2_us = []
+    for W_, basis, a_ in c2:
+        lo_c, fr_c = (sfa.offsets_fib if basis == "fib" else sfa.offsets_pow2)(a_)
+        for t in range(2):
+            q, k, v, _ = sets[t % NSETS]
+            sfa.fwd(q, k, v, W_, lo_c, fr_c, rope, out=o_buf)
+        torch.cuda.synchronize()
+        sfa.profile_reset()
+        sfa.profile_enable(True)
+        for t in range(5):
+            q, k, v, _ = sets[t % NSETS]
+            sfa.fwd(q, k, v, W_, lo_c, fr_c, rope, out=o_buf)
+        torch.cuda.synchronize()
+        sfa.profile_enable(False)
+        ms_, c_ = sfa.profile_read("fwd_offsets")
+        c2_us.append(1e3 * ms_ / c_)
+    c2_mean = sum(c2_us) / len(c2_us)
+    staggered_forward = {
+        "workload": "page1_staggered: 81 forward calls (16 coprime layers x W 6/8/10/12, power-of-2 base at W 8 "
+                    "over the same 16 layers, alpha = 1 control), 32 x 1024, 8/2 heads, D 64, bf16, RoPE 1e4",
+        "calls": len(c2_us),
+        "mean_us_per_call": round(c2_mean, 3),
+        "min_us": round(min(c2_us), 3),
+        "max_us": round(max(c2_us), 3),
+        "sum_us_all_calls": round(sum(c2_us), 1),
+        "queries_per_s_per_call": round(B * n / (c2_mean * 1e-6), 1),
+        "algorithmic_GBs": round(ab["fwd_only"] / (c2_mean * 1e-6) / 1e9, 1),
+        "frac_of_hbm_peak": round(ab["fwd_only"] / (c2_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "by_window_mean_us": {str(W_): round(sum(u for (w2, b2, _), u in zip(c2, c2_us) if w2 == W_ and b2 == "fib")
+                                             / ws_["layers"], 3) for W_ in ws_["windows"]},
+        "pow2_w8_mean_us": round(sum(u for (w2, b2, _), u in zip(c2, c2_us) if b2 == "pow2") / (ws_["layers"] + 1), 3),
+    }
+    log("staggered forward: mean %.2f us per call over %d calls" % (c2_mean, len(c2_us)))
+
     # Page 3's Christoffel layer trained: forward with LSE + backward (no
     # offset gradient) at context 2048, 8 x 2048 tokens, 4/4 heads, no
     # rotation; views of the resident tensors.  Causal: self + 128
     # carry-word offsets (m = 128, k = 1024).  Bidirectional by signed
-    # offsets: self + -O and +O of m = 64, k = 512, the same 129 slots.
+    # offsets: self + -O and +O of the same m = 128, k = 1024 (257 slots).
     wc = si.WORKLOADS["ctx2048_christoffel"]
     Bc, nc, hc = wc["batch"], wc["seqlen"], wc["hq"]
     ne = Bc * nc * hc * D
@@ -503,14 +576,22 @@ def main():
             ms_, c_ = sfa.profile_read(name)
             if c_:
                 ck[name] = round(1e3 * ms_ / c_, 3)
-        return {"slots": 1 + len(offs), "ms_per_step": round(1e3 * cwall / args.steps, 4),
-                "queries_per_s": round(Bc * nc / (cwall / args.steps), 1), "kernels_avg_us": ck}
+        S_ = 1 + len(offs)
+        fwd_flops = 4 * S_ * D * Bc * nc * hc  # logits and value sum, 2 S D each per query-head
+        fwd_bytes = 4 * ne * 2 + Bc * hc * nc * 4  # Q, K, V read, O written (bf16), LSE
+        fu = ck.get("fwd_offsets", float("nan"))
+        return {"slots": S_, "ms_per_step": round(1e3 * cwall / args.steps, 4),
+                "queries_per_s": round(Bc * nc / (cwall / args.steps), 1), "kernels_avg_us": ck,
+                "fwd_alu": {"flops_per_launch": fwd_flops, "achieved_TFLOPs": round(fwd_flops / (fu * 1e-6) / 1e12, 2),
+                            "frac_of_valu_peak": round(fwd_flops / (fu * 1e-6) / 1e12 / VALU_PEAK_TFLOPS, 4)},
+                "fwd_hbm": {"bytes_per_launch": fwd_bytes, "achieved_GBs": round(fwd_bytes / (fu * 1e-6) / 1e9, 1),
+                            "frac_of_hbm_peak": round(fwd_bytes / (fu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
 
     christoffel_step = {
         "workload": "ctx2048_christoffel: 8 x 2048, 4/4 heads, D 64, bf16, no rotation, forward with LSE + "
                     "backward without dd",
         "causal_m128_k1024": time_christoffel(sfa.offsets_christoffel(wc["m"], wc["k"]), False),
-        "bidirectional_signed_m64_k512": time_christoffel(sfa.offsets_christoffel_signed(64, 512), True),
+        "bidirectional_signed_m128_k1024": time_christoffel(sfa.offsets_christoffel_signed(wc["m"], wc["k"]), True),
     }
     log("christoffel steps:", {k_: v_["ms_per_step"] for k_, v_ in christoffel_step.items() if k_ != "workload"})
 
@@ -547,9 +628,13 @@ def main():
         ms_, c_ = sfa.profile_read(name)
         if c_:
             pk[name] = round(1e3 * ms_ / c_, 3)
+    fe_us = pk.get("fwd_edges", float("nan"))
+    fe_bytes = 4 * ne * 2 + Bc * hc * nc * 4 + e_h.nbytes + c_h.nbytes  # Q, K, V, O, LSE and the lists
     powerlaw_step = {
         "workload": "ctx2048_powerlaw: 8 x 2048, 4/4 heads, D 64, bf16, 64-wide bidirectional edge lists "
                     "(mean %.1f keys), forward with LSE + backward" % float(c_h.mean()),
+        "fwd_hbm": {"bytes_per_launch": int(fe_bytes), "achieved_GBs": round(fe_bytes / (fe_us * 1e-6) / 1e9, 1),
+                    "frac_of_hbm_peak": round(fe_bytes / (fe_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "ms_per_step": round(1e3 * pwall / args.steps, 4),
         "queries_per_s": round(Bc * nc / (pwall / args.steps), 1),
         "kernels_avg_us": pk,
@@ -568,7 +653,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16 in/out; f16 and f32 operands; f32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": "page1_learned_step",
@@ -576,13 +661,17 @@ def main():
             "rungs": "fibonacci x alpha (interpolated)", "alpha": alpha, "rope_theta": w["rope_theta"],
             "io_dtype": "bf16", "global_batch_tokens": B * n, "parallelism": "single-gpu",
         },
+        "step_algorithmic_bytes": ab["step"],
         "step_algorithmic_GBs": round(step_gbs, 1),
         "step_frac_of_hbm_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_bytes_without_o_read": ab["step_without_o"],
+        "step_events": step_events,
         # (not in counter runs: its copies would join the calibration copy's)
         "hbm_copy_GBs": None if args.calibrate_copy else copy_bandwidth_gbs(),
         "kernels_avg_us": {k_: round(v_["avg_us"], 3) for k_, v_ in kern.items()},
         "roofline": roofline,
         "fwd_only": fwd_only,
+        "staggered_forward": staggered_forward,
         "integer_vs_learned": integer_vs_learned,
         "christoffel_step": christoffel_step,
         "powerlaw_step": powerlaw_step,

@@ -41,8 +41,8 @@ SFA_F32 = 0
 SFA_BF16 = 1
 SFA_FLAG_INTERP_KERNEL = 1
 SFA_FLAG_SIGNED_OFFSETS = 2
-MAX_OFFSETS = 128
-MAX_SLOTS = 192
+MAX_OFFSETS = 256
+MAX_SLOTS = 320
 NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 SCHEDULES = {"fixed": 0, "linear": 1, "coprime": 2}
 

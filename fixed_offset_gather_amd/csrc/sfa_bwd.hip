@@ -657,7 +657,7 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   constexpr bool BOTH = PART == 2;  // dK and dV in one workgroup (G = 1)
   static_assert(!BOTH || G == 1, "both halves only with one head per KV head");
   constexpr int PPR = (BOTH ? 2 : GW) * XH;  // staging pieces per row
-  constexpr int NQ = SMALL ? 1 : 3;  // VGPRs per slot-table column
+  constexpr int NQ = SMALL ? 1 : (SFA_MAX_SLOTS + 63) / 64;  // VGPRs per slot-table column
   // steps of weight loads in flight (2 and 4 were measured slower: the key
   // pass is not bound by their latency)
   constexpr int PF = 1;
@@ -688,9 +688,11 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   for (int x = 0; x < (BOTH ? KC : 1); ++x) accv[x] = 0.f;
 
   // The slot table lives in VGPRs for the loops (lane l holds slot l, then
-  // l + 64 and l + 128) and is read with v_readlane: no scalar memory access
-  // inside the loops, whose waits would also drain the LDS reads (both count
-  // on lgkmcnt, and scalar loads return out of order).
+  // l + 64, l + 128, ...) and is read with v_readlane: no scalar memory
+  // access inside the loops, whose waits would also drain the LDS reads (both
+  // count on lgkmcnt, and scalar loads return out of order).  A column is
+  // picked with vector selects and read with one v_readlane (vector work:
+  // the scalar unit is the busier one in this pass).
   const int S = st.count;
   const int lane = tid & 63;
   int vlo[NQ], vfr[NQ], vtaps[NQ];
@@ -708,11 +710,7 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
     if constexpr (SMALL) {
       return __builtin_amdgcn_readlane(v[0], sj);
     } else {
-      const int l = sj & 63;
-      const int x0 = __builtin_amdgcn_readlane(v[0], l);
-      const int x1 = __builtin_amdgcn_readlane(v[1], l);
-      const int x2 = __builtin_amdgcn_readlane(v[2], l);
-      return sj < 64 ? x0 : (sj < 128 ? x1 : x2);
+      return __builtin_amdgcn_readlane(v[sj >> 6], sj & 63);  // uniform column index
     }
   };
 

@@ -104,9 +104,11 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
 
   // Slot table copied to LDS once: the hot loops read it with uniform
   // addresses instead of scalar loads from the kernel arguments.
-  __shared__ int s_lo[SFA_MAX_SLOTS];
-  __shared__ float s_w[SFA_MAX_SLOTS];
-  __shared__ float s_mult[SFA_MAX_SLOTS];
+  // (dynamic LDS of 3 x count words, so a short table takes little LDS)
+  extern __shared__ __align__(16) int fwd_slot_smem[];
+  int* const s_lo = fwd_slot_smem;
+  float* const s_w = reinterpret_cast<float*>(fwd_slot_smem + st.count);
+  float* const s_mult = reinterpret_cast<float*>(fwd_slot_smem + 2 * st.count);
   for (int t = threadIdx.x; t < st.count; t += blockDim.x) {
     s_lo[t] = st.s[t].lo;
     s_w[t] = st.s[t].frac;
@@ -329,9 +331,12 @@ __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Sl
   // The fraction is kept as its bit pattern: frac is +0 or positive, so the
   // bits read as a non-negative integer decide interpolation with scalar
   // integer operations.
-  __shared__ int s_lo[SFA_MAX_SLOTS];
-  __shared__ int s_wb[SFA_MAX_SLOTS];
-  __shared__ float s_mult[SFA_MAX_SLOTS];
+  // (dynamic LDS of 3 x count words: the page-1 table takes 312 bytes, so
+  // four workgroups still share a CU)
+  extern __shared__ __align__(16) int fwd_slot_smem[];
+  int* const s_lo = fwd_slot_smem;
+  int* const s_wb = fwd_slot_smem + st.count;
+  float* const s_mult = reinterpret_cast<float*>(fwd_slot_smem + 2 * st.count);
   for (int t = threadIdx.x; t < st.count; t += blockDim.x) {
     s_lo[t] = st.s[t].lo;
     s_wb[t] = __float_as_int(st.s[t].frac);
@@ -711,11 +716,12 @@ void launch_fwd_offsets_i(const SlotTable& t, const FwdArgs& a0, hipStream_t st)
     a.nblk = (a.n + BQH - 1) / BQH;
     a.tiles = a.nblk * a.tiles_per_blk;
     hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, BQH, kCap, INTERP>),
-                       dim3(a.tiles), dim3(BQH * LPQ), 0, st, a, t);
+                       dim3(a.tiles), dim3(BQH * LPQ), 3 * 4 * t.count, st, a, t);
   } else {
     constexpr int LPQ = fwd_lpq<D, G>();
     const FwdArgs& a = a0;
-    hipLaunchKernelGGL((fwd_offsets_kernel<T, D, G, LPQ, kCap, INTERP>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a,
+    hipLaunchKernelGGL((fwd_offsets_kernel<T, D, G, LPQ, kCap, INTERP>), dim3(a.tiles), dim3(BQ * LPQ),
+                       3 * 4 * t.count, st, a,
                        t);
   }
 }

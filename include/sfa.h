@@ -66,8 +66,8 @@ extern "C" {
  * not supported and is not checked.
  */
 
-#define SFA_MAX_OFFSETS 128 /* shared offsets per call */
-#define SFA_MAX_SLOTS 192   /* window + 1 + offsets */
+#define SFA_MAX_OFFSETS 256 /* shared offsets per call (page 3's m = 128, k = 1024 made bidirectional) */
+#define SFA_MAX_SLOTS 320   /* window + 1 + offsets */
 #define SFA_MAX_EDGE_WIDTH 256
 
 #define SFA_SCHEDULE_FIXED 0

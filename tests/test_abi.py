@@ -133,7 +133,8 @@ def _fwd(a, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None):
     (dict(head_dim=48), sfa.SFA_ERR_UNSUPPORTED),
     (dict(dtype=7), sfa.SFA_ERR_ARG),
     (dict(window=-1), sfa.SFA_ERR_ARG),
-    (dict(window=191, lo=[1], frac=[0.0]), sfa.SFA_ERR_UNSUPPORTED),
+    (dict(window=319, lo=[1], frac=[0.0]), sfa.SFA_ERR_UNSUPPORTED),
+    (dict(lo=list(range(257)), frac=[0.0] * 257), sfa.SFA_ERR_UNSUPPORTED),
     (dict(lo=[1, -2], frac=[0.0, 0.0]), sfa.SFA_ERR_ARG),
     (dict(lo=[1], frac=[1.0]), sfa.SFA_ERR_ARG),
     (dict(lo=[1], frac=[float("nan")]), sfa.SFA_ERR_ARG),

@@ -546,13 +546,17 @@ def test_negative_interpolated_offsets(dtype):
     _bwd_check(case, 2, lo, fr, 1.0, np.array([5, 2, 3], dtype=np.int32), signed=True)
 
 
-def test_bidirectional_christoffel_full_size():
-    # m = 64, k = 512 made bidirectional: 128 signed offsets + self, the same
-    # 129 slots as the causal m = 128 layer; context 2048, sequence 0 of 8.
+@pytest.mark.parametrize("m,k", [(128, 1024), (64, 512)])
+def test_bidirectional_christoffel_full_size(m, k):
+    # Page 3's example m = 128, k = 1024 made bidirectional: 256 signed
+    # offsets + self = 257 slots (more than five 64-slot columns of the key
+    # pass's slot table); and m = 64, k = 512 (129 slots).  Context 2048,
+    # sequence 0 of 8.
     sfa = _sfa()
     w = si.WORKLOADS["ctx2048_christoffel"]
     case = Case(w["batch"], w["seqlen"], w["hq"], w["hkv"], w["head_dim"], w["dtype"], rope_theta=0.0)
-    offs = sfa.offsets_christoffel_signed(64, 512)
+    offs = sfa.offsets_christoffel_signed(m, k)
+    assert len(offs) == 2 * m
     fr = np.zeros(len(offs), dtype=np.float32)
     _fwd_check(case, 0, offs, fr, sel=slice(0, 1), signed=True)
     _bwd_check(case, 0, offs, fr, None, None, sel=slice(0, 1), want_dd=False, signed=True)
