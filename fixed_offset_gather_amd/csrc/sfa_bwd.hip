@@ -462,8 +462,10 @@ constexpr int key_half_row_words(int G, int D) {
 
 // Rows per stage of a bf16 key-pass half.  As many as let 16 waves per CU
 // share the 160 KiB of LDS, but at least the block plus 12 rows (a window
-// of 10 and the interpolation tap in one stage) and at most the block plus
-// 64.
+// of 10 and the interpolation tap in one stage; with offsets 8 apart, as in
+// page 3's layer, two offsets per stage: a capacity of the block plus 7
+// measured 163 against 160 us causal and 433 against 349 us bidirectional)
+// and at most the block plus 64.
 inline int key_half_cap(int G, int D) {
   constexpr int kb = kKeyBlockH16, nw = kb / 64;
   const int budget = 163840 * nw / 16;
@@ -645,8 +647,8 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
 // 32 FMAs (dK and dV) for one set of per-step bookkeeping (slot cursor,
 // weight loads, ring address), which is scalar work that otherwise bounds
 // the pass (more SALU than VALU instructions per wave with the halves
-// apart).  SMALL: at most 64 slots (one VGPR per slot-table column).
-template <int D, int G, int PART, bool SMALL>
+// apart).
+template <int D, int G, int PART>
 __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable& st, const int tile) {
   constexpr int KB = kKeyBlockH16;
   constexpr int KC = key_chunk_h16(D, G);
@@ -657,7 +659,6 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   constexpr bool BOTH = PART == 2;  // dK and dV in one workgroup (G = 1)
   static_assert(!BOTH || G == 1, "both halves only with one head per KV head");
   constexpr int PPR = (BOTH ? 2 : GW) * XH;  // staging pieces per row
-  constexpr int NQ = SMALL ? 1 : (SFA_MAX_SLOTS + 63) / 64;  // VGPRs per slot-table column
   // steps of weight loads in flight (2 and 4 were measured slower: the key
   // pass is not bound by their latency)
   constexpr int PF = 1;
@@ -665,6 +666,7 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   // Dynamic LDS: a.kcap staged rows of RW words.
   extern __shared__ __align__(16) uint32_t key_smem[];
   uint32_t* Ws = key_smem;
+  constexpr int NQ = (SFA_MAX_SLOTS + 63) / 64;  // slot-table columns of 64 slots
 
   const int tid = threadIdx.x;
   const int c = tile % NCH;
@@ -687,32 +689,29 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
 #pragma unroll
   for (int x = 0; x < (BOTH ? KC : 1); ++x) accv[x] = 0.f;
 
-  // The slot table lives in VGPRs for the loops (lane l holds slot l, then
-  // l + 64, l + 128, ...) and is read with v_readlane: no scalar memory
-  // access inside the loops, whose waits would also drain the LDS reads (both
-  // count on lgkmcnt, and scalar loads return out of order).  A column is
-  // picked with vector selects and read with one v_readlane (vector work:
-  // the scalar unit is the busier one in this pass).
+  // The slot table lives in VGPRs (lane l holds slot l of each 64-slot
+  // column) and is read with v_readlane: no scalar memory access inside the
+  // step loop, whose waits would also drain the LDS reads (both count on
+  // lgkmcnt, and scalar loads return out of order).  Per slot: 2 min(lo, n)
+  // + taps - 1 (|lo| < 2^30, so the doubling fits) and the fraction bits.
+  // Only the prefetch cursor reads it, in slot order: it reads column 0 and
+  // shifts the columns down by one when it crosses into the next (static
+  // register indices only).  The step loop takes each step's row delta and
+  // slot from the queue entry the cursor filled; the stage bounds read the
+  // kernel-argument table between barriers.
   const int S = st.count;
   const int lane = tid & 63;
-  int vlo[NQ], vfr[NQ], vtaps[NQ];
+  int vpk[NQ], vfr[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int sl = q * 64 + lane;
     const bool in = sl < S;
     const int sc = in ? sl : 0;
     const float fr = in ? st.s[sc].frac : 0.f;
-    vlo[q] = in ? min(st.s[sc].lo, n) : n;
+    vpk[q] = 2 * (in ? min(st.s[sc].lo, n) : n) + (fr > 0.f ? 1 : 0);
     vfr[q] = __float_as_int(fr);
-    vtaps[q] = fr > 0.f ? 2 : 1;  // an interpolated slot has a second tap
   }
-  auto slot_i = [&](const int (&v)[NQ], int sj) {  // sj wave-uniform, < 64 * NQ
-    if constexpr (SMALL) {
-      return __builtin_amdgcn_readlane(v[0], sj);
-    } else {
-      return __builtin_amdgcn_readlane(v[sj >> 6], sj & 63);  // uniform column index
-    }
-  };
+  auto slot_lo = [&](int sj) { return min(st.s[sj].lo, n); };  // stage bounds only
 
   // p (and for dK dp and Dvec) of one (slot, tap) step, loaded without a
   // branch: the row is clamped to n - 1, and every clamped row is one the
@@ -721,38 +720,44 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   // weights in convert().
   constexpr int NR = PART == 1 ? 1 : 3;
   constexpr int NWT = BOTH ? 2 : GW;  // weight words per step
-  const float* __restrict__ Pseq = a.P + size_t(seq) * a.S * n * G;
-  const float* __restrict__ dPseq = a.dP + size_t(seq) * a.S * n * G;
-  const float* __restrict__ Dseq = a.Dvec + size_t(seq) * n * G;
-  // the prefetch cursor: step (fs, ft) and its slot's min(lo, n), taps and
-  // fraction
+  // Scalar bases of this sequence's p, dp and Dvec; a slot's plane is a
+  // scalar byte offset from them (advanced by one plane per slot), the row a
+  // 32-bit lane offset.
+  const float* const Pseq = uniform_ptr(a.P + size_t(seq) * a.S * n * G);
+  const float* const dPseq = uniform_ptr(a.dP + size_t(seq) * a.S * n * G);
+  const float* const Dseq = uniform_ptr(a.Dvec + size_t(seq) * n * G);
+  const unsigned plane_b = unsigned(n) * unsigned(G * 4);
+  // the prefetch cursor: step (fs, ft), its slot's min(lo, n), taps and
+  // fraction, and the byte offset of its slot's plane (kept at the last
+  // slot once past the end)
   int fs = 0, ft = 0, flo = 0, ftaps = 1;
   float fw = 0.f;
-  // A queue entry: the loads of one (slot, tap) step and its weight factor,
-  // the tap weight wt (1 - frac for the nearer row, frac for the farther
-  // one) times the scale for dK, and 0 for a masked step.
+  unsigned fplane = 0;
+  // A queue entry: the loads of one (slot, tap) step, its weight factor
+  // (the tap weight wt, 1 - frac for the nearer row and frac for the farther
+  // one, or 0 for a masked step), its slot (S past the end) and its row
+  // delta lo + tap.
   struct QE {
     float raw[NR][G];
     float ws;
+    int slot, delta;
   };
   // The three loads share the lane's 32-bit byte offset i * G * 4 from
   // uniform bases (the slot's planes of p and dp, and Dvec), so the address
   // arithmetic is scalar except for that offset.
   auto load_step = [&](QE& q) {
-    const int sc = fs < S ? fs : S - 1;
     const int i = min(max(j + flo + ft, 0), n - 1);
     const unsigned ioff = unsigned(i) * unsigned(G * 4);
-    const float* pb = uniform_ptr(Pseq + size_t(sc) * n * G);
-    load_global_at<G>(pb, ioff, q.raw[0]);
+    load_global_at<G>(Pseq, fplane + ioff, q.raw[0]);
     if constexpr (PART != 1) {
-      const float* db = uniform_ptr(dPseq + size_t(sc) * n * G);
-      const float* vb = uniform_ptr(Dseq);
-      load_global_at<G>(db, ioff, q.raw[1]);
-      load_global_at<G>(vb, ioff, q.raw[2]);
+      load_global_at<G>(dPseq, fplane + ioff, q.raw[1]);
+      load_global_at<G>(Dseq, ioff, q.raw[2]);
     }
     const bool valid = fs < S && unsigned(j + flo + ft) < unsigned(n);
     const float wt = ft ? fw : 1.f - fw;
     q.ws = valid ? wt : 0.f;
+    q.slot = fs;
+    q.delta = flo + ft;
   };
   // f16 weight pairs of a queued step (G = 1: one fp32 weight): ws dS, dS =
   // p (dp - Dvec), for dK, ws p for dV.  Every loaded value is finite (a
@@ -780,6 +785,19 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
     }
   };
   // advance the cursor one step; it stays at (S, 0) once past the end
+  auto set_cursor_slot = [&]() {  // fs < S
+    if ((fs & 63) == 0 && fs > 0) {  // into the next column: shift them down
+#pragma unroll
+      for (int q = 0; q + 1 < NQ; ++q) {
+        vpk[q] = vpk[q + 1];
+        vfr[q] = vfr[q + 1];
+      }
+    }
+    const int x = __builtin_amdgcn_readlane(vpk[0], fs & 63);
+    flo = x >> 1;
+    ftaps = (x & 1) + 1;
+    fw = ftaps > 1 ? __int_as_float(__builtin_amdgcn_readlane(vfr[0], fs & 63)) : 0.f;
+  };
   auto advance = [&]() {
     if (ft + 1 < ftaps) {
       ++ft;
@@ -787,9 +805,8 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
       ++fs;
       ft = 0;
       if (fs < S) {
-        flo = slot_i(vlo, fs);
-        ftaps = slot_i(vtaps, fs);
-        fw = __int_as_float(slot_i(vfr, fs));
+        set_cursor_slot();
+        fplane += plane_b;
       }
     }
   };
@@ -801,13 +818,14 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   // weights, shifts the queue and loads the step PF ahead, so every load has
   // PF steps to arrive.
   uint32_t wts[NWT] = {};
+  int wslot = S, wdelta = 0;  // slot and row delta of the step being computed
   QE que[PF];
   if (S > 0) {
-    flo = slot_i(vlo, 0);
-    ftaps = slot_i(vtaps, 0);
-    fw = __int_as_float(slot_i(vfr, 0));
+    set_cursor_slot();
     load_step(que[0]);
     convert(que[0], wts);
+    wslot = que[0].slot;
+    wdelta = que[0].delta;
 #pragma unroll
     for (int k = 0; k < PF; ++k) {
       advance();
@@ -830,12 +848,12 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   bool first_stage = true;
   int s = 0;
   while (s < S) {
-    const int lo0 = slot_i(vlo, s);
+    const int lo0 = slot_lo(s);
     if (j0 + lo0 > n - 1) break;
     int lomax = lo0;
     int e = s;
     while (e < S) {
-      const int le = slot_i(vlo, e);
+      const int le = slot_lo(e);
       if (j0 + le > n - 1 || le - lo0 + KB + 1 > kcap) break;
       lomax = le;
       ++e;
@@ -973,11 +991,10 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
     __syncthreads();
     have_hi = max(have_hi, hi);
 
-    for (int sj = s; sj < e; ++sj) {
-      const int lo = slot_i(vlo, sj);
-      const int ntaps = slot_i(vtaps, sj);
-      for (int tap = 0; tap < ntaps; ++tap) {
-        const int delta = lo + tap;
+    // every step of the slots [s, e): the steps are in slot order
+    while (wslot < e) {
+      {
+        const int delta = wdelta;
         // Query j + delta; the query pass stored p = 0 where the slot has no
         // row for it.  Masked steps read ring slot 0 with zero weights.
         // The tap weight (1 - frac or frac) is already in the step's
@@ -1022,6 +1039,8 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
 
         // weights of the next step, then the loads of the step PF ahead
         convert(que[0], wts);
+        wslot = que[0].slot;
+        wdelta = que[0].delta;
 #pragma unroll
         for (int k = 0; k + 1 < PF; ++k) que[k] = que[k + 1];
         __builtin_amdgcn_sched_barrier(0);
@@ -1042,16 +1061,16 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
 // tiles, dispatched in that order, so dV workgroups start on the CUs that
 // dK workgroups leave instead of waiting for the slowest of them (page-1 key
 // pass 146 -> 137 us, Christoffel 298 -> 266 us against two launches).
-template <int D, int G, bool SMALL>
+template <int D, int G>
 __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_h16_kernel(BwdArgs a, SlotTable st) {
   if constexpr (G == 1) {
-    key_half_body<D, 1, 2, SMALL>(a, st, xcd_tile(blockIdx.x, a.tiles));  // both halves
+    key_half_body<D, 1, 2>(a, st, xcd_tile(blockIdx.x, a.tiles));  // both halves
   } else {
     const int t2 = xcd_tile(blockIdx.x, 2 * a.tiles);
     if (t2 < a.tiles)
-      key_half_body<D, G, 0, SMALL>(a, st, t2);
+      key_half_body<D, G, 0>(a, st, t2);
     else
-      key_half_body<D, G, 1, SMALL>(a, st, t2 - a.tiles);
+      key_half_body<D, G, 1>(a, st, t2 - a.tiles);
   }
 }
 
@@ -1204,12 +1223,8 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
     a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk_h16(D, G));
     a.kcap = key_half_cap(G, D);
     const size_t lds = size_t(a.kcap) * key_half_row_words(G, D) * 4;
-    const bool small = t.count <= 64;
     const int grid = G == 1 ? a.tiles : 2 * a.tiles;  // G = 1: both halves in each workgroup
-    if (small)
-      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, true>), dim3(grid), dim3(KB), lds, st, a, t);
-    else
-      hipLaunchKernelGGL((bwd_key_h16_kernel<D, G, false>), dim3(grid), dim3(KB), lds, st, a, t);
+    hipLaunchKernelGGL((bwd_key_h16_kernel<D, G>), dim3(grid), dim3(KB), lds, st, a, t);
   } else {
     constexpr int KB = key_block(sizeof(T), G, D);
     a.nblk = (a.n + KB - 1) / KB;
