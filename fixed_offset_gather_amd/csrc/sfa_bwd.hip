@@ -87,11 +87,13 @@ __device__ __forceinline__ float own_dot(const float (&a)[G][DC], const float (&
 // bit-identical dot sums after the reduce-scatter; rung r of the launch's
 // window [a.r0, a.r0 + RPL * ND) is kept by the duplicate lane u = (r - r0)
 // % ND in register (r - r0) / ND.
-// The LDS of two workgroups fits a CU, and with G <= 4 their 16 waves fit
-// the register file when a lane stays within 128 VGPRs: ask for that.
+// The LDS of two workgroups fits a CU, and at four heads per KV head their
+// 16 waves fit the register file when a lane stays within 128 VGPRs (the
+// offset-gradient registers would otherwise take it to 134): ask for that.
+// Other group sizes fit (G <= 2) or do not come close (G = 8) without it.
 template <int G>
 constexpr int bwd_query_waves_per_eu() {
-  return G <= 4 ? 4 : 1;
+  return G == 4 ? 4 : 1;
 }
 template <typename T, int D, int G, int LPQ, int CAP, int BQ, int RPL>
 __global__ __launch_bounds__(BQ* LPQ) __attribute__((amdgpu_waves_per_eu(bwd_query_waves_per_eu<G>())))

@@ -1,0 +1,316 @@
+"""Host model of the index arithmetic of the HIP kernels (test infrastructure).
+
+Each function below walks one kernel of fixed_offset_gather_amd/csrc the way
+the kernel walks its work: the slot-table order and stage grouping, the LDS
+rows a stage stages and the rows each lane then reads, the LDS ring of the
+bf16 key pass (which slot holds which query row), the rotary-table rows and
+the workspace offsets.  Lanes are numpy vectors, one element per thread, so a
+whole workgroup is checked at once.  Every address is checked against the
+buffer it indexes (raising IndexModelError), and ring reads are checked to
+find the row they expect.  The model follows the kernels' source: a change to
+their index arithmetic must be made here too (the kernel functions are named
+in each docstring).  It computes nothing of the attention itself.
+"""
+
+import numpy as np
+
+MAX_SLOTS = 320
+BQ_FWD_F32 = 64      # sfa_fwd.hip: BQ
+CAP = 128            # sfa_fwd.hip / sfa_bwd.hip: kCap
+KB_H16 = 128         # sfa_bwd.hip: kKeyBlockH16
+
+
+class IndexModelError(AssertionError):
+    pass
+
+
+def check(cond, what):
+    if not np.all(cond):
+        raise IndexModelError(what)
+
+
+# ------------------------------------------------------------ slot table
+
+def build_slots(window, lo, frac, merge=False):
+    """sfa_api.hip build_slots: window distances then offsets, stable sort by
+    lo; with merge, equal (lo, frac) neighbours become one slot.  Returns a
+    list of (lo, frac, mult, rung)."""
+    v = [(s, 0.0, -1) for s in range(window + 1)]
+    v += [(int(l), float(np.float32(f)), k) for k, (l, f) in enumerate(zip(lo, frac))]
+    v.sort(key=lambda x: x[0])  # Python's sort is stable
+    out = []
+    for l, f, r in v:
+        if merge and out and out[-1][0] == l and out[-1][1] == f:
+            out[-1] = (l, f, out[-1][2] + 1.0, -1)
+            continue
+        out.append((l, f, 1.0, r))
+    check(len(out) <= MAX_SLOTS, "slot table over SFA_MAX_SLOTS")
+    return out
+
+
+# ------------------------------------------------------------ forward
+
+def fwd_h16_shape(D, G):
+    """sfa_fwd.hip fwd_h16_lpq / fwd_h16_bq: (lanes per query, queries per block)."""
+    want = max(2 * G, D // 16)
+    lpq = min(want, min(D // 2, 16))
+    bq = 256 // lpq if lpq >= 8 else 64
+    return lpq, bq
+
+
+def forward(n, window, lo, frac, bq, interp=True):
+    """Stages of fwd_offsets_kernel / fwd_offsets_h16_kernel for every query
+    block: staged positions, the LDS rows each lane reads for each slot (row r
+    and its interpolation partner r - 1) and the rotary rows.  Returns the
+    number of (block, stage) pairs."""
+    sl = build_slots(window, lo, frac, merge=True)
+    S = len(sl)
+    nblk = (n + bq - 1) // bq
+    stages = 0
+    for blk in range(nblk):
+        i0 = blk * bq
+        i_last = min(i0 + bq, n) - 1
+        i = i0 + np.arange(bq)
+        s = 0
+        while s < S:
+            lo0 = sl[s][0]
+            if lo0 > i_last:
+                break
+            two = lambda t: 1 if (interp and sl[t][1] > 0.0) else 0
+            lomax = lo0 + two(s)
+            e = s + 1
+            while e < S:
+                le = sl[e][0]
+                if le > i_last:
+                    break
+                need = max(lomax, le + two(e))
+                if need - lo0 + bq > CAP:
+                    break
+                lomax = need
+                e += 1
+            r0 = i0 - lomax
+            nrows = lomax - lo0 + bq
+            check(0 < nrows <= CAP, "forward stage rows within the LDS capacity")
+            pos = r0 + np.arange(nrows)
+            loaded = (pos >= 0) & (pos < n)
+            check(pos[loaded] < n, "staged rows (and their rotary rows) below n")
+            for sj in range(s, e):
+                l, f = sl[sj][0], sl[sj][1]
+                r = i - l - r0
+                check((r >= 0) & (r < nrows), "forward slot row inside the stage")
+                if interp and f > 0.0:
+                    check(r - 1 >= 0, "forward interpolation partner inside the stage")
+                else:
+                    check(r - 1 >= -1, "forward pad row")
+            stages += 1
+            s = e
+    return stages
+
+
+# ------------------------------------------------------------ query pass
+
+def bwd_lpq(D, G):
+    """sfa_bwd.hip bwd_lpq."""
+    dims = 4 if G >= 4 else 8
+    a = max(2 * G, D // dims)
+    return min(min(a, D // 2), 16)
+
+
+def bwd_bq(G):
+    return 32 if G >= 4 else 64
+
+
+def query_pass(n, window, lo, frac, D, G, want_dd=True, batch_kv=1):
+    """bwd_query_kernel: stages (slots with a second row: interpolated or dd),
+    the LDS rows each query reads, the p / dp workspace offsets of the writer
+    lanes and the dd partial indices (one launch per rung window)."""
+    sl = build_slots(window, lo, frac)
+    S = len(sl)
+    n_rungs = len(lo)
+    lpq, bq = bwd_lpq(D, G), bwd_bq(G)
+    nd = lpq // G
+    rpl_small = 1 if nd >= 16 else 16 // nd
+    rpl = rpl_small if (not want_dd or n_rungs <= rpl_small * nd) else 16
+    windows = [0] if (not want_dd or n_rungs <= rpl * nd) else list(range(0, n_rungs, rpl * nd))
+    nblk = (n + bq - 1) // bq
+    tiles = nblk * batch_kv
+    p_size = batch_kv * S * n * G  # floats per p (or dp) array
+    for r0w in windows:
+        dd_of = lambda t: want_dd and n_rungs > 0 and 0 <= sl[t][3] - r0w < rpl * nd
+        for blk in range(nblk):
+            i0 = blk * bq
+            i_last = min(i0 + bq, n) - 1
+            i = i0 + np.arange(bq)
+            active = i < n
+            s = 0
+            while s < S:
+                lo0 = sl[s][0]
+                if lo0 > i_last:
+                    break
+                two = lambda t: 1 if (sl[t][1] > 0.0 or dd_of(t)) else 0
+                lomax = lo0 + two(s)
+                e = s + 1
+                while e < S:
+                    le = sl[e][0]
+                    if le > i_last:
+                        break
+                    need = max(lomax, le + two(e))
+                    if need - lo0 + bq > CAP:
+                        break
+                    lomax = need
+                    e += 1
+                r0 = i0 - lomax
+                nrows = lomax - lo0 + bq
+                check(0 < nrows <= CAP, "query-pass stage within the LDS capacity")
+                for sj in range(s, e):
+                    l, f, _, rung = sl[sj]
+                    r = i - l - r0
+                    check((r >= 0) & (r < nrows), "query-pass slot row inside the stage")
+                    if f > 0.0 or dd_of(sj):
+                        check(r - 1 >= 0, "query-pass second row inside the stage")
+                    # the extreme (sequence, head) pairs bound every other
+                    lo_idx = (sj * n + i[active]) * G
+                    hi_idx = (((batch_kv - 1) * S + sj) * n + i[active]) * G + G - 1
+                    check((lo_idx >= 0) & (hi_idx < p_size), "p / dp workspace offset")
+                s = e
+            if want_dd and n_rungs:
+                r_last = r0w + min(n_rungs - r0w, rpl * nd) - 1
+                check(r_last * tiles + tiles - 1 < n_rungs * tiles, "dd partial index")
+    return len(windows)
+
+
+# ------------------------------------------------------------ key passes
+
+def key_half_cap(G, D):
+    """sfa_bwd.hip key_half_cap."""
+    kc = 16
+    rw = 2 * kc + 4 if G == 1 else kc * ((G + 1) // 2) + 4
+    cap = (163840 * (KB_H16 // 64) // 16) // (4 * rw)
+    return min(max(cap, KB_H16 + 12), KB_H16 + 64)
+
+
+def key_pass_h16(n, window, lo, frac, G, D=64, batch_kv=1):
+    """key_half_body (bf16): stage bounds, the ring of staged query rows (slot
+    (q - q0) mod kcap of query j0 + q), the ring slot each lane reads at each
+    (slot, tap) step and that it holds query j + delta, and the clamped rows
+    and plane offsets of the weight loads.  Returns the number of steps."""
+    sl = build_slots(window, lo, frac)
+    S = len(sl)
+    kcap = key_half_cap(G, D)
+    KB = KB_H16
+    nblk = (n + KB - 1) // KB
+    tid = np.arange(KB)
+    lo_c = [min(x[0], n) for x in sl]              # 2 min(lo, n) + taps - 1, halved back
+    taps = [2 if x[1] > 0.0 else 1 for x in sl]
+    p_size = batch_kv * S * n * G
+    steps = 0
+    for blk in range(nblk):
+        j0 = blk * KB
+        j = j0 + tid
+        ring = np.full(kcap, -(10 ** 9), dtype=np.int64)  # query held by each ring slot
+        q0, have_hi, first = 0, 0, True
+        # the prefetch cursor's weight loads run over every step of the table
+        # (rows clamped to [0, n); the last sequence bounds the others)
+        for fs in range(S):
+            i = np.clip(j + lo_c[fs] + np.arange(taps[fs])[:, None], 0, n - 1)
+            check((fs * n * G + i * G >= 0) & (((batch_kv - 1) * S + fs) * n * G + i * G + G <= p_size),
+                  "key-pass weight load offset")
+        s = 0
+        while s < S:
+            lo0 = lo_c[s]
+            if j0 + lo0 > n - 1:
+                break
+            lomax, e = lo0, s
+            while e < S:
+                le = lo_c[e]
+                if j0 + le > n - 1 or le - lo0 + KB + 1 > kcap:
+                    break
+                lomax = le
+                e += 1
+            check(e > s, "a stage holds at least one slot")
+            r0 = j0 + lo0
+            nrows = min(lomax - lo0 + KB + 1, n - r0)
+            hi = lo0 + nrows - 1
+            if first:
+                q0, have_hi, first = lo0, lo0 - 1, False
+            check(lo0 >= q0, "stages in increasing offset order")
+            base = (lo0 - q0) % kcap
+            fnew = max(lo0, have_hi + 1)
+            nnew = hi - fnew + 1
+            rows = np.arange(max(nnew, 0))
+            slot = fnew - lo0 + rows + base
+            check(slot < 2 * kcap, "ring slot before the wrap")
+            slot = np.where(slot >= kcap, slot - kcap, slot)
+            check((slot >= 0) & (slot < kcap), "ring slot of a staged row")
+            rn = j0 + fnew
+            check(rn + rows < n, "staged query rows below n")
+            ring[slot] = rn + rows  # rows before the sequence are staged as zeros
+            have_hi = max(have_hi, hi)
+            for sj in range(s, e):
+                for tap in range(taps[sj]):
+                    delta = lo_c[sj] + tap
+                    valid = (j + delta >= 0) & (j + delta < n)
+                    soff = delta - lo0 + base
+                    wrap = tid >= kcap - soff
+                    rs = tid + soff - np.where(wrap, kcap, 0)
+                    check((rs[valid] >= 0) & (rs[valid] < kcap), "ring slot of a step")
+                    check(ring[rs[valid]] == (j + delta)[valid], "ring slot holds the step's query row")
+                    steps += 1
+            s = e
+        check(np.all(j[j < n] < n), "dK rotary row")
+    return steps
+
+
+def key_block_f32(G, D):
+    """sfa_bwd.hip key_block for float tensors."""
+    return 128 if 2 * G * 16 * 4 <= 256 else 64
+
+
+def fp32_key_rope_row(delta):
+    """bwd_key_kernel: rotary row of a step, R(delta) for a past offset and
+    R(|delta|)^T for a future (negative) one."""
+    return np.where(delta >= 0, delta, -delta)
+
+
+def key_pass_f32(n, window, lo, frac, G, D=64, rope_row=fp32_key_rope_row):
+    """bwd_key_kernel (float32): stage bounds, staged rows, the LDS row and
+    the rotary row of each valid step, the workspace offset of its loads."""
+    sl = build_slots(window, lo, frac)
+    S = len(sl)
+    KB = key_block_f32(G, D)
+    KCAP = KB + 48
+    nblk = (n + KB - 1) // KB
+    tid = np.arange(KB)
+    steps = 0
+    for blk in range(nblk):
+        j0 = blk * KB
+        j = j0 + tid
+        activej = j < n
+        s = 0
+        while s < S:
+            lo0 = sl[s][0]
+            if j0 + lo0 > n - 1:
+                break
+            lomax, e = lo0, s
+            while e < S:
+                le = sl[e][0]
+                if j0 + le > n - 1 or le - lo0 + KB + 1 > KCAP:
+                    break
+                lomax = le
+                e += 1
+            r0 = j0 + lo0
+            nrows = min(lomax - lo0 + KB + 1, n - r0)
+            check(0 < nrows <= KCAP, "fp32 key-pass stage within the LDS capacity")
+            for sj in range(s, e):
+                l, f = sl[sj][0], sl[sj][1]
+                for tap in range(2 if f > 0.0 else 1):
+                    i = j + l + tap
+                    valid = activej & (i >= 0) & (i < n) & ((tap == 1) | (j > 0) | (f == 0.0))
+                    delta = l + tap
+                    row = j + delta - r0
+                    check((row[valid] >= 0) & (row[valid] < nrows), "fp32 key-pass LDS row")
+                    rr = rope_row(np.full(KB, delta))
+                    check((rr[valid] >= 0) & (rr[valid] < n), "fp32 key-pass rotary row")
+                    steps += 1
+            s = e
+    return steps

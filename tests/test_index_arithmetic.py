@@ -1,0 +1,118 @@
+"""Index arithmetic of the HIP kernels, checked on the CPU (no GPU).
+
+tests/index_model.py walks each kernel's stages, LDS rows, key-pass ring
+slots, rotary rows and workspace offsets for the slot tables the library
+runs: the page-1 learned and fixed layers, the staggered schedule, page 3's
+causal and bidirectional Christoffel layers at context 2048, the maximum slot
+count, and seeded random tables (interpolated, signed), at full and ragged
+lengths.  Two planted mistakes in the model (a rotary row taken from a
+negative offset as it stands, a ring slot read without its wrap) must be
+caught, so the checks are known to bite.
+"""
+
+import numpy as np
+import pytest
+
+import index_model as im
+from oracle import christoffel as ref_chr
+from oracle import offsets as ref_off
+
+
+def _tables():
+    rng = np.random.default_rng(3)
+    learned = 0.7886644640192136
+    lo_l, fr_l = ref_off.rung_offsets(learned)
+    lo_1, fr_1 = ref_off.rung_offsets(1.0)
+    causal = np.array(ref_chr.offsets(128, 1024), dtype=np.int64)
+    signed = np.concatenate([-causal[::-1], causal])
+    rnd_lo = rng.integers(0, 300, size=256)
+    rnd_fr = rng.random(256).astype(np.float32)
+    rnd_fr[::3] = 0.0
+    neg_lo = np.array([-5, -2, 3, -40, 17, 0], dtype=np.int64)
+    neg_fr = np.array([0.3, 0.0, 0.6, 0.5, 0.0, 0.25], dtype=np.float32)
+    stag = ref_off.schedule_alpha("coprime", 5, 16, 7)
+    lo_s, fr_s = ref_off.rung_offsets(stag)
+    return {
+        "page1_learned": (1024, 10, lo_l, fr_l),
+        "page1_fixed": (1024, 8, lo_1, fr_1),
+        "page1_staggered_l5": (1024, 12, lo_s, fr_s),
+        "christoffel_causal": (2048, 0, causal, np.zeros(128, np.float32)),
+        "christoffel_signed": (2048, 0, signed, np.zeros(256, np.float32)),
+        "max_slots": (260, 63, rnd_lo, rnd_fr),
+        "negative_interpolated": (150, 2, neg_lo, neg_fr),
+        "ragged_200": (200, 10, lo_l, fr_l),
+        "short_65": (65, 8, lo_l, fr_l),
+        "single": (1, 8, lo_l, fr_l),
+    }
+
+
+TABLES = _tables()
+IDS = sorted(TABLES)
+
+
+@pytest.mark.parametrize("name", IDS)
+def test_forward_stages_and_rows(name):
+    n, W, lo, fr = TABLES[name]
+    assert im.forward(n, W, lo, fr, im.BQ_FWD_F32) > 0
+    for D, G in ((64, 4), (64, 1), (16, 8)):
+        _, bq = im.fwd_h16_shape(D, G)
+        assert im.forward(n, W, lo, fr, bq) > 0
+    if not np.any(np.asarray(fr) > 0):
+        assert im.forward(n, W, lo, fr, im.BQ_FWD_F32, interp=False) > 0
+
+
+@pytest.mark.parametrize("name", IDS)
+def test_query_pass_stages_rows_and_workspace(name):
+    n, W, lo, fr = TABLES[name]
+    for D, G in ((64, 4), (64, 1), (32, 2), (16, 8)):
+        im.query_pass(n, W, lo, fr, D, G, want_dd=True, batch_kv=2)
+        im.query_pass(n, W, lo, fr, D, G, want_dd=False)
+
+
+def test_query_pass_rung_windows():
+    # 256 rungs at one lane per query head (G = 8, D = 16) take one launch
+    # per 16-rung window; at G = 4, D = 64 the 15 Fibonacci rungs take one
+    n, W, lo, fr = TABLES["max_slots"]
+    assert im.query_pass(n, W, lo, fr, 16, 8) == 16
+    n, W, lo, fr = TABLES["page1_learned"]
+    assert im.query_pass(n, W, lo, fr, 64, 4) == 1
+
+
+@pytest.mark.parametrize("name", IDS)
+def test_key_pass_ring_holds_each_steps_row(name):
+    n, W, lo, fr = TABLES[name]
+    for G in (1, 2, 4, 8):
+        im.key_pass_h16(n, W, lo, fr, G, batch_kv=2)
+
+
+@pytest.mark.parametrize("name", IDS)
+def test_fp32_key_pass_rows_and_rotary_rows(name):
+    n, W, lo, fr = TABLES[name]
+    for G in (1, 4):
+        im.key_pass_f32(n, W, lo, fr, G)
+
+
+def test_negative_offset_rotary_row_mistake_is_caught():
+    # A future (negative) offset rotated by the table row delta itself reads
+    # before the table; the kernel uses row |delta|.
+    n, W, lo, fr = TABLES["christoffel_signed"]
+    with pytest.raises(im.IndexModelError, match="rotary row"):
+        im.key_pass_f32(n, W, lo, fr, 1, rope_row=lambda d: d)
+    n, W, lo, fr = TABLES["negative_interpolated"]
+    with pytest.raises(im.IndexModelError, match="rotary row"):
+        im.key_pass_f32(n, W, lo, fr, 4, rope_row=lambda d: d)
+
+
+def test_ring_wrap_mistake_is_caught(monkeypatch):
+    # The same ring without the wrap at kcap reads past the ring.
+    orig = np.where
+
+    def no_wrap(cond, a, b):
+        if np.isscalar(a) and a == im.key_half_cap(4, 64) and np.isscalar(b) and b == 0:
+            return np.zeros_like(cond, dtype=np.int64)
+        return orig(cond, a, b)
+
+    monkeypatch.setattr(im.np, "where", no_wrap)
+    n, W, lo, fr = TABLES["page1_learned"]
+    with pytest.raises(im.IndexModelError):
+        im.key_pass_h16(n, W, lo, fr, 4)
