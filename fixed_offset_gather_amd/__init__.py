@@ -44,6 +44,8 @@ SFA_FLAG_SIGNED_OFFSETS = 2
 MAX_OFFSETS = 256
 MAX_SLOTS = 320
 NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
+BF16_MAX_ABS = 46318.0
+BF16_MIN_ABS = 2.0 ** -14
 SCHEDULES = {"fixed": 0, "linear": 1, "coprime": 2}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -97,6 +99,7 @@ _sig("sfa_bwd_noalloc", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _vp, _vp, _vp,
 _sig("sfa_bwd_edges_workspace_bytes", _c.c_size_t, [_c.POINTER(SfaAttn), _c.c_int])
 _sig("sfa_bwd_edges", _c.c_int, [_c.POINTER(SfaAttn), _vp, _vp, _c.c_int, _vp, _vp, _c.c_int, _vp, _vp, _vp,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _c.c_size_t, _vp])
+_sig("sfa_absmax", _c.c_int, [_vp, _c.c_int64, _c.c_int, _vp, _vp])
 _sig("sfa_profile_enable", _c.c_int, [_c.c_int])
 _sig("sfa_profile_read", _c.c_int, [_c.c_char_p, _c.POINTER(_c.c_double), _c.POINTER(_c.c_int64)])
 _sig("sfa_profile_reset", _c.c_int, [])
@@ -108,6 +111,20 @@ class SfaError(RuntimeError):
         self.code = code
         msg = _lib.sfa_last_error().decode(errors="replace")
         super().__init__("%s failed (%d): %s" % (fn, code, msg))
+
+
+class RangeError(ValueError):
+    """A bfloat16 input outside the range of the kernels' f16 operands."""
+
+    def __init__(self, name, amax):
+        self.tensor, self.absmax = name, amax
+        if amax != amax or amax == float("inf"):
+            why = "holds a non-finite value"
+        elif amax > BF16_MAX_ABS:
+            why = "has max |x| = %.6g above %.6g (f16 operands would overflow)" % (amax, BF16_MAX_ABS)
+        else:
+            why = "has max |x| = %.6g below %.6g (f16 operands would be subnormal)" % (amax, BF16_MIN_ABS)
+        super().__init__("bfloat16 %s %s" % (name, why))
 
 
 def _check(fn, rc):
@@ -287,6 +304,29 @@ def _check_shapes(q, k, v=None, dout=None):
             raise ValueError("%s is on %s, q on %s" % (nm, t.device, q.device))
 
 
+def absmax(t):
+    """Largest |x| of a device tensor (inf or nan if it holds one), from
+    sfa_absmax; synchronises the tensor's stream."""
+    torch = _torch()
+    _require(t, "tensor")
+    res = torch.zeros(1, dtype=torch.int32, device=t.device)
+    _check("sfa_absmax", _lib.sfa_absmax(_ptr(t), t.numel(), _dtype_code(t), _ptr(res), _stream(t)))
+    return float(res.cpu().view(torch.float32).item())
+
+
+def check_range(**tensors):
+    """Raise RangeError for the first bfloat16 tensor outside the kernels'
+    f16 operand range: max |x| above BF16_MAX_ABS, non-finite, or nonzero and
+    below BF16_MIN_ABS.  float32 tensors are not restricted."""
+    torch = _torch()
+    for name, t in tensors.items():
+        if t is None or t.dtype != torch.bfloat16 or t.numel() == 0:
+            continue
+        m = absmax(t)
+        if not (m <= BF16_MAX_ABS) or 0.0 < m < BF16_MIN_ABS:
+            raise RangeError(name, m)
+
+
 class Problem:
     """Holds an ``sfa_attn`` and the host arrays it points to."""
 
@@ -308,17 +348,21 @@ class Problem:
 
 
 def fwd(q, k, v, window=0, lo=None, frac=None, rope=None, scale=0.0, want_lse=False, out=None, lse=None,
-        interp_kernel=False, signed_offsets=False):
+        interp_kernel=False, signed_offsets=False, range_check=False):
     """Forward over the window 0..window plus shared offsets (lo, frac).
 
     interp_kernel=True runs the interpolating instantiation even when every
     frac is 0 (SFA_FLAG_INTERP_KERNEL); the result is the same.
     signed_offsets=True admits negative lo (later rows; SFA_FLAG_SIGNED_OFFSETS).
+    range_check=True scans bfloat16 inputs first (check_range) and raises
+    RangeError, launching nothing, if one is outside the f16 operand range.
     """
     torch = _torch()
     _check_shapes(q, k, v)
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, nm, q.dtype)
+    if range_check:
+        check_range(q=q, k=k, v=v)
     B, n, hq, d = q.shape
     pr = Problem(q, k, window, lo, frac, rope, scale, (SFA_FLAG_INTERP_KERNEL if interp_kernel else 0) |
                  (SFA_FLAG_SIGNED_OFFSETS if signed_offsets else 0))
@@ -332,12 +376,14 @@ def fwd(q, k, v, window=0, lo=None, frac=None, rope=None, scale=0.0, want_lse=Fa
     return (o, lse) if (want_lse or lse is not None) else o
 
 
-def fwd_edges(q, k, v, edges, count, rope=None, scale=0.0, want_lse=False, out=None):
+def fwd_edges(q, k, v, edges, count, rope=None, scale=0.0, want_lse=False, out=None, range_check=False):
     """Forward over per-query edge lists (device int32 [n, width], [n])."""
     torch = _torch()
     _check_shapes(q, k, v)
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
         _require(t, nm, q.dtype)
+    if range_check:
+        check_range(q=q, k=k, v=v)
     B, n, hq, d = q.shape
     _require(edges, "edges", torch.int32)
     _require(count, "count", torch.int32, (n,))
@@ -360,13 +406,17 @@ def bwd_workspace_bytes(q, k, window=0, lo=None, frac=None, rope=None, scale=0.0
 
 
 def bwd(q, k, v, lse, dout, window=0, lo=None, frac=None, rope=None, scale=0.0,
-        base=None, alpha=None, workspace=None, want_dd=True, signed_offsets=False, out=None):
+        base=None, alpha=None, workspace=None, want_dd=True, signed_offsets=False, out=None,
+        range_check=False):
     """Backward: returns (dq, dk, dv, dd or None, dtheta or None).  out:
-    optional (dq, dk, dv) tensors to write (like q, k, v)."""
+    optional (dq, dk, dv) tensors to write (like q, k, v).  range_check as
+    for fwd, over q, k, v and dout."""
     torch = _torch()
     _check_shapes(q, k, v, dout)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _require(t, nm, q.dtype)
+    if range_check:
+        check_range(q=q, k=k, v=v, dout=dout)
     B, n, hq, d = q.shape
     _require(lse, "lse", torch.float32, (B, hq, n))
     pr = Problem(q, k, window, lo, frac, rope, scale, SFA_FLAG_SIGNED_OFFSETS if signed_offsets else 0)
@@ -403,13 +453,16 @@ def bwd_edges_workspace_bytes(q, k, width, rope=None, scale=0.0):
     return nb
 
 
-def bwd_edges(q, k, v, lse, dout, edges, count, inv, inv_count, rope=None, scale=0.0, workspace=None):
+def bwd_edges(q, k, v, lse, dout, edges, count, inv, inv_count, rope=None, scale=0.0, workspace=None,
+              range_check=False):
     """Edge-list backward: returns (dq, dk, dv).  edges/count/inv/inv_count
     are device int32 tensors ([n, width], [n], [n, cap], [n])."""
     torch = _torch()
     _check_shapes(q, k, v, dout)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _require(t, nm, q.dtype)
+    if range_check:
+        check_range(q=q, k=k, v=v, dout=dout)
     B, n, hq, d = q.shape
     _require(lse, "lse", torch.float32, (B, hq, n))
     for t, nm in ((edges, "edges"), (count, "count"), (inv, "inv"), (inv_count, "inv_count")):

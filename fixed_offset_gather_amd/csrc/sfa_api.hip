@@ -10,6 +10,7 @@
 #include <string>
 #include <vector>
 
+#include "sfa_device.h"
 #include "sfa_internal.h"
 
 namespace sfa {
@@ -194,7 +195,58 @@ extern "C" int sfa_profile_read(const char* kernel, double* total_ms, int64_t* l
   return SFA_OK;
 }
 
+// ------------------------------------------------------------ range scan
+
+namespace {
+
+// Largest |x| of count elements, as IEEE bits (NaN above +inf above every
+// finite value, so the bit order is the magnitude order with non-finite
+// values on top): every thread reads 8 elements (16 bytes of bf16, two
+// float4 of fp32) per grid-stride iteration, the wave takes the maximum of
+// its lanes and one lane per wave folds it into *result with an atomic max.
+template <typename T>
+__global__ __launch_bounds__(256) void absmax_kernel(const T* __restrict__ x, int64_t count,
+                                                     unsigned* __restrict__ result) {
+  unsigned m = 0;
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x * 8;
+  for (int64_t i0 = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 8; i0 < count; i0 += stride) {
+    float v[8];
+    if (i0 + 8 <= count) {
+      load_vec<8>(x + i0, v);
+    } else {
+      for (int u = 0; u < 8; ++u) v[u] = i0 + u < count ? load1(x + i0 + u) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = max(m, __float_as_uint(v[u]) & 0x7fffffffu);
+  }
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) m = max(m, unsigned(__shfl_xor(int(m), s)));
+  if ((threadIdx.x & 63) == 0 && m) atomicMax(result, m);
+}
+
+}  // namespace
+
 // ------------------------------------------------------------ entry points
+
+extern "C" int sfa_absmax(const void* x, int64_t count, int dtype, uint32_t* result, void* stream) {
+  clear_error();
+  if (count < 0) return fail(SFA_ERR_ARG, "sfa_absmax: count must be >= 0");
+  if (dtype != SFA_F32 && dtype != SFA_BF16) return fail(SFA_ERR_ARG, "sfa_absmax: unknown dtype %d", dtype);
+  if (count == 0) return SFA_OK;
+  if (!x || !result) return fail(SFA_ERR_ARG, "sfa_absmax: NULL pointer");
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(result) & 3u))
+    return fail(SFA_ERR_ARG, "sfa_absmax: x must be 16-byte aligned, result 4-byte aligned");
+  const int64_t per_block = 256 * 8;
+  const int blocks = int(std::min<int64_t>((count + per_block - 1) / per_block, 2048));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == SFA_BF16)
+    hipLaunchKernelGGL(absmax_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, static_cast<const bf16_t*>(x), count,
+                       reinterpret_cast<unsigned*>(result));
+  else
+    hipLaunchKernelGGL(absmax_kernel<float>, dim3(blocks), dim3(256), 0, st, static_cast<const float*>(x), count,
+                       reinterpret_cast<unsigned*>(result));
+  return hip_status(int(hipGetLastError()), "sfa_absmax launch");
+}
 
 extern "C" int sfa_fwd(const sfa_attn* a, const void* q, const void* k, const void* v, void* o,
                        float* lse, void* stream) {

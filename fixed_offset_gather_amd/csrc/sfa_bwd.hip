@@ -45,6 +45,15 @@ constexpr int kCap = 128;
 // Dims per key-pass tile (and per chunk of a packed key-pass row).
 constexpr int key_chunk(int D) { return D >= 16 ? 16 : D; }
 
+// Queries per bwd_query workgroup.  A workgroup's LDS (its stage rows) lets
+// two share a CU; with G >= 4 the 16-lane queries already give 8 waves per
+// workgroup, with fewer heads 8-lane queries need 64 queries for the same
+// (Christoffel query pass 210 -> 163 us; G = 4 at 64 queries: 124 -> 142 us).
+template <int G>
+constexpr int bwd_bq() {
+  return G >= 4 ? 32 : 64;
+}
+
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -60,6 +69,7 @@ struct BwdArgs {
   float* dd_part;
   uint32_t* xq;  // packed key-pass rows (see BwdWorkspace), or null
   uint32_t* xd;
+  float* wmax;   // per query-pass workgroup bound on |dS| / scale (see BwdWorkspace), or null
   const float* rope;
   int n, hq, hkv, nblk, tiles, S, n_rungs;
   int kcap;     // bwd_key: rows one stage may hold (dynamic LDS)
@@ -162,6 +172,10 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
   const bool want_dd = a.want_dd != 0;
   const int ddu = c & (ND - 1);
   float psum = 0.f;  // sum_slots p of the own head (1 up to the rounding of lse)
+  // bf16 with G >= 2: max_slots |p dp| of the own head, for the bound on
+  // |dS| the key pass scales its f16 weights by
+  constexpr bool kBound = sizeof(T) == 2 && G >= 2;
+  float umax = 0.f;
   float xacc[RPL], yacc[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) xacc[r] = yacc[r] = 0.f;
@@ -293,6 +307,7 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
       const float pdp = p * dp;
       dvec += pdp;
       psum += p;
+      if constexpr (kBound) umax = fmaxf(umax, fabsf(pdp));
       if (active && HS::writer(c)) {  // p = 0 where the slot has no row for query i
         // The slot's plane bases stay scalar (global_store with an SGPR
         // base and the lane's 32-bit offset) instead of being folded into
@@ -381,6 +396,24 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
     }
   }
   if (active && HS::writer(c)) a.Dvec[(size_t(seq) * n + i) * G + own] = dvec;
+  if constexpr (kBound) {
+    // |dS| / scale = |p dp - p Dvec| <= |p dp| + psum |Dvec| (every p <=
+    // sum p): the workgroup's maximum of that bound, for the key pass
+    if (a.wmax) {
+      __shared__ float wbw[NWV];
+      float u = umax + psum * fabsf(dvec);
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) u = fmaxf(u, __shfl_xor(u, m));
+      if ((tid & 63) == 0) wbw[tid >> 6] = u;
+      __syncthreads();
+      if (tid == 0) {
+        float m = wbw[0];
+#pragma unroll
+        for (int w_ = 1; w_ < NWV; ++w_) m = fmaxf(m, wbw[w_]);
+        a.wmax[size_t(seq) * a.nblk + blk] = m;
+      }
+    }
+  }
   if (want_dd) {
     // sum_(query, head) of Y - Dvec X per rung over the workgroup: each
     // (query, head) counts once (its duplicate lane u holds the rung), so
@@ -686,6 +719,39 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   const size_t kv_off = (size_t(b) * n + j) * size_t(a.hkv) * D + size_t(g) * D + c * KC;
 
   float acc[KC], accv[BOTH ? KC : 1];  // dK~ (or dV), and dV for BOTH
+
+  // dK with f16 weights: dS = scale p (dp - Dvec) scales with dO and V and
+  // can fall below f16's normal range (2^-14) while both are well inside
+  // it, losing the weights' precision.  The weights enter scaled by 2^e,
+  // e chosen so that the largest bound on |dS| over the query-pass
+  // workgroups holding this block's rows [j0 + lo_first, j0 + KB + lo_last]
+  // maps to [2^13, 2^14), and the sum is scaled back by 2^-e before the
+  // store (both exact).  Each wave takes the maximum itself (no barrier);
+  // the waves agree, and each scales back its own keys either way.
+  float kscale = a.scale, kunscale = 1.f;
+  if constexpr (PART == 0 && !BOTH) {
+    if (a.wmax && st.count > 0) {
+      constexpr int BQQ = bwd_bq<G>();
+      const int nq = (n + BQQ - 1) / BQQ;
+      const int ilo = max(j0 + max(st.s[0].lo, -n), 0);
+      const int ihi = min(j0 + KB + min(st.s[st.count - 1].lo, n), n - 1);
+      float u = 0.f;
+      if (ilo <= ihi) {
+        const float* wm = a.wmax + size_t(seq) * nq;
+        for (int t = ilo / BQQ + (tid & 63); t <= ihi / BQQ; t += 64) u = fmaxf(u, wm[t]);
+      }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) u = fmaxf(u, __shfl_xor(u, m));
+      const float w = a.scale * u;
+      if (w > 0.f && w <= 3.4e38f) {
+        int ex;
+        (void)frexpf(w, &ex);  // w < 2^ex
+        const int e = min(max(14 - ex, -120), 120);
+        kscale = ldexpf(a.scale, e);
+        kunscale = ldexpf(1.f, -e);
+      }
+    }
+  }
 #pragma unroll
   for (int x = 0; x < KC; ++x) acc[x] = 0.f;
 #pragma unroll
@@ -770,7 +836,7 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
       wts[0] = __float_as_uint(a.scale * p * (q.raw[1][0] - q.raw[2][0]));
       wts[1] = __float_as_uint(p);
     } else {
-      const float ws = PART == 0 ? a.scale * q.ws : q.ws;
+      const float ws = PART == 0 ? kscale * q.ws : q.ws;
 #pragma unroll
       for (int hp = 0; hp < GW; ++hp) {
         const int h0 = 2 * hp, h1 = 2 * hp + 1 < G ? 2 * hp + 1 : 2 * hp;
@@ -1053,6 +1119,10 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
     s = e;
   }
   if (activej) {
+    if constexpr (PART == 0 && !BOTH) {
+#pragma unroll
+      for (int x = 0; x < KC; ++x) acc[x] *= kunscale;
+    }
     if (rope) rotate_pairs<KC, -1>(acc, a.rope + size_t(j) * D, c * KC);  // dK = R(j)^T dK~
     store_vec<KC>(static_cast<bf16_t*>(PART == 1 ? a.dv : a.dk) + kv_off, acc);
     if constexpr (BOTH) store_vec<KC>(static_cast<bf16_t*>(a.dv) + kv_off, accv);
@@ -1140,15 +1210,6 @@ constexpr int bwd_lpq() {
   return b < 16 ? b : 16;
 }
 
-// Queries per bwd_query workgroup.  A workgroup's LDS (its stage rows) lets
-// two share a CU; with G >= 4 the 16-lane queries already give 8 waves per
-// workgroup, with fewer heads 8-lane queries need 64 queries for the same
-// (Christoffel query pass 210 -> 163 us; G = 4 at 64 queries: 124 -> 142 us).
-template <int G>
-constexpr int bwd_bq() {
-  return G >= 4 ? 32 : 64;
-}
-
 // Lanes per query in bwd_edges_query (keys straight from global memory):
 // at most 8 dims per lane, same other limits.
 template <int D, int G>
@@ -1166,6 +1227,7 @@ BwdArgs make_args(const Problem& p, const SlotTable& t, const BwdWorkspace& ws) 
   a.dd_part = ws.dd_part;
   a.xq = ws.xq;
   a.xd = ws.xd;
+  a.wmax = ws.wmax;
   a.rope = p.rope;
   a.n = p.n;
   a.hq = p.hq;
@@ -1506,6 +1568,8 @@ size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, Bw
   const size_t dd_e = al(size_t(ws->blocks) * (t.n_rungs > 0 ? t.n_rungs : 1));
   // packed key-pass rows (bf16, G >= 2): D * G / 2 words per (sequence, row)
   const size_t xe = (h16 && p.G >= 2) ? al(size_t(p.B) * p.hkv * size_t(p.n) * p.D * (p.G / 2)) : 0;
+  // dS bounds (bf16, G >= 2): one per query-pass workgroup
+  const size_t we = (h16 && p.G >= 2) ? al(size_t(ws->blocks)) : 0;
   float* f = static_cast<float*>(base);
   ws->p = f;
   ws->dp = f ? f + pe : nullptr;
@@ -1513,7 +1577,8 @@ size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, Bw
   ws->dd_part = f ? f + 2 * pe + de : nullptr;
   ws->xq = (f && xe) ? reinterpret_cast<uint32_t*>(f + 2 * pe + de + dd_e) : nullptr;
   ws->xd = (f && xe) ? reinterpret_cast<uint32_t*>(f + 2 * pe + de + dd_e + xe) : nullptr;
-  ws->bytes = (2 * pe + de + dd_e + 2 * xe) * sizeof(float);
+  ws->wmax = (f && we) ? f + 2 * pe + de + dd_e + 2 * xe : nullptr;
+  ws->bytes = (2 * pe + de + dd_e + 2 * xe + we) * sizeof(float);
   return ws->bytes;
 }
 

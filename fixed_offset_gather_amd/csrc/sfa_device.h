@@ -84,6 +84,10 @@ __device__ __forceinline__ void load_vec(const bf16_t* __restrict__ p, float (&o
   }
 }
 
+// One element widened to float.
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+__device__ __forceinline__ float load1(const bf16_t* p) { return __uint_as_float(uint32_t(*p) << 16); }
+
 // N consecutive floats at a uniform base plus a 32-bit per-lane byte offset,
 // loaded through the global address space (global_load with an SGPR base).
 // The caller keeps `base` uniform; the empty asm keeps the offset a 32-bit

@@ -63,6 +63,10 @@ struct BwdWorkspace {
   // and dO.  Null otherwise (the key pass then stages from q and dO).
   uint32_t* xq;
   uint32_t* xd;
+  // bf16 with G >= 2: per query-pass workgroup ([B][Hkv][n / bq]), a bound
+  // on |dS| / scale over its (query, head, slot) entries, from which the key
+  // pass scales its f16 dS weights by a power of two.  Null otherwise.
+  float* wmax;
   size_t bytes;
   int blocks;
 };

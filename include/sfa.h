@@ -56,15 +56,25 @@ extern "C" {
 #define SFA_F32 0  /* float32 tensors */
 #define SFA_BF16 1 /* bfloat16 tensors (accumulation is float32) */
 /*
- * With SFA_BF16 the kernels take their products on f16 operands: the staged
- * K and V rows (K rotated), the scaled query, the staged rows of the key
- * pass and the probability weights are rounded to f16, and every sum is
- * accumulated in float32.  Inputs must therefore stay within f16's range:
- * every element of Q, K, V and dO, after rotation (which can grow one
- * element of a pair by up to sqrt 2), below 65504 in magnitude; values below
- * 2^-14 keep only f16's subnormal precision.  bf16's wider exponent range is
- * not supported and is not checked.
+ * With SFA_BF16 the forward and the key pass take their products on f16
+ * operands: the staged K and V rows (K rotated), the scaled query, the staged
+ * rows of the key pass and its probability weights are rounded to f16, and
+ * every sum is accumulated in float32 (the query pass and the offset gradient
+ * use float32 operands).  Inputs must therefore lie within f16's range:
+ * the largest magnitude of each of Q, K, V and dO at most SFA_BF16_MAX_ABS
+ * (65504 / sqrt 2, as a rotation can grow one element of a pair by up to
+ * sqrt 2) and, unless the tensor is all zeros, at least SFA_BF16_MIN_ABS
+ * (2^-14, the smallest normal f16: a tensor wholly below it keeps only f16's
+ * subnormal precision).  The kernels do not test this, as a scan costs a
+ * pass over every input; sfa_absmax is that scan, for callers who cannot
+ * vouch for their inputs, and a tensor outside the range must not be given
+ * to the bf16 kernels (larger inputs give non-finite outputs).  Products of
+ * in-range inputs need no such care: the key pass scales its f16 dS weights
+ * by a power of two taken from a bound the query pass records, so small dO
+ * and V together do not push them below f16's normal range.
  */
+#define SFA_BF16_MAX_ABS 46318.0f
+#define SFA_BF16_MIN_ABS 6.103515625e-05f
 
 #define SFA_MAX_OFFSETS 256 /* shared offsets per call (page 3's m = 128, k = 1024 made bidirectional) */
 #define SFA_MAX_SLOTS 320   /* window + 1 + offsets */
@@ -189,6 +199,19 @@ int sfa_rope_table(int n, int head_dim, double theta, float* table);
 /* ------------------------------------------------------------------ */
 /* Device attention                                                     */
 /* ------------------------------------------------------------------ */
+
+/*
+ * Largest magnitude of a device tensor, for the bf16 range check (see
+ * SFA_BF16): folds the IEEE bits of max |x| over the count elements of x
+ * (dtype SFA_F32 or SFA_BF16, 16-byte aligned) into the device word *result
+ * (4-byte aligned, caller-owned, cleared by the caller) with an atomic
+ * maximum.  Read as a float, *result is the largest magnitude, +inf if some
+ * element is infinite and NaN if some element is NaN.  Asynchronous on
+ * `stream`.  Returns SFA_OK, SFA_ERR_ARG on a bad argument (before any HIP
+ * call) or SFA_ERR_HIP.
+ */
+int sfa_absmax(const void* x, int64_t count, int dtype, uint32_t* result,
+               void* stream);
 
 /*
  * sfa_attn.flags.  SFA_FLAG_INTERP_KERNEL: sfa_fwd runs the interpolating

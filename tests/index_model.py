@@ -173,6 +173,8 @@ def query_pass(n, window, lo, frac, D, G, want_dd=True, batch_kv=1):
                     hi_idx = (((batch_kv - 1) * S + sj) * n + i[active]) * G + G - 1
                     check((lo_idx >= 0) & (hi_idx < p_size), "p / dp workspace offset")
                 s = e
+            # the workgroup's bound on |dS| (bf16, G >= 2), one per tile
+            check(0 <= (batch_kv - 1) * nblk + blk < tiles, "dS bound index")
             if want_dd and n_rungs:
                 r_last = r0w + min(n_rungs - r0w, rpl * nd) - 1
                 check(r_last * tiles + tiles - 1 < n_rungs * tiles, "dd partial index")
@@ -203,10 +205,17 @@ def key_pass_h16(n, window, lo, frac, G, D=64, batch_kv=1):
     lo_c = [min(x[0], n) for x in sl]              # 2 min(lo, n) + taps - 1, halved back
     taps = [2 if x[1] > 0.0 else 1 for x in sl]
     p_size = batch_kv * S * n * G
+    bq = bwd_bq(G)
+    nq = (n + bq - 1) // bq
     steps = 0
     for blk in range(nblk):
         j0 = blk * KB
         j = j0 + tid
+        # dK (G >= 2): the query rows whose dS bounds scale the weights
+        ilo = max(j0 + max(sl[0][0], -n), 0)
+        ihi = min(j0 + KB + min(sl[-1][0], n), n - 1)
+        if G >= 2 and ilo <= ihi:
+            check(0 <= ilo // bq <= ihi // bq < nq, "dS bound tiles inside the sequence")
         ring = np.full(kcap, -(10 ** 9), dtype=np.int64)  # query held by each ring slot
         q0, have_hi, first = 0, 0, True
         # the prefetch cursor's weight loads run over every step of the table
@@ -255,6 +264,9 @@ def key_pass_h16(n, window, lo, frac, G, D=64, batch_kv=1):
                     rs = tid + soff - np.where(wrap, kcap, 0)
                     check((rs[valid] >= 0) & (rs[valid] < kcap), "ring slot of a step")
                     check(ring[rs[valid]] == (j + delta)[valid], "ring slot holds the step's query row")
+                    if G >= 2:
+                        check(((j + delta)[valid] >= ilo) & ((j + delta)[valid] <= ihi),
+                              "dS bound covers every weight's query row")
                     steps += 1
             s = e
         check(np.all(j[j < n] < n), "dK rotary row")

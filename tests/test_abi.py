@@ -179,7 +179,9 @@ def test_bwd_validation_and_workspace_size():
     dd = al(blocks * 15)
     # packed key-pass rows of q and dO (bf16, G >= 2): D * G / 2 words per row
     xe = al(2 * 2 * 100 * 64 * 2)
-    assert nb == (2 * pe + de + dd + 2 * xe) * 4
+    # bounds on |dS| (bf16, G >= 2): one per query-pass workgroup
+    we = al(blocks)
+    assert nb == (2 * pe + de + dd + 2 * xe + we) * 4
     assert lib.sfa_bwd_workspace_bytes(ctypes.byref(_prob(head_dim=48))) == 0
     base = sfa.base_fib()
     bp = base.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
@@ -356,3 +358,30 @@ def test_noalloc_rejects_oversize_and_invalid_before_any_device_call():
     assert b"static scratch" in lib.sfa_last_error()
     rc = lib.sfa_bwd_noalloc(ctypes.byref(_prob(head_dim=48)), *args, bp, 0.8, FAKE, None)
     assert rc == sfa.SFA_ERR_UNSUPPORTED
+
+
+def test_absmax_rejects_invalid_before_any_device_call():
+    lib = sfa.library()
+    res = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails its checks first
+    assert lib.sfa_absmax(FAKE, -1, sfa.SFA_BF16, res, None) == sfa.SFA_ERR_ARG
+    assert lib.sfa_absmax(FAKE, 16, 7, res, None) == sfa.SFA_ERR_ARG
+    assert b"dtype" in lib.sfa_last_error()
+    assert lib.sfa_absmax(None, 16, sfa.SFA_F32, res, None) == sfa.SFA_ERR_ARG
+    assert lib.sfa_absmax(FAKE, 16, sfa.SFA_F32, None, None) == sfa.SFA_ERR_ARG
+    assert lib.sfa_absmax(ctypes.c_void_p(0x100008), 16, sfa.SFA_F32, res, None) == sfa.SFA_ERR_ARG
+    assert lib.sfa_absmax(FAKE, 16, sfa.SFA_F32, ctypes.c_void_p(0x100002), None) == sfa.SFA_ERR_ARG
+    assert b"aligned" in lib.sfa_last_error()
+    # an empty tensor launches nothing
+    assert lib.sfa_absmax(None, 0, sfa.SFA_BF16, None, None) == sfa.SFA_OK
+
+
+def test_range_error_messages_and_limits():
+    # SFA_BF16_MAX_ABS is 65504 / sqrt 2 rounded down (a rotated pair stays
+    # below f16's largest finite value); SFA_BF16_MIN_ABS is 2^-14
+    assert sfa.BF16_MAX_ABS * 2 ** 0.5 <= 65504.0 < (sfa.BF16_MAX_ABS + 1) * 2 ** 0.5
+    assert sfa.BF16_MIN_ABS == float(np.finfo(np.float16).tiny)
+    assert "overflow" in str(sfa.RangeError("q", 5e4))
+    assert "subnormal" in str(sfa.RangeError("dout", 1e-6))
+    assert "non-finite" in str(sfa.RangeError("v", float("inf")))
+    assert "non-finite" in str(sfa.RangeError("k", float("nan")))
+    assert issubclass(sfa.RangeError, ValueError)

@@ -1,0 +1,166 @@
+"""Input range of the bf16 path, on the GPU, through the C ABI.
+
+The bf16 kernels take f16 operands (include/sfa.h, SFA_BF16): each of Q, K,
+V and dO must have its largest magnitude within [2^-14, 65504 / sqrt 2] (or
+be all zeros).  sfa_absmax is the scan that checks it; the binding's
+range_check=True refuses a tensor outside that range with RangeError before
+anything is launched.  Inside the range the results meet the bf16 bar
+relative to each output's own scale (|err| <= 1e-2 max |ref|), also where
+dO and V are small enough that dS = scale p (dp - Dvec) falls below f16's
+normal range (the key pass rescales those weights by a power of two).  The
+float32 path takes float32 operands and has no such range.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as si
+from oracle import attention as ref
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+W = 8
+ALPHA = 0.75
+
+
+def _sfa():
+    import fixed_offset_gather_amd as sfa
+    return sfa
+
+
+def _np(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def _inputs(dtype, sq=1.0, sk=1.0, sv=1.0, sd=1.0, n=200, hq=8, hkv=2, D=64):
+    q, k, v = si.qkv(1, n, hq, hkv, D, dtype, si.SEED)
+    do = si.upstream(1, n, hq, D, dtype, si.SEED)
+    tdt = q.dtype
+    return [t.to(torch.float32).mul(s).to(tdt) for t, s in ((q, sq), (k, sk), (v, sv), (do, sd))]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("count", [1, 7, 8, 9, 2047, 2048 * 2048 * 8 + 5])
+def test_absmax_is_exact(dtype, count):
+    sfa = _sfa()
+    g = torch.Generator().manual_seed(count)
+    x = torch.randn(count, generator=g).to(dtype)
+    at = int(torch.randint(0, count, (1,), generator=g).item())
+    x[at] = -7.5  # the largest magnitude, possibly in the ragged tail
+    if count > 9:
+        x[count - 1] = 7.0
+    xd = x.to(DEV)
+    print("absmax %s count %d planted at %d" % (dtype, count, at), flush=True)
+    assert sfa.absmax(xd) == float(x.abs().max())
+    x[at // 2] = float("inf")
+    assert sfa.absmax(x.to(DEV)) == float("inf")
+    x[at // 3] = float("nan")
+    assert np.isnan(sfa.absmax(x.to(DEV)))
+    assert sfa.absmax(torch.zeros(0, dtype=dtype, device=DEV)) == 0.0
+
+
+def _attn_args(n):
+    sfa = _sfa()
+    lo, frac = sfa.offsets_fib(ALPHA)
+    return lo, frac, sfa.rope_table_device(n, 64, 1e4, DEV)
+
+
+@pytest.mark.parametrize("scale,which,why", [
+    ((1e5, 1e5, 1e5, 1e5), "q", "overflow"),
+    ((1.0, 1.0, 1e5, 1.0), "v", "overflow"),
+    ((1e-6, 1e-6, 1e-6, 1e-6), "q", "subnormal"),
+    ((1.0, 1e-6, 1.0, 1.0), "k", "subnormal"),
+])
+def test_bf16_out_of_range_is_refused(scale, which, why):
+    sfa = _sfa()
+    q, k, v, do = (t.to(DEV) for t in _inputs("bf16", *scale))
+    lo, frac, rope = _attn_args(q.shape[1])
+    print("range refusal case", scale, flush=True)
+    with pytest.raises(sfa.RangeError, match=why) as ei:
+        sfa.fwd(q, k, v, W, lo, frac, rope, range_check=True)
+    assert ei.value.tensor == which
+    lse = torch.zeros(1, 8, q.shape[1], dtype=torch.float32, device=DEV)
+    with pytest.raises(sfa.RangeError, match=why):
+        sfa.bwd(q, k, v, lse, do, W, lo, frac, rope, base=sfa.base_fib(), alpha=ALPHA, range_check=True)
+
+
+def test_bf16_small_upstream_gradient_is_refused():
+    sfa = _sfa()
+    q, k, v, do = (t.to(DEV) for t in _inputs("bf16", sd=1e-6))
+    lo, frac, rope = _attn_args(q.shape[1])
+    o, lse = sfa.fwd(q, k, v, W, lo, frac, rope, want_lse=True, range_check=True)  # q, k, v in range
+    with pytest.raises(sfa.RangeError, match="subnormal") as ei:
+        sfa.bwd(q, k, v, lse, do, W, lo, frac, rope, range_check=True)
+    assert ei.value.tensor == "dout"
+
+
+def test_bf16_nonfinite_is_refused():
+    sfa = _sfa()
+    q, k, v, do = _inputs("bf16")
+    v[0, 17, 1, 5] = float("nan")
+    q, k, v = (t.to(DEV) for t in (q, k, v))
+    lo, frac, rope = _attn_args(q.shape[1])
+    with pytest.raises(sfa.RangeError, match="non-finite") as ei:
+        sfa.fwd(q, k, v, W, lo, frac, rope, range_check=True)
+    assert ei.value.tensor == "v"
+
+
+def test_range_check_passes_in_range_inputs_unchanged():
+    sfa = _sfa()
+    q, k, v, do = (t.to(DEV) for t in _inputs("bf16"))
+    lo, frac, rope = _attn_args(q.shape[1])
+    o1, l1 = sfa.fwd(q, k, v, W, lo, frac, rope, want_lse=True, range_check=True)
+    o2, l2 = sfa.fwd(q, k, v, W, lo, frac, rope, want_lse=True)
+    g1 = sfa.bwd(q, k, v, l1, do, W, lo, frac, rope, base=sfa.base_fib(), alpha=ALPHA, range_check=True)
+    g2 = sfa.bwd(q, k, v, l2, do, W, lo, frac, rope, base=sfa.base_fib(), alpha=ALPHA)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    # all zeros is in range (dO = 0 gives zero gradients)
+    z = torch.zeros_like(do)
+    dq, dk, dv, dd, dth = sfa.bwd(q, k, v, l1, z, W, lo, frac, rope, base=sfa.base_fib(), alpha=ALPHA,
+                                  range_check=True)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv, dd, dth):
+        assert float(t.abs().max()) == 0.0
+
+
+def _scale_relative_check(dtype, tol, **scales):
+    sfa = _sfa()
+    q, k, v, do = _inputs(dtype, **scales)
+    n = q.shape[1]
+    lo, frac, rope = _attn_args(n)
+    qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
+    o, lse = sfa.fwd(qd, kd, vd, W, lo, frac, rope, want_lse=True, range_check=True)
+    dq, dk, dv, dd, dth = sfa.bwd(qd, kd, vd, lse, dod, W, lo, frac, rope, base=sfa.base_fib(), alpha=ALPHA,
+                                  range_check=True)
+    torch.cuda.synchronize()
+    f64 = [t.to(torch.float64).numpy() for t in (q, k, v, do)]
+    ro, rl = ref.forward(*f64[:3], W, lo, frac, 1e4)
+    g = ref.backward(*f64, W, lo, frac, 1e4)
+    errs = {}
+    for nm, got, want in (("o", o, ro), ("dq", dq, g["dq"]), ("dk", dk, g["dk"]), ("dv", dv, g["dv"]),
+                          ("dd", dd, g["dd"])):
+        errs[nm] = float(np.abs(_np(got) - want).max() / np.abs(want).max())
+    errs["lse_abs"] = float(np.abs(_np(lse) - rl).max())
+    print("scales", scales, "error / max |ref|:", {k_: "%.3g" % e for k_, e in errs.items()}, flush=True)
+    for nm, e in errs.items():
+        assert e <= tol, nm
+
+
+@pytest.mark.parametrize("scales", [
+    dict(sv=1e-3, sd=1e-3),   # dS ~ 1e-7: below f16's normal range before rescaling
+    dict(sd=1e-4),
+    dict(sv=1e4),
+    dict(sq=0.05, sk=0.05, sv=2e-3, sd=2e-3),
+])
+def test_bf16_in_range_scales_meet_the_bar_relative_to_scale(scales):
+    _scale_relative_check("bf16", 1e-2, **scales)
+
+
+@pytest.mark.parametrize("scales", [dict(sv=1e5, sd=1e-6), dict(sq=1e-6, sv=1e-6, sd=1e5)])
+def test_fp32_has_no_operand_range(scales):
+    _scale_relative_check("f32", 1e-5, **scales)

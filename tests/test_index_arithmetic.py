@@ -1,7 +1,8 @@
 """Index arithmetic of the HIP kernels, checked on the CPU (no GPU).
 
 tests/index_model.py walks each kernel's stages, LDS rows, key-pass ring
-slots, rotary rows and workspace offsets for the slot tables the library
+slots, rotary rows, workspace offsets and the tiles of the dS bounds the
+key pass reads for the slot tables the library
 runs: the page-1 learned and fixed layers, the staggered schedule, page 3's
 causal and bidirectional Christoffel layers at context 2048, the maximum slot
 count, and seeded random tables (interpolated, signed), at full and ragged
