@@ -245,20 +245,22 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
       load_vec<DC>(kp + KS, kt);
       load_vec<DC>(kp + KS + VOFF, vt);
       if (interp || dds) {
-        // dK, dV = row r - 1 minus row r: the lerp's slope and dd's factor
+        // dK = row r - 1 minus row r: the lerp's slope and dd's factor.  A
+        // dd slot keeps both V rows as they are (dv = row r - 1): dp and
+        // dO . dV then follow from the two row dots, and V needs no lerp.
         float kb[DC], vb[DC];
         load_vec<DC>(kp, kb);
         load_vec<DC>(kp + VOFF, vb);
 #pragma unroll
         for (int x = 0; x < DC; ++x) {
           dk[x] = kb[x] - kt[x];
-          dv[x] = vb[x] - vt[x];
+          dv[x] = dds ? vb[x] : vb[x] - vt[x];
         }
         if (interp) {
 #pragma unroll
           for (int x = 0; x < DC; ++x) {
             kt[x] = fmaf(w, dk[x], kt[x]);
-            vt[x] = fmaf(w, dv[x], vt[x]);
+            if (!dds) vt[x] = fmaf(w, dv[x], vt[x]);
           }
         }
       }
@@ -275,7 +277,7 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
         dps[j] = s2;
       }
       const float sdot = HS::reduce(sp);
-      const float dp = HS::reduce(dps);
+      float dp = HS::reduce(dps);  // a dd slot: dO . V[r], the nearer row
       // dd slot: sd = q~ . dK and vd = dO . dV of the own head, fp32
       float sd = 0.f, vd = 0.f;
       if (dds) {
@@ -292,7 +294,8 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
           vdp[j] = s2;
         }
         sd = HS::reduce(sdp);
-        vd = HS::reduce(vdp);
+        vd = HS::reduce(vdp) - dp;  // dO . V[r - 1] - dO . V[r]
+        dp = fmaf(w, vd, dp);       // dO . lerp(V[r], V[r - 1], frac)
       }
       // The nearer row i - lo exists when mn <= i - lo <= n - 1, mn = 1 for
       // an interpolated slot (its farther row i - lo - 1 must exist too):
@@ -333,9 +336,17 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
         const float X = active ? a.scale * p * sd : 0.f;
         const float Y = active ? p * fmaf(a.scale * dp, sd, vd) : 0.f;
         const int rr = cur.rung - a.r0;
-        if (ddu == (rr & (ND - 1))) {
-          xacc[rr / ND] = X;
-          yacc[rr / ND] = Y;
+        const bool mine = ddu == (rr & (ND - 1));
+        // The register index rr / ND is uniform: a scalar branch per
+        // register (the empty asm keeps each one a branch rather than a
+        // select over every register) and one select per array.
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+          if (r == rr / ND) {
+            asm volatile("" ::: "memory");
+            xacc[r] = mine ? X : xacc[r];
+            yacc[r] = mine ? Y : yacc[r];
+          }
         }
       }
     }
