@@ -390,10 +390,11 @@ int bwd_impl(const sfa_attn* a, const void* q, const void* k, const void* v, con
   }
   {
     ProfileScope ps("bwd_key", stream);
-    rc = hip_status(launch_bwd_key(p, t, q, k, v, dout, dk, dv, ws, stream), "bwd key launch");
+    rc = hip_status(launch_bwd_key(p, t, q, k, v, dout, dk, dv, ws, base_f, alpha, dd, dtheta, stream),
+                    "bwd key launch");
     if (rc) return rc;
   }
-  if (dd || dtheta) {
+  if ((dd || dtheta) && !bwd_key_reduces(p, t, true)) {
     ProfileScope ps("bwd_reduce", stream);
     rc = hip_status(launch_bwd_reduce(t, ws, base_f, alpha, dd, dtheta, stream), "bwd reduce launch");
   }

@@ -490,6 +490,62 @@ constexpr int key_block(int esize, int G, int D) {
 }
 constexpr int key_cap(int kb) { return kb + 48; }
 
+struct ReduceArgs {
+  const float* dd_part;
+  float* dd;
+  float* dtheta;
+  int blocks, n_rungs;
+  double alpha;
+  float base[SFA_MAX_OFFSETS];
+};
+
+// dd and dtheta from the query pass's partials, by one workgroup of NT
+// threads.  The partials (one per query-pass workgroup) are stored
+// rung-major ([rung][block]), so wave w reduces rungs w, w + NT/64, ... with
+// coalesced loads: lane l adds the partials of blocks l, l+64, ... in block
+// order, then the wave adds its 64 lanes in a fixed shuffle tree, all in
+// double (a dd_k is a sum over every query and head of the batch, often a
+// near cancellation).  The order does not depend on NT or on timing.  sdd:
+// n_rungs doubles of LDS.
+__device__ __forceinline__ void reduce_body(const ReduceArgs& a, double* sdd, int nt) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int r = wave; r < a.n_rungs; r += nt / 64) {
+    double acc = 0.0;
+    const float* row = a.dd_part + size_t(r) * a.blocks;
+    int blk = lane;
+    for (; blk + 7 * 64 < a.blocks; blk += 8 * 64) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = row[blk + u * 64];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += double(x[u]);
+    }
+    for (; blk < a.blocks; blk += 64) acc += double(row[blk]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) acc += __shfl_xor(acc, m);
+    if (lane == 0) {
+      sdd[r] = acc;
+      if (a.dd) a.dd[r] = float(acc);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && a.dtheta) {
+    double da = 0.0;
+    for (int r = 0; r < a.n_rungs; ++r) da += double(a.base[r]) * sdd[r];
+    a.dtheta[0] = float((a.alpha - 0.5) * (1.5 - a.alpha) * da);
+  }
+}
+
+// The reduction as a kernel of its own (the float32 backward and the empty
+// problem), one workgroup of 16 waves.
+constexpr int kReduceThreads = 1024;
+
+__global__ __launch_bounds__(kReduceThreads) void bwd_reduce_kernel(ReduceArgs a) {
+  __shared__ double sdd[SFA_MAX_OFFSETS];
+  reduce_body(a, sdd, kReduceThreads);
+}
+
 // bf16 key pass: workgroups of 128 keys of two kinds in one launch, dK
 // (staging q~) and dV (staging dO).  Words per staged row: the chunk of
 // every head as f16 head pairs, plus a 4-word pad against bank conflicts.
@@ -1144,64 +1200,30 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
 // tiles, dispatched in that order, so dV workgroups start on the CUs that
 // dK workgroups leave instead of waiting for the slowest of them (page-1 key
 // pass 146 -> 137 us, Christoffel 298 -> 266 us against two launches).
+// With the offset gradient requested the launch leads with kNumXcd more
+// workgroups: the first reduces dd and dtheta (the query pass, which wrote
+// their partials, has finished), concurrently with the key tiles instead of
+// as a kernel after them; the others return at once, so every key tile
+// keeps its XCD.
 template <int D, int G>
-__global__ __launch_bounds__(kKeyBlockH16) void bwd_key_h16_kernel(BwdArgs a, SlotTable st) {
+__global__ __launch_bounds__(kKeyBlockH16) void bwd_key_h16_kernel(BwdArgs a, SlotTable st, ReduceArgs ra) {
+  int bid = blockIdx.x;
+  if (ra.n_rungs > 0) {
+    if (bid < kNumXcd) {
+      extern __shared__ __align__(16) uint32_t key_smem[];
+      if (bid == 0) reduce_body(ra, reinterpret_cast<double*>(key_smem), kKeyBlockH16);
+      return;
+    }
+    bid -= kNumXcd;
+  }
   if constexpr (G == 1) {
-    key_half_body<D, 1, 2>(a, st, xcd_tile(blockIdx.x, a.tiles));  // both halves
+    key_half_body<D, 1, 2>(a, st, xcd_tile(bid, a.tiles));  // both halves
   } else {
-    const int t2 = xcd_tile(blockIdx.x, 2 * a.tiles);
+    const int t2 = xcd_tile(bid, 2 * a.tiles);
     if (t2 < a.tiles)
       key_half_body<D, G, 0>(a, st, t2);
     else
       key_half_body<D, G, 1>(a, st, t2 - a.tiles);
-  }
-}
-
-struct ReduceArgs {
-  const float* dd_part;
-  float* dd;
-  float* dtheta;
-  int blocks, n_rungs;
-  double alpha;
-  float base[SFA_MAX_OFFSETS];
-};
-
-// One workgroup of 16 waves.  The partials (one per query-pass workgroup)
-// are stored rung-major ([rung][block]), so wave w reduces rungs w, w+16,
-// ... with coalesced loads: lane l adds the partials of blocks l, l+64, ...
-// in block order, then the wave adds its 64 lanes in a fixed shuffle tree,
-// all in double (a dd_k is a sum over every query and head of the batch,
-// often a near cancellation).  The result does not depend on timing.
-constexpr int kReduceThreads = 1024;
-
-__global__ __launch_bounds__(kReduceThreads) void bwd_reduce_kernel(ReduceArgs a) {
-  __shared__ double sdd[SFA_MAX_OFFSETS];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  for (int r = wave; r < a.n_rungs; r += kReduceThreads / 64) {
-    double acc = 0.0;
-    const float* row = a.dd_part + size_t(r) * a.blocks;
-    int blk = lane;
-    for (; blk + 7 * 64 < a.blocks; blk += 8 * 64) {
-      float x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = row[blk + u * 64];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc += double(x[u]);
-    }
-    for (; blk < a.blocks; blk += 64) acc += double(row[blk]);
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) acc += __shfl_xor(acc, m);
-    if (lane == 0) {
-      sdd[r] = acc;
-      if (a.dd) a.dd[r] = float(acc);
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0 && a.dtheta) {
-    double da = 0.0;
-    for (int r = 0; r < a.n_rungs; ++r) da += double(a.base[r]) * sdd[r];
-    a.dtheta[0] = float((a.alpha - 0.5) * (1.5 - a.alpha) * da);
   }
 }
 
@@ -1290,7 +1312,7 @@ int launch_query_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
 }
 
 template <typename T, int D, int G>
-int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
+int launch_key_t(const BwdArgs& a0, const SlotTable& t, const ReduceArgs* ra, hipStream_t st) {
   BwdArgs a = a0;
   if constexpr (sizeof(T) == 2) {
     constexpr int KB = kKeyBlockH16;
@@ -1298,8 +1320,12 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
     a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk_h16(D, G));
     a.kcap = key_half_cap(G, D);
     const size_t lds = size_t(a.kcap) * key_half_row_words(G, D) * 4;
-    const int grid = G == 1 ? a.tiles : 2 * a.tiles;  // G = 1: both halves in each workgroup
-    hipLaunchKernelGGL((bwd_key_h16_kernel<D, G>), dim3(grid), dim3(KB), lds, st, a, t);
+    static_assert(sizeof(double) * SFA_MAX_OFFSETS <= size_t(kKeyBlockH16 + 12) * 4 * key_half_row_words(G, D),
+                  "the reduce workgroup's doubles fit the key pass's LDS");
+    ReduceArgs r{};  // n_rungs = 0: no reduce workgroups
+    if (ra) r = *ra;
+    const int grid = (G == 1 ? a.tiles : 2 * a.tiles) + (r.n_rungs > 0 ? kNumXcd : 0);
+    hipLaunchKernelGGL((bwd_key_h16_kernel<D, G>), dim3(grid), dim3(KB), lds, st, a, t, r);
   } else {
     constexpr int KB = key_block(sizeof(T), G, D);
     a.nblk = (a.n + KB - 1) / KB;
@@ -1608,8 +1634,20 @@ int launch_bwd_query(const Problem& p, const SlotTable& t, const void* q, const 
   SFA_DISPATCH(launch_query_t, p, a, t, st);
 }
 
+void fill_reduce_args(ReduceArgs* a, const SlotTable& t, const BwdWorkspace& ws, const float* base_f, double alpha,
+                      float* dd, float* dtheta) {
+  a->dd_part = ws.dd_part;
+  a->dd = dd;
+  a->dtheta = dtheta;
+  a->blocks = ws.blocks;
+  a->n_rungs = t.n_rungs;
+  a->alpha = alpha;
+  for (int k = 0; k < t.n_rungs; ++k) a->base[k] = base_f[k];
+}
+
 int launch_bwd_key(const Problem& p, const SlotTable& t, const void* q, const void* k, const void* v,
-                   const void* dout, void* dk, void* dv, const BwdWorkspace& ws, void* stream) {
+                   const void* dout, void* dk, void* dv, const BwdWorkspace& ws, const float* base_f,
+                   double alpha, float* dd, float* dtheta, void* stream) {
   BwdArgs a = make_args(p, t, ws);
   a.q = q;
   a.k = k;
@@ -1618,19 +1656,21 @@ int launch_bwd_key(const Problem& p, const SlotTable& t, const void* q, const vo
   a.dk = dk;
   a.dv = dv;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  SFA_DISPATCH(launch_key_t, p, a, t, st);
+  // bf16: dd and dtheta are reduced by a leading workgroup of the key pass
+  ReduceArgs r{};
+  const bool fold = p.dtype == SFA_BF16 && (dd || dtheta) && t.n_rungs > 0;
+  if (fold) fill_reduce_args(&r, t, ws, base_f, alpha, dd, dtheta);
+  SFA_DISPATCH(launch_key_t, p, a, t, fold ? &r : nullptr, st);
+}
+
+bool bwd_key_reduces(const Problem& p, const SlotTable& t, bool want) {
+  return p.dtype == SFA_BF16 && want && t.n_rungs > 0;
 }
 
 int launch_bwd_reduce(const SlotTable& t, const BwdWorkspace& ws, const float* base_f, double alpha, float* dd,
                       float* dtheta, void* stream) {
   ReduceArgs a{};
-  a.dd_part = ws.dd_part;
-  a.dd = dd;
-  a.dtheta = dtheta;
-  a.blocks = ws.blocks;
-  a.n_rungs = t.n_rungs;
-  a.alpha = alpha;
-  for (int k = 0; k < t.n_rungs; ++k) a.base[k] = base_f[k];
+  fill_reduce_args(&a, t, ws, base_f, alpha, dd, dtheta);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, static_cast<hipStream_t>(stream), a);
   return int(hipGetLastError());
 }

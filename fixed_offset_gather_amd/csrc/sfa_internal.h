@@ -86,9 +86,14 @@ int launch_bwd_query(const Problem& p, const SlotTable& t, const void* q,
                      const void* k, const void* v, const float* lse,
                      const void* dout, void* dq, const BwdWorkspace& ws,
                      bool want_dd, void* stream);
+// With dd or dtheta requested the bf16 key pass also reduces them (see
+// bwd_key_reduces); otherwise base_f, alpha, dd and dtheta are unused.
 int launch_bwd_key(const Problem& p, const SlotTable& t, const void* q,
                    const void* k, const void* v, const void* dout, void* dk,
-                   void* dv, const BwdWorkspace& ws, void* stream);
+                   void* dv, const BwdWorkspace& ws, const float* base_f,
+                   double alpha, float* dd, float* dtheta, void* stream);
+// Whether launch_bwd_key reduces dd / dtheta itself (want: either is asked).
+bool bwd_key_reduces(const Problem& p, const SlotTable& t, bool want);
 int launch_bwd_reduce(const SlotTable& t, const BwdWorkspace& ws,
                       const float* base_f, double alpha, float* dd,
                       float* dtheta, void* stream);
