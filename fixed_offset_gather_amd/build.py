@@ -18,6 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsfa.so")
+PROBE = os.path.join(PKG, "lds_probe")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["sfa_api.hip", "sfa_fwd.hip", "sfa_bwd.hip", "sfa_noalloc.hip"]
@@ -83,6 +84,14 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError("libsfa link failed:\n" + r.stdout.decode(errors="replace"))
     os.replace(tmp, LIB)
+    # the LDS access-pattern calibration program used with the bank-conflict
+    # counters (not part of the library)
+    probe = [hipcc, os.path.join(CSRC, "lds_probe.hip"), "-o", PROBE] + [f for f in HIP_FLAGS if f != "-fPIC"]
+    if verbose:
+        print(" ".join(probe), flush=True)
+    r = subprocess.run(probe, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("lds_probe build failed:\n" + r.stdout.decode(errors="replace"))
     return LIB
 
 
