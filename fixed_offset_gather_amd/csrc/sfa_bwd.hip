@@ -26,10 +26,12 @@
 //   form contiguous ranges, so each lane gathers instead of scattering.
 //   fp32: one kernel; dK uses the relative rotation R(j)^T R(i) = R(i-j)
 //   with i-j fixed per (slot, tap), so unrotated Q rows are combined first
-//   and rotated once.  bf16: one launch of dK and dV workgroups, each
-//   staging half a query row into an LDS ring of rows that consecutive
-//   stages share.
-// bwd_reduce: sums the dd partials in block order (in double);
+//   and rotated once.  bf16: one launch of dK and dV workgroups (both in
+//   one workgroup with one head per KV head) staging query rows into an LDS
+//   ring of rows that consecutive stages share; with dd or dtheta asked,
+//   a leading workgroup of the same launch does the reduction below.
+// The dd reduction (reduce_body; a kernel of its own, bwd_reduce, for the
+//   fp32 backward): sums the partials in block order (in double);
 //   dalpha = sum f_k dd_k; dtheta = (alpha - 1/2)(3/2 - alpha) dalpha.
 // The edge-list backward (bwd_edges_query, bwd_edges_key, further below)
 // does the same per query and per key over explicit lists.

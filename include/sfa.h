@@ -298,7 +298,8 @@ size_t sfa_bwd_workspace_bytes(const sfa_attn* a);
  * [B, n, Hkv, D] in dtype (overwritten).  dd: optional device float
  * [n_off], dd[k] = dL/dd_k inside the current interpolation cell (the
  * derivative of the row pair: row(i-lo-1) - row(i-lo), taken also when
- * frac = 0).  dtheta: optional device float scalar, (alpha - 1/2)(3/2 -
+ * frac = 0), formed from float32 operands and summed in double for either
+ * dtype.  dtheta: optional device float scalar, (alpha - 1/2)(3/2 -
  * alpha) * sum_k base[k] dd[k] ([P1] alpha parameterisation); needs base
  * (host int32 [n_off], the unscaled rungs) and alpha.  workspace: device
  * buffer of at least sfa_bwd_workspace_bytes(a) bytes, 16-byte aligned,
@@ -330,10 +331,6 @@ int sfa_bwd_noalloc(const sfa_attn* a, const void* q, const void* k, const void*
                     float* dd, const int32_t* base, double alpha, float* dtheta,
                     void* stream);
 
-/* ------------------------------------------------------------------ */
-/* Kernel timing (measurement support; off by default)                  */
-/* ------------------------------------------------------------------ */
-
 /*
  * Backward of sfa_fwd_edges for L = <O, dO> (training with the per-query
  * masks: [P2] item 4, [P3]).  edges/count: the device lists of the forward;
@@ -352,12 +349,17 @@ int sfa_bwd_edges(const sfa_attn* a, const int32_t* edges, const int32_t* count,
                   const void* k, const void* v, const float* lse, const void* dout, void* dq,
                   void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------ */
+/* Kernel timing (measurement support; off by default)                  */
+/* ------------------------------------------------------------------ */
+
 /*
  * When enabled, every kernel launch is bracketed by two HIP events recorded
  * on its launch stream.  sfa_profile_read synchronises the recorded events
  * and returns the accumulated milliseconds and launch count of the named
  * kernel ("fwd_offsets", "fwd_edges", "bwd_query", "bwd_key",
- * "bwd_edges_query", "bwd_edges_key", "bwd_reduce");
+ * "bwd_edges_query", "bwd_edges_key", "bwd_reduce"; with bf16 tensors the
+ * dd reduction runs inside the "bwd_key" launch);
  * sfa_profile_reset drops all records.  sfa_profile_select(name) restricts
  * the recording to the launches of the named kernel (each recorded launch
  * adds two event packets to its stream, which also delay the stream's next
