@@ -507,16 +507,18 @@ __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Sl
 #pragma unroll
             for (int x = 0; x < DW; ++x) vw[x] = lerp_h2(vw[x], vb[x], w2);
           }
-          // Each value element is widened to fp32 once and then feeds G
-          // plain fp32 FMAs; the empty asm keeps the widening from being
-          // folded back into G mixed-precision FMAs, which issue at half
-          // the rate.
+          // With G >= 2 heads each value element is widened to fp32 once
+          // and then feeds G plain fp32 FMAs; the empty asm keeps the
+          // widening from being folded back into G mixed-precision FMAs,
+          // which issue at half the rate.  With one head the element feeds
+          // one FMA, and the folded form (one v_fma_mix_f32 instead of a
+          // conversion and an FMA) is the cheaper one.
           float vf[DC];
 #pragma unroll
           for (int x = 0; x < DW; ++x) {
             vf[2 * x] = float(as_h2(vw[x]).x);
             vf[2 * x + 1] = float(as_h2(vw[x]).y);
-            asm volatile("" : "+v"(vf[2 * x]), "+v"(vf[2 * x + 1]));
+            if constexpr (G >= 2) asm volatile("" : "+v"(vf[2 * x]), "+v"(vf[2 * x + 1]));
           }
 #pragma unroll
           for (int h = 0; h < G; ++h)
