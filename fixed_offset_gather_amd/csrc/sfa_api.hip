@@ -304,7 +304,7 @@ extern "C" size_t sfa_bwd_edges_workspace_bytes(const sfa_attn* a, int width) {
     fail(SFA_ERR_ARG, "sfa_bwd_edges_workspace_bytes: width must be in [1, %d]", SFA_MAX_EDGE_WIDTH);
     return 0;
   }
-  return bwd_edges_workspace_layout(p, width, nullptr, nullptr, nullptr, nullptr);
+  return bwd_edges_workspace_layout(p, width, nullptr, nullptr, nullptr, nullptr, nullptr);
 }
 
 extern "C" int sfa_bwd_edges(const sfa_attn* a, const int32_t* edges, const int32_t* count, int width,
@@ -328,7 +328,7 @@ extern "C" int sfa_bwd_edges(const sfa_attn* a, const int32_t* edges, const int3
       (reinterpret_cast<uintptr_t>(count) & 3u) || (reinterpret_cast<uintptr_t>(inv) & 3u) ||
       (reinterpret_cast<uintptr_t>(inv_count) & 3u))
     return fail(SFA_ERR_ARG, "sfa_bwd_edges: misaligned pointer");
-  const size_t need = bwd_edges_workspace_layout(p, width, nullptr, nullptr, nullptr, nullptr);
+  const size_t need = bwd_edges_workspace_layout(p, width, nullptr, nullptr, nullptr, nullptr, nullptr);
   if (!workspace || ws_bytes < need || !aligned16(workspace))
     return fail(SFA_ERR_CAPACITY, "sfa_bwd_edges: workspace needs %zu bytes (16-byte aligned), got %zu", need,
                 ws_bytes);

@@ -13,8 +13,12 @@
 //   rounded forward output), and dq~ = scale sum p (dp - Dvec) k~ is
 //   accumulated as scale (sum p dp k~ - Dvec sum p k~), then rotated back to
 //   dQ.  The per-slot dot sums over a query's lanes are a reduce-scatter
-//   over the heads (HeadSlice).  p (0 where the slot has no row), dp and
-//   Dvec of every (query, slot, head) go to the workspace.  The offset
+//   over the heads (HeadSlice).  Every p is taken relative to l = sum_slots
+//   p (1 up to the forward's lse, whose f16 logits are off by an amount
+//   that grows with the logits): dQ, Dvec and, through 1/l stored beside p,
+//   the key pass use p / l, the softmax of the fp32 logits.  p (0 where the
+//   slot has no row), dp, Dvec / l and 1/l of every (query, slot, head) go
+//   to the workspace.  The offset
 //   gradient is formed here too, from the fp32 rows and weights: for rung k
 //   and query head (i, h), dd_k gets scale dS (q~ . dK) + p (dO . dV) with
 //   dK = Kr[i-lo-1] - Kr[i-lo] and dV likewise; written as
@@ -67,7 +71,8 @@ struct BwdArgs {
   void* dv;
   float* P;
   float* dP;
-  float* Dvec;
+  float* Dvec;   // Dvec / l per (query, head)
+  float* Linv;   // 1 / l per (query, head), l = sum_slots p
   float* dd_part;
   uint32_t* xq;  // packed key-pass rows (see BwdWorkspace), or null
   uint32_t* xd;
@@ -408,13 +413,19 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
       }
     }
   }
-  if (active && HS::writer(c)) a.Dvec[(size_t(seq) * n + i) * G + own] = dvec;
+  // p relative to l = sum p: dvn = Dvec / l is Dvec of the normalised p
+  const float linv = psum > 0.f ? 1.f / psum : 0.f;
+  const float dvn = dvec * linv;
+  if (active && HS::writer(c)) {
+    a.Dvec[(size_t(seq) * n + i) * G + own] = dvn;
+    a.Linv[(size_t(seq) * n + i) * G + own] = linv;
+  }
   if constexpr (kBound) {
-    // |dS| / scale = |p dp - p Dvec| <= |p dp| + psum |Dvec| (every p <=
-    // sum p): the workgroup's maximum of that bound, for the key pass
+    // |dS| / scale = |p/l (dp - dvn)| <= |p dp| / l + |dvn| (every p <= l):
+    // the workgroup's maximum of that bound, for the key pass
     if (a.wmax) {
       __shared__ float wbw[NWV];
-      float u = umax + psum * fabsf(dvec);
+      float u = fmaf(umax, linv, fabsf(dvn));
 #pragma unroll
       for (int m = 1; m < 64; m <<= 1) u = fmaxf(u, __shfl_xor(u, m));
       if ((tid & 63) == 0) wbw[tid >> 6] = u;
@@ -439,8 +450,6 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
     // one, as the exact softmax does.
     __shared__ float ddw[NWV][RW_DD];
     const int lane = tid & 63, wave = tid >> 6;
-    const float linv = psum > 0.f ? 1.f / psum : 0.f;
-    const float dvn = dvec * linv;
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
       float t = linv * fmaf(-dvn, xacc[r], yacc[r]);
@@ -457,15 +466,17 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
       a.dd_part[size_t(a.r0 + r) * a.tiles + tile] = t;
     }
   }
-  float dvh[G];
-  HS::bcast(dvec, dvh);
+  // dq~ = scale / l (sum p dp k~ - dvn sum p k~)
+  float dvh[G], slh[G];
+  HS::bcast(dvn, dvh);
+  HS::bcast(a.scale * linv, slh);
   if (active) {
     T* dQ = static_cast<T*>(a.dq);
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       float dq[DC];
 #pragma unroll
-      for (int x = 0; x < DC; ++x) dq[x] = a.scale * fmaf(-dvh[j], acc_p[j][x], acc_pd[j][x]);
+      for (int x = 0; x < DC; ++x) dq[x] = slh[j] * fmaf(-dvh[j], acc_p[j][x], acc_pd[j][x]);
       if (a.rope) rotate_pairs<DC, -1>(dq, a.rope + size_t(i) * D, c * DC);
       store_vec<DC>(dQ + ((size_t(b) * n + i) * a.hq + size_t(g) * G + HS::head(c, j)) * D + c * DC, dq);
     }
@@ -652,13 +663,18 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
       const int i = j + st.s[sj].lo + tap;
       return activej && i >= 0 && i < n && (tap == 1 || j > 0 || w == 0.f);
     };
+    // p is loaded as p / l (times the stored 1/l of its query and head)
     auto load_step = [&](int sj, int tap, float (&pg)[G], float (&dpg)[G], float (&dvg)[G]) {
       if (step_valid(sj, tap)) {
         const int i = j + st.s[sj].lo + tap;
         const size_t widx = ((ws_seq + sj) * n + i) * G;
+        float lg[G];
         load_vec<G>(a.P + widx, pg);
         load_vec<G>(a.dP + widx, dpg);
         load_vec<G>(a.Dvec + (size_t(seq) * n + i) * G, dvg);
+        load_vec<G>(a.Linv + (size_t(seq) * n + i) * G, lg);
+#pragma unroll
+        for (int h = 0; h < G; ++h) pg[h] *= lg[h];
       } else {
 #pragma unroll
         for (int h = 0; h < G; ++h) pg[h] = dpg[h] = dvg[h] = 0.f;
@@ -850,12 +866,13 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   }
   auto slot_lo = [&](int sj) { return min(st.s[sj].lo, n); };  // stage bounds only
 
-  // p (and for dK dp and Dvec) of one (slot, tap) step, loaded without a
-  // branch: the row is clamped to n - 1, and every clamped row is one the
-  // query pass wrote (a slot is only reached while j0 + lo <= n - 1).  A
-  // step past the end reloads the last slot's rows; masked steps get zero
-  // weights in convert().
-  constexpr int NR = PART == 1 ? 1 : 3;
+  // p and 1/l (and for dK dp and Dvec / l) of one (slot, tap) step, loaded
+  // without a branch: the row is clamped to n - 1, and every clamped row is
+  // one the query pass wrote (a slot is only reached while j0 + lo <= n - 1).
+  // A step past the end reloads the last slot's rows; masked steps get zero
+  // weights in convert().  raw: p, 1/l (dV); p, dp, Dvec / l, 1/l (dK).
+  constexpr int NR = PART == 1 ? 2 : 4;
+  constexpr int RL = NR - 1;  // the 1/l entry
   constexpr int NWT = BOTH ? 2 : GW;  // weight words per step
   // Scalar bases of this sequence's p, dp and Dvec; a slot's plane is a
   // scalar byte offset from them (advanced by one plane per slot), the row a
@@ -863,6 +880,7 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   const float* const Pseq = uniform_ptr(a.P + size_t(seq) * a.S * n * G);
   const float* const dPseq = uniform_ptr(a.dP + size_t(seq) * a.S * n * G);
   const float* const Dseq = uniform_ptr(a.Dvec + size_t(seq) * n * G);
+  const float* const Lseq = uniform_ptr(a.Linv + size_t(seq) * n * G);
   const unsigned plane_b = unsigned(n) * unsigned(G * 4);
   // the prefetch cursor: step (fs, ft), its slot's min(lo, n), taps and
   // fraction, and the byte offset of its slot's plane (kept at the last
@@ -890,6 +908,7 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
       load_global_at<G>(dPseq, fplane + ioff, q.raw[1]);
       load_global_at<G>(Dseq, ioff, q.raw[2]);
     }
+    load_global_at<G>(Lseq, ioff, q.raw[RL]);
     const bool valid = fs < S && unsigned(j + flo + ft) < unsigned(n);
     const float wt = ft ? fw : 1.f - fw;
     q.ws = valid ? wt : 0.f;
@@ -897,11 +916,11 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
     q.delta = flo + ft;
   };
   // f16 weight pairs of a queued step (G = 1: one fp32 weight): ws dS, dS =
-  // p (dp - Dvec), for dK, ws p for dV.  Every loaded value is finite (a
-  // clamped row the query pass wrote), so a masked step's ws = 0 gives 0.
+  // p/l (dp - Dvec/l), for dK, ws p/l for dV.  Every loaded value is finite
+  // (a clamped row the query pass wrote), so a masked step's ws = 0 gives 0.
   auto convert = [&](const QE& q, uint32_t (&wts)[NWT]) {
     if constexpr (BOTH) {
-      const float p = q.ws * q.raw[0][0];
+      const float p = q.ws * q.raw[0][0] * q.raw[RL][0];
       wts[0] = __float_as_uint(a.scale * p * (q.raw[1][0] - q.raw[2][0]));
       wts[1] = __float_as_uint(p);
     } else {
@@ -909,7 +928,7 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
 #pragma unroll
       for (int hp = 0; hp < GW; ++hp) {
         const int h0 = 2 * hp, h1 = 2 * hp + 1 < G ? 2 * hp + 1 : 2 * hp;
-        float w0 = q.raw[0][h0], w1 = 2 * hp + 1 < G ? q.raw[0][h1] : 0.f;
+        float w0 = q.raw[0][h0] * q.raw[RL][h0], w1 = 2 * hp + 1 < G ? q.raw[0][h1] * q.raw[RL][h1] : 0.f;
         if constexpr (PART == 0) {
           w0 = ws * w0 * (q.raw[1][h0] - q.raw[2][h0]);
           w1 = ws * w1 * (q.raw[1][h1] - q.raw[2][h1]);
@@ -1259,6 +1278,7 @@ BwdArgs make_args(const Problem& p, const SlotTable& t, const BwdWorkspace& ws) 
   a.P = ws.p;
   a.dP = ws.dp;
   a.Dvec = ws.dvec;
+  a.Linv = ws.linv;
   a.dd_part = ws.dd_part;
   a.xq = ws.xq;
   a.xd = ws.xd;
@@ -1382,7 +1402,8 @@ struct EdgeBwdArgs {
   void* dv;
   float* P;     // [B*Hkv][n][width][G]
   float* dP;    // [B*Hkv][n][width][G]
-  float* Dvec;  // [B*Hkv][n][G]
+  float* Dvec;  // [B*Hkv][n][G] Dvec / l
+  float* Linv;  // [B*Hkv][n][G] 1 / l, l = sum over the list of p
   const float* rope;
   const int32_t* edges;
   const int32_t* count;
@@ -1441,6 +1462,7 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
   const int32_t* erow = a.edges + size_t(active ? i : 0) * a.width;
   const size_t wrow = (size_t(seq) * n + (active ? i : 0)) * a.width;
   float dvec = 0.f;
+  float psum = 0.f;  // l = sum p (1 up to the forward's lse)
 
   // Branch-free over the wave's longest list, the next list entry read one
   // step ahead: a padding entry (or a key outside [0, n)) reads row 0 and is
@@ -1461,6 +1483,7 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
     const float p = valid ? ex : 0.f;
     const float pdp = p * dp;
     dvec += pdp;
+    psum += p;
     if (valid && HS::writer(c)) {
       a.P[(wrow + t) * G + own] = p;
       a.dP[(wrow + t) * G + own] = dp;
@@ -1477,16 +1500,23 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
       }
   }
 
-  if (active && HS::writer(c)) a.Dvec[(size_t(seq) * n + i) * G + own] = dvec;
-  float dvh[G];
-  HS::bcast(dvec, dvh);
+  // p relative to l = sum p, as in the offset query pass
+  const float linv = psum > 0.f ? 1.f / psum : 0.f;
+  const float dvn = dvec * linv;
+  if (active && HS::writer(c)) {
+    a.Dvec[(size_t(seq) * n + i) * G + own] = dvn;
+    a.Linv[(size_t(seq) * n + i) * G + own] = linv;
+  }
+  float dvh[G], slh[G];
+  HS::bcast(dvn, dvh);
+  HS::bcast(a.scale * linv, slh);
   if (active) {
     T* dQ = static_cast<T*>(a.dq);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float dq[DC];
 #pragma unroll
-      for (int x = 0; x < DC; ++x) dq[x] = a.scale * fmaf(-dvh[h], acc_p[h][x], acc_pd[h][x]);
+      for (int x = 0; x < DC; ++x) dq[x] = slh[h] * fmaf(-dvh[h], acc_p[h][x], acc_pd[h][x]);
       if (a.rope) rotate_pairs<DC, -1>(dq, a.rope + size_t(i) * D, c * DC);
       store_vec<DC>(dQ + ((size_t(b) * n + i) * a.hq + size_t(g) * G + HS::head(c, h)) * D + c * DC, dq);
     }
@@ -1536,10 +1566,13 @@ __global__ __launch_bounds__(kEdgeKB) void bwd_edges_key_kernel(EdgeBwdArgs a) {
     const int ec = ok ? e : 0;
     const int i = ec / a.width, t = ec - i * a.width;
     const size_t w = ((size_t(seq) * n + i) * a.width + t) * G;
-    float pg[G], dpg[G], dvg[G];
+    float pg[G], dpg[G], dvg[G], lg[G];
     load_vec<G>(a.P + w, pg);
     load_vec<G>(a.dP + w, dpg);
     load_vec<G>(a.Dvec + (size_t(seq) * n + i) * G, dvg);
+    load_vec<G>(a.Linv + (size_t(seq) * n + i) * G, lg);
+#pragma unroll
+    for (int h = 0; h < G; ++h) pg[h] *= lg[h];  // p / l
     float yk[KC], yv[KC];
 #pragma unroll
     for (int x = 0; x < KC; ++x) yk[x] = yv[x] = 0.f;
@@ -1613,11 +1646,12 @@ size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base, Bw
   ws->p = f;
   ws->dp = f ? f + pe : nullptr;
   ws->dvec = f ? f + 2 * pe : nullptr;
-  ws->dd_part = f ? f + 2 * pe + de : nullptr;
-  ws->xq = (f && xe) ? reinterpret_cast<uint32_t*>(f + 2 * pe + de + dd_e) : nullptr;
-  ws->xd = (f && xe) ? reinterpret_cast<uint32_t*>(f + 2 * pe + de + dd_e + xe) : nullptr;
-  ws->wmax = (f && we) ? f + 2 * pe + de + dd_e + 2 * xe : nullptr;
-  ws->bytes = (2 * pe + de + dd_e + 2 * xe + we) * sizeof(float);
+  ws->linv = f ? f + 2 * pe + de : nullptr;
+  ws->dd_part = f ? f + 2 * pe + 2 * de : nullptr;
+  ws->xq = (f && xe) ? reinterpret_cast<uint32_t*>(f + 2 * pe + 2 * de + dd_e) : nullptr;
+  ws->xd = (f && xe) ? reinterpret_cast<uint32_t*>(f + 2 * pe + 2 * de + dd_e + xe) : nullptr;
+  ws->wmax = (f && we) ? f + 2 * pe + 2 * de + dd_e + 2 * xe : nullptr;
+  ws->bytes = (2 * pe + 2 * de + dd_e + 2 * xe + we) * sizeof(float);
   return ws->bytes;
 }
 
@@ -1677,7 +1711,8 @@ int launch_bwd_reduce(const SlotTable& t, const BwdWorkspace& ws, const float* b
   return int(hipGetLastError());
 }
 
-size_t bwd_edges_workspace_layout(const Problem& p, int width, void* base, float** P, float** dP, float** Dvec) {
+size_t bwd_edges_workspace_layout(const Problem& p, int width, void* base, float** P, float** dP, float** Dvec,
+                                  float** Linv) {
   auto al = [](size_t e) { return (e + 63) & ~size_t(63); };
   const size_t pe = al(size_t(p.B) * p.hkv * size_t(p.n) * size_t(width) * p.G);
   const size_t de = al(size_t(p.B) * p.hkv * size_t(p.n) * p.G);
@@ -1685,7 +1720,8 @@ size_t bwd_edges_workspace_layout(const Problem& p, int width, void* base, float
   if (P) *P = f;
   if (dP) *dP = f ? f + pe : nullptr;
   if (Dvec) *Dvec = f ? f + 2 * pe : nullptr;
-  return (2 * pe + de) * sizeof(float);
+  if (Linv) *Linv = f ? f + 2 * pe + de : nullptr;
+  return (2 * pe + 2 * de) * sizeof(float);
 }
 
 int launch_bwd_edges(const Problem& p, const int32_t* edges, const int32_t* count, int width, const int32_t* inv,
@@ -1701,7 +1737,7 @@ int launch_bwd_edges(const Problem& p, const int32_t* edges, const int32_t* coun
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  bwd_edges_workspace_layout(p, width, workspace, &a.P, &a.dP, &a.Dvec);
+  bwd_edges_workspace_layout(p, width, workspace, &a.P, &a.dP, &a.Dvec, &a.Linv);
   a.rope = p.rope;
   a.edges = edges;
   a.count = count;

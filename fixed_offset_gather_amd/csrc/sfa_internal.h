@@ -55,7 +55,8 @@ int launch_fwd_edges(const Problem& p, const int32_t* edges,
 struct BwdWorkspace {
   float* p;        // [B][Hkv][S][n][G] softmax probabilities (0 where a slot has no row)
   float* dp;       // [B][Hkv][S][n][G] dO . v~
-  float* dvec;     // [B][Hkv][n][G] rowsum(dO * O) = sum_slots p dp
+  float* dvec;     // [B][Hkv][n][G] rowsum(dO * O) of p / l: (sum_slots p dp) / l
+  float* linv;     // [B][Hkv][n][G] 1 / l, l = sum_slots p (1 up to the forward's lse)
   float* dd_part;  // [n_rungs][blocks] per-block partial sums of dL/dd_k (one per query-pass workgroup)
   // bf16 with G >= 2: the query pass's rows for the key pass, as f16 head
   // pairs in the key pass's LDS row layout, [B][Hkv][n][D/16][G/2][16] words
@@ -73,10 +74,11 @@ struct BwdWorkspace {
 size_t bwd_workspace_layout(const Problem& p, const SlotTable& t, void* base,
                             BwdWorkspace* ws);
 
-// Edge-list backward: workspace p, dp [B*Hkv][n][width][G] and Dvec
-// [B*Hkv][n][G] (floats); returns its size in bytes.
+// Edge-list backward: workspace p, dp [B*Hkv][n][width][G], Dvec / l and
+// 1 / l [B*Hkv][n][G] (floats; l = sum over the list of p); returns its size
+// in bytes.
 size_t bwd_edges_workspace_layout(const Problem& p, int width, void* base, float** P, float** dP,
-                                  float** Dvec);
+                                  float** Dvec, float** Linv);
 int launch_bwd_edges(const Problem& p, const int32_t* edges, const int32_t* count, int width,
                      const int32_t* inv, const int32_t* inv_count, int inv_width, const void* q,
                      const void* k, const void* v, const float* lse, const void* dout, void* dq,

@@ -172,7 +172,7 @@ def test_bwd_validation_and_workspace_size():
     S = 10 + 1 + 15
     al = lambda e: (e + 63) // 64 * 64
     pe = al(2 * 2 * S * 100 * 4)          # p and dp: [B][Hkv][S][n][G]
-    de = al(2 * 2 * 100 * 4)              # Dvec: [B][Hkv][n][G]
+    de = al(2 * 2 * 100 * 4)              # Dvec / l and 1 / l: [B][Hkv][n][G] each
     # dd partials: one per query-pass workgroup (32-query blocks at 4 heads
     # per KV head, x B x Hkv)
     blocks = 4 * 2 * 2
@@ -181,7 +181,7 @@ def test_bwd_validation_and_workspace_size():
     xe = al(2 * 2 * 100 * 64 * 2)
     # bounds on |dS| (bf16, G >= 2): one per query-pass workgroup
     we = al(blocks)
-    assert nb == (2 * pe + de + dd + 2 * xe + we) * 4
+    assert nb == (2 * pe + 2 * de + dd + 2 * xe + we) * 4
     assert lib.sfa_bwd_workspace_bytes(ctypes.byref(_prob(head_dim=48))) == 0
     base = sfa.base_fib()
     bp = base.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
@@ -246,7 +246,8 @@ def test_bwd_edges_validation_and_workspace_size():
     a = _prob(batch=2, seqlen=100, hq=4, hkv=4)
     al = lambda e: (e + 63) // 64 * 64
     nb = lib.sfa_bwd_edges_workspace_bytes(ctypes.byref(a), 64)
-    assert nb == (2 * al(2 * 4 * 100 * 64 * 1) + al(2 * 4 * 100 * 1)) * 4
+    # p, dp [B*Hkv][n][width][G]; Dvec / l and 1 / l [B*Hkv][n][G]
+    assert nb == (2 * al(2 * 4 * 100 * 64 * 1) + 2 * al(2 * 4 * 100 * 1)) * 4
     assert lib.sfa_bwd_edges_workspace_bytes(ctypes.byref(a), 0) == 0
     t = [FAKE] * 8  # q, k, v, lse, dout, dq, dk, dv
     call = lambda width, invw, ws, wsb, ptrs=t, e=FAKE: lib.sfa_bwd_edges(
