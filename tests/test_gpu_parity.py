@@ -276,16 +276,32 @@ def test_offsets_beyond_sequence_are_masked():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_maximum_slot_count(dtype):
-    # 192 slots (128 offsets, a third of them integer, plus a window of 63)
-    # with 4 query heads per KV head: the key pass's three-column slot table,
-    # and dd of 128 rungs in the query pass, more than one launch's rung
-    # window holds (64 at this shape), so two launches each sum a window.
+    # The full table: 320 slots, the maximum 256 offsets (a third of them
+    # integer) plus a window of 63, with 4 query heads per KV head: the
+    # forward's LDS copy of the table, the key pass's five 64-slot columns,
+    # and dd of 256 rungs in the query pass, four launches of a 64-rung
+    # window each.
     sfa = _sfa()
     rng = np.random.default_rng(0)
+    lo = rng.integers(0, 300, size=sfa.MAX_OFFSETS).astype(np.int32)
+    fr = rng.random(sfa.MAX_OFFSETS).astype(np.float32)
+    fr[::3] = 0.0
+    case = Case(1, 260, 8, 2, 64, dtype, seed=37)
+    W = sfa.MAX_SLOTS - 1 - sfa.MAX_OFFSETS
+    _fwd_check(case, W, lo, fr)
+    _bwd_check(case, W, lo, fr, 1.0, np.ones(sfa.MAX_OFFSETS, dtype=np.int32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_maximum_window(dtype):
+    # 320 slots as a window of 191 and 128 offsets: stages of up to 128 rows
+    # hold many window slots, and two 64-rung dd windows.
+    sfa = _sfa()
+    rng = np.random.default_rng(1)
     lo = rng.integers(0, 300, size=128).astype(np.int32)
     fr = rng.random(128).astype(np.float32)
     fr[::3] = 0.0
-    case = Case(1, 260, 8, 2, 64, dtype, seed=37)
+    case = Case(1, 260, 8, 2, 64, dtype, seed=38)
     W = sfa.MAX_SLOTS - 1 - 128
     _fwd_check(case, W, lo, fr)
     _bwd_check(case, W, lo, fr, 1.0, np.ones(128, dtype=np.int32))
