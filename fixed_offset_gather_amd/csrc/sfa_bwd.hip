@@ -1464,19 +1464,29 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
   float dvec = 0.f;
   float psum = 0.f;  // l = sum p (1 up to the forward's lse)
 
-  // Branch-free over the wave's longest list, the next list entry read one
-  // step ahead: a padding entry (or a key outside [0, n)) reads row 0 and is
-  // masked by p = 0.
-  int key_next = cnt > 0 ? erow[0] : -1;
+  // Branch-free over the wave's longest list: a padding entry (or a key
+  // outside [0, n)) reads row 0 and is masked by p = 0.  Software pipeline:
+  // the K and V rows of entry t + 1 are loaded while entry t is computed,
+  // and the list entry t + 2 is read with them, so neither the rows' nor
+  // the index's L2 latency sits on the step's dependency chain.
+  auto row_of = [&](int t) {
+    const int key = t < cnt ? erow[t] : -1;
+    return (key >= 0 && key < n) ? key : -1;  // -1: masked
+  };
+  int key = row_of(0);
+  int key_next = row_of(1);
+  float kt[DC], vt[DC];
+  load_vec<DC>(Kseq + size_t(max(key, 0)) * kv_row, kt);
+  load_vec<DC>(Vseq + size_t(max(key, 0)) * kv_row, vt);
   for (int t = 0; t < cmax; ++t) {
-    const int key = key_next;
-    key_next = t + 1 < cnt ? erow[t + 1] : -1;
-    const bool valid = key >= 0 && key < n;
+    const bool valid = key >= 0;
     const int kc = valid ? key : 0;
-    float kt[DC], vt[DC];
-    load_vec<DC>(Kseq + size_t(kc) * kv_row, kt);
+    // the next entry's rows and the entry after it
+    const int key_after = row_of(t + 2);
+    float kn[DC], vn[DC];
+    load_vec<DC>(Kseq + size_t(max(key_next, 0)) * kv_row, kn);
+    load_vec<DC>(Vseq + size_t(max(key_next, 0)) * kv_row, vn);
     if (a.rope) rotate_pairs<DC, 1>(kt, a.rope + size_t(kc) * D, c * DC);
-    load_vec<DC>(Vseq + size_t(kc) * kv_row, vt);
     const float sdot = own_dot<G, LPQ, DC>(qv, kt);
     const float dp = own_dot<G, LPQ, DC>(dov, vt);
     const float ex = __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2);
@@ -1498,6 +1508,13 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
         acc_pd[h][x] = fmaf(pdh[h], kt[x], acc_pd[h][x]);
         acc_p[h][x] = fmaf(ph[h], kt[x], acc_p[h][x]);
       }
+#pragma unroll
+    for (int x = 0; x < DC; ++x) {
+      kt[x] = kn[x];
+      vt[x] = vn[x];
+    }
+    key = key_next;
+    key_next = key_after;
   }
 
   // p relative to l = sum p, as in the offset query pass
@@ -1553,37 +1570,67 @@ __global__ __launch_bounds__(kEdgeKB) void bwd_edges_key_kernel(EdgeBwdArgs a) {
   float ak[KC], av[KC];
 #pragma unroll
   for (int x = 0; x < KC; ++x) ak[x] = av[x] = 0.f;
-  // Branch-free over the wave's longest list: the next entry of the list is
-  // read one iteration ahead, so each entry costs one round trip (its P, dP,
-  // Dvec, Q and dO rows, all addressed by the entry) rather than two; an
-  // entry past the lane's count, or one that is not a slot of the table,
-  // reads slot 0 and enters with zero weights.
-  int e_next = cnt > 0 ? irow[0] : -1;
-  for (int u = 0; u < cmax; ++u) {
-    const int e = e_next;
-    e_next = u + 1 < cnt ? irow[u + 1] : -1;
-    const bool ok = e >= 0 && e < nslots;
-    const int ec = ok ? e : 0;
-    const int i = ec / a.width, t = ec - i * a.width;
-    const size_t w = ((size_t(seq) * n + i) * a.width + t) * G;
+  // Branch-free over the wave's longest list: an entry past the lane's
+  // count, or one that is not a slot of the table, reads slot 0 and enters
+  // with zero weights.  Software pipeline: the loads of entry u + 1 (its P,
+  // dP, Dvec, 1/l and, with one head per KV head, its Q and dO rows, all
+  // addressed by the entry) are issued before entry u is computed, and the
+  // list entry u + 2 with them, so their L2 latency overlaps entry u's work.
+  // (With more heads the rows of two entries would not fit the registers;
+  // there the weights are loaded ahead and the rows in the step.)
+  constexpr bool kRowsAhead = G == 1;
+  struct Ent {
+    int i;
+    bool ok;
     float pg[G], dpg[G], dvg[G], lg[G];
-    load_vec<G>(a.P + w, pg);
-    load_vec<G>(a.dP + w, dpg);
-    load_vec<G>(a.Dvec + (size_t(seq) * n + i) * G, dvg);
-    load_vec<G>(a.Linv + (size_t(seq) * n + i) * G, lg);
-#pragma unroll
-    for (int h = 0; h < G; ++h) pg[h] *= lg[h];  // p / l
+    float qx[kRowsAhead ? KC : 1], ox[kRowsAhead ? KC : 1];
+  };
+  auto entry_at = [&](int u) { return u < cnt ? irow[u] : -1; };
+  auto load_ent = [&](int e, Ent& x) {
+    x.ok = e >= 0 && e < nslots;
+    const int ec = x.ok ? e : 0;
+    x.i = ec / a.width;
+    const int t = ec - x.i * a.width;
+    const size_t w = ((size_t(seq) * n + x.i) * a.width + t) * G;
+    load_vec<G>(a.P + w, x.pg);
+    load_vec<G>(a.dP + w, x.dpg);
+    load_vec<G>(a.Dvec + (size_t(seq) * n + x.i) * G, x.dvg);
+    load_vec<G>(a.Linv + (size_t(seq) * n + x.i) * G, x.lg);
+    if constexpr (kRowsAhead) {
+      const size_t off = ((size_t(b) * n + x.i) * a.hq + size_t(g) * G) * D + c * KC;
+      load_vec<KC>(Q + off, x.qx);
+      load_vec<KC>(dO + off, x.ox);
+    }
+  };
+  Ent cur;
+  load_ent(entry_at(0), cur);
+  int e_after = entry_at(1);
+  for (int u = 0; u < cmax; ++u) {
+    Ent nxt;
+    const int e_next = e_after;
+    e_after = entry_at(u + 2);
+    load_ent(e_next, nxt);
+    const int i = cur.i;
     float yk[KC], yv[KC];
 #pragma unroll
     for (int x = 0; x < KC; ++x) yk[x] = yv[x] = 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * KC;
-      const float ds = ok ? a.scale * pg[h] * (dpg[h] - dvg[h]) : 0.f;
-      const float pw = ok ? pg[h] : 0.f;
+      const float pgl = cur.pg[h] * cur.lg[h];  // p / l
+      const float ds = cur.ok ? a.scale * pgl * (cur.dpg[h] - cur.dvg[h]) : 0.f;
+      const float pw = cur.ok ? pgl : 0.f;
       float qx[KC], ox[KC];
-      load_vec<KC>(Q + off, qx);
-      load_vec<KC>(dO + off, ox);
+      if constexpr (kRowsAhead) {
+#pragma unroll
+        for (int x = 0; x < KC; ++x) {
+          qx[x] = cur.qx[x];
+          ox[x] = cur.ox[x];
+        }
+      } else {
+        const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * KC;
+        load_vec<KC>(Q + off, qx);
+        load_vec<KC>(dO + off, ox);
+      }
 #pragma unroll
       for (int x = 0; x < KC; ++x) {
         yk[x] = fmaf(ds, qx[x], yk[x]);
@@ -1596,6 +1643,7 @@ __global__ __launch_bounds__(kEdgeKB) void bwd_edges_key_kernel(EdgeBwdArgs a) {
       ak[x] += yk[x];
       av[x] += yv[x];
     }
+    cur = nxt;
   }
   if (activej) {
     if (a.rope) rotate_pairs<KC, -1>(ak, a.rope + size_t(j) * D, c * KC);  // dK = R(j)^T dK~
