@@ -609,18 +609,26 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
     for (int x = 0; x < DC; ++x) o[h][x] = 0.f;
   float m = neg_inf(), l = 0.f;
 
+  // The list entries of a chunk are read one chunk ahead, so the index
+  // loads leave the chunk's dependency chain (index, then K row, then
+  // logit).  An entry index is clamped to the width: a chunk can run past
+  // it when the width is not a multiple of ESC.
+  int keys[ESC];
+#pragma unroll
+  for (int j = 0; j < ESC; ++j) keys[j] = erow[min(j, a.width - 1)];
   for (int t0 = 0; t0 < cmax; t0 += ESC) {
     // Branch-free over the lanes' different lists: an entry past the
     // query's count or a padding entry reads row 0 (row 0 exists) and is
-    // masked by its logit, so p = 0 for it.  The list index is clamped to
-    // the width: the chunk can run past it when the width is not a
-    // multiple of ESC.
+    // masked by its logit, so p = 0 for it.
+    int knext[ESC];
+#pragma unroll
+    for (int j = 0; j < ESC; ++j) knext[j] = erow[min(t0 + ESC + j, a.width - 1)];
     float sl[ESC];
     int jj[ESC];
 #pragma unroll
     for (int j = 0; j < ESC; ++j) {
       const int t = t0 + j;
-      const int key = erow[min(t, a.width - 1)];
+      const int key = keys[j];
       const bool valid = t < cnt && key >= 0 && key < n;
       jj[j] = valid ? key : 0;
       float kt[DC];
@@ -660,6 +668,8 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
 #pragma unroll
         for (int x = 0; x < DC; ++x) o[h][x] = fmaf(ph[h], vt[x], o[h][x]);
     }
+#pragma unroll
+    for (int j = 0; j < ESC; ++j) keys[j] = knext[j];
   }
 
   float lh[G];
