@@ -5,8 +5,8 @@ Sources:
 * page 1, "Depth-Staggered Fibonacci Spacing for Sparse Attention": the key set
   of query i is the dense window of distances 0..W (self included) plus one
   interpolated key per rung; rung k sits at distance d_k = lo_k + frac_k and is
-  the linear interpolation of the rows i - lo_k and i - lo_k - 1 (floor and
-  floor-plus-one distances) of the rotary-rotated keys; values are gathered
+  the linear interpolation of the rows i - lo_k and i - lo_k - 1 (the two
+  integer distances around d_k) of the rotary-rotated keys; values are gathered
   the same way without rotation.  Heads are grouped (GQA, 8 query heads over
   2 key/value heads on that page).
 * page 2, "Critical power-law sparse attention", item 2, and page 3,

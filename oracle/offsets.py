@@ -1,8 +1,8 @@
 """Rung bases, the alpha map, per-layer schedules and rung offsets (fp64).
 
 Source: "Depth-Staggered Fibonacci Spacing for Sparse Attention" (page 1):
-the fib equation (K = 15 rungs), the gather paragraph (d_k = alpha * f_k,
-interpolated between the floor and floor-plus-one rows), the alpha
+the fib equation (K = 15 rungs), the gather paragraph (d_k = alpha * f_k;
+a fractional distance lerps the two rows whose distances bracket it), the alpha
 parameterisation (alpha = 0.5 + sigmoid(theta)), the schedule list (fixed,
 learned, staggered linear, staggered coprime with S = 7 over L = 16 layers)
 and the reach-matched power-of-2 control.
