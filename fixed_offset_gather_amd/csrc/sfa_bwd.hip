@@ -140,9 +140,10 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
   const int qq = tid / LPQ;
   const int c = tid % LPQ;
   const int own = HS::own(c);
-  const int tile = xcd_tile(blockIdx.x, a.tiles);
-  const int seq = tile / a.nblk;
-  const int blk = a.nblk - 1 - tile % a.nblk;
+  const SeqBlock sb = lpt_seq_block(blockIdx.x, a.tiles, a.nblk);
+  const int tile = sb.canon;  // index of this workgroup's dd partials
+  const int seq = sb.seq;
+  const int blk = sb.blk;
   const int b = seq / a.hkv, g = seq % a.hkv;
   const int n = a.n;
   const int i0 = blk * BQ;

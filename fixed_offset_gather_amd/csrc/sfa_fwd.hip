@@ -92,9 +92,9 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
   const int qq = tid / LPQ;
   const int c = tid % LPQ;
   const int own = c % G;
-  const int tile = xcd_tile(blockIdx.x, a.tiles);
-  const int seq = tile / a.nblk;
-  const int blk = a.nblk - 1 - tile % a.nblk;  // longest blocks first
+  const SeqBlock sb = lpt_seq_block(blockIdx.x, a.tiles, a.nblk);  // longest blocks first
+  const int seq = sb.seq;
+  const int blk = sb.blk;
   const int b = seq / a.hkv, g = seq % a.hkv;
   const int n = a.n;
   const int i0 = blk * BQ;
@@ -316,9 +316,9 @@ __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Sl
   const int qq = tid / LPQ;
   const int c = tid % LPQ;
   const int own = HS::own(c);
-  const int tile = xcd_tile(blockIdx.x, a.tiles);
-  const int seq = tile / a.nblk;
-  const int blk = a.nblk - 1 - tile % a.nblk;  // longest blocks first
+  const SeqBlock sb = lpt_seq_block(blockIdx.x, a.tiles, a.nblk);  // longest blocks first
+  const int seq = sb.seq;
+  const int blk = sb.blk;
   const int b = seq / a.hkv, g = seq % a.hkv;
   const int n = a.n;
   const int i0 = blk * BQH;

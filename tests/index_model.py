@@ -29,6 +29,35 @@ def check(cond, what):
         raise IndexModelError(what)
 
 
+# ------------------------------------------------------------ tile order
+
+NUM_XCD = 8          # sfa_device.h: kNumXcd
+
+
+def xcd_tile(ids, total):
+    """sfa_device.h xcd_tile: dispatch id -> tile, XCD-contiguous ranges."""
+    ids = np.asarray(ids)
+    if total % NUM_XCD:
+        return ids
+    per = total // NUM_XCD
+    return (ids % NUM_XCD) * per + ids // NUM_XCD
+
+
+def lpt_seq_block(ids, total, nblk):
+    """sfa_device.h lpt_seq_block: dispatch id -> (seq, blk, canon)."""
+    tile = xcd_tile(ids, total)
+    per = total // NUM_XCD
+    if total % NUM_XCD == 0 and per % nblk == 0:
+        k = per // nblk
+        r = tile - (tile // per) * per
+        seq = (tile // per) * k + r % k
+        rank = r // k
+    else:
+        seq = tile // nblk
+        rank = tile % nblk
+    return seq, nblk - 1 - rank, seq * nblk + rank
+
+
 # ------------------------------------------------------------ slot table
 
 def build_slots(window, lo, frac, merge=False):

@@ -117,3 +117,27 @@ def test_ring_wrap_mistake_is_caught(monkeypatch):
     n, W, lo, fr = TABLES["page1_learned"]
     with pytest.raises(im.IndexModelError):
         im.key_pass_h16(n, W, lo, fr, 4)
+
+
+@pytest.mark.parametrize("nseq,nblk", [(64, 32), (32, 64), (16, 2), (8, 1), (3, 32), (64, 7), (5, 3), (1, 1),
+                                       (256, 8), (24, 32), (8, 128)])
+def test_tile_order_is_a_longest_first_bijection(nseq, nblk):
+    # Every workgroup of a launch gets one (sequence, block) in range, each
+    # exactly once; canon is the sequence-major numbering of the
+    # per-workgroup dd partials; an XCD starts its blocks longest first
+    # (the block index never rises along its dispatch order) and, when it
+    # holds whole sequences, every block of a sequence runs on one XCD.
+    total = nseq * nblk
+    ids = np.arange(total)
+    seq, blk, canon = im.lpt_seq_block(ids, total, nblk)
+    assert seq.min() >= 0 and seq.max() < nseq and blk.min() >= 0 and blk.max() < nblk
+    assert len(set(zip(seq.tolist(), blk.tolist()))) == total
+    assert np.array_equal(canon, seq * nblk + (nblk - 1 - blk))
+    assert np.array_equal(np.sort(canon), ids)
+    if total % im.NUM_XCD == 0:
+        for x in range(im.NUM_XCD):
+            on = ids[ids % im.NUM_XCD == x]  # dispatch order of XCD x
+            if (total // im.NUM_XCD) % nblk == 0:
+                assert np.all(np.diff(blk[on]) <= 0)
+                for s_ in np.unique(seq[on]):
+                    assert np.all(seq[ids % im.NUM_XCD != x] != s_)
