@@ -51,13 +51,22 @@ constexpr int kCap = 128;
 // Dims per key-pass tile (and per chunk of a packed key-pass row).
 constexpr int key_chunk(int D) { return D >= 16 ? 16 : D; }
 
-// Queries per bwd_query workgroup.  A workgroup's LDS (its stage rows) lets
-// two share a CU; with G >= 4 the 16-lane queries already give 8 waves per
-// workgroup, with fewer heads 8-lane queries need 64 queries for the same
-// (Christoffel query pass 210 -> 163 us; G = 4 at 64 queries: 124 -> 142 us).
+// Queries per bwd_query workgroup and rows per stage.  With fewer than 4
+// heads per KV head, 8-lane queries in blocks of 64 (8 waves) with 128-row
+// stages: two workgroups share a CU (Christoffel query pass 210 -> 163 us
+// against 32-query blocks).  With G >= 4 a query takes 16 lanes, and blocks
+// of 16 queries (4 waves) with 72-row stages (39.7 KB of LDS) put four
+// workgroups on a CU: the same 16 waves as two of 32 queries with 128-row
+// stages, in workgroups half as long, so the launch's tail (the CUs left
+// idle while its last workgroups finish) is half as long too (page-1 query
+// pass 155.4 -> 148.9 us; 64 queries: 124 -> 142 us in an earlier build).
 template <int G>
 constexpr int bwd_bq() {
-  return G >= 4 ? 32 : 64;
+  return G >= 4 ? 16 : 64;
+}
+template <int G>
+constexpr int bwd_query_cap() {
+  return G >= 4 ? 72 : kCap;
 }
 
 struct BwdArgs {
@@ -1322,12 +1331,12 @@ int launch_query_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
   a.want_dd = dd ? 1 : 0;
   a.r0 = 0;
   if (!dd || t.n_rungs <= RS * ND) {
-    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, kCap, BQ, RS>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<G>(), BQ, RS>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
     return int(hipGetLastError());
   }
   for (int r0 = 0; r0 < t.n_rungs; r0 += kRplLarge * ND) {
     a.r0 = r0;
-    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, kCap, BQ, kRplLarge>), dim3(a.tiles), dim3(BQ * LPQ), 0, st,
+    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<G>(), BQ, kRplLarge>), dim3(a.tiles), dim3(BQ * LPQ), 0, st,
                        a, t);
     if (hipError_t e = hipGetLastError()) return int(e);
   }

@@ -146,7 +146,12 @@ def bwd_lpq(D, G):
 
 
 def bwd_bq(G):
-    return 32 if G >= 4 else 64
+    return 16 if G >= 4 else 64
+
+
+def bwd_query_cap(G):
+    """sfa_bwd.hip bwd_query_cap: rows per query-pass stage."""
+    return 72 if G >= 4 else CAP
 
 
 def query_pass(n, window, lo, frac, D, G, want_dd=True, batch_kv=1):
@@ -156,7 +161,7 @@ def query_pass(n, window, lo, frac, D, G, want_dd=True, batch_kv=1):
     sl = build_slots(window, lo, frac)
     S = len(sl)
     n_rungs = len(lo)
-    lpq, bq = bwd_lpq(D, G), bwd_bq(G)
+    lpq, bq, qcap = bwd_lpq(D, G), bwd_bq(G), bwd_query_cap(G)
     nd = lpq // G
     rpl_small = 1 if nd >= 16 else 16 // nd
     rpl = rpl_small if (not want_dd or n_rungs <= rpl_small * nd) else 16
@@ -184,13 +189,13 @@ def query_pass(n, window, lo, frac, D, G, want_dd=True, batch_kv=1):
                     if le > i_last:
                         break
                     need = max(lomax, le + two(e))
-                    if need - lo0 + bq > CAP:
+                    if need - lo0 + bq > qcap:
                         break
                     lomax = need
                     e += 1
                 r0 = i0 - lomax
                 nrows = lomax - lo0 + bq
-                check(0 < nrows <= CAP, "query-pass stage within the LDS capacity")
+                check(0 < nrows <= qcap, "query-pass stage within the LDS capacity")
                 for sj in range(s, e):
                     l, f, _, rung = sl[sj]
                     r = i - l - r0

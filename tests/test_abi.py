@@ -173,9 +173,9 @@ def test_bwd_validation_and_workspace_size():
     al = lambda e: (e + 63) // 64 * 64
     pe = al(2 * 2 * S * 100 * 4)          # p and dp: [B][Hkv][S][n][G]
     de = al(2 * 2 * 100 * 4)              # Dvec / l and 1 / l: [B][Hkv][n][G] each
-    # dd partials: one per query-pass workgroup (32-query blocks at 4 heads
+    # dd partials: one per query-pass workgroup (16-query blocks at 4 heads
     # per KV head, x B x Hkv)
-    blocks = 4 * 2 * 2
+    blocks = 7 * 2 * 2
     dd = al(blocks * 15)
     # packed key-pass rows of q and dO (bf16, G >= 2): D * G / 2 words per row
     xe = al(2 * 2 * 100 * 64 * 2)
