@@ -1227,10 +1227,36 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   }
 }
 
-// Both halves in one launch: tiles [0, T) are dK tiles and [T, 2T) dV
-// tiles, dispatched in that order, so dV workgroups start on the CUs that
-// dK workgroups leave instead of waiting for the slowest of them (page-1 key
-// pass 146 -> 137 us, Christoffel 298 -> 266 us against two launches).
+// Order of the key-pass tiles: a launch of `halves` kinds of workgroup (dK
+// and dV, or one kind doing both) over T = nseq * nblk * nch tiles each.
+// Every XCD takes the same share of each kind, its dK tiles first and then
+// the dV tiles of the same sequences, so dV workgroups start on the CUs
+// that dK workgroups leave (page-1 key pass 146 -> 137 us, Christoffel
+// 298 -> 266 us against two launches) and no XCD holds only the cheaper
+// kind (with the kinds split across the XCDs, 89.7 -> 86.4 us).  Within a
+// kind an XCD runs its tiles block rank by block rank across its sequences,
+// longest first: key block 0 is reached by every offset, later blocks by
+// fewer (86.4 -> 82.6 us).  Without whole sequences per XCD, each kind
+// runs sequence by sequence.
+struct KeyTile {
+  int part, tile;
+};
+__device__ __forceinline__ KeyTile key_tile_order(int bid, int T, int halves, int nblk, int nch) {
+  const int total = halves * T;
+  const int t = xcd_tile(bid, total);
+  if (T % kNumXcd != 0) return {t >= T ? 1 : 0, t >= T ? t - T : t};
+  const int h = T / kNumXcd, per = halves * h;
+  const int x = t / per, r = t - x * per;
+  const int part = r >= h ? 1 : 0, rr = r - part * h;
+  const int spx = h / (nblk * nch);  // sequences per XCD
+  int tile = x * h + rr;
+  if (spx * nblk * nch == h) {
+    const int rank = rr / (spx * nch), rem = rr - rank * (spx * nch);
+    tile = ((x * spx + rem / nch) * nblk + rank) * nch + rem % nch;
+  }
+  return {part, tile};
+}
+
 // With the offset gradient requested the launch leads with kNumXcd more
 // workgroups: the first reduces dd and dtheta (the query pass, which wrote
 // their partials, has finished), concurrently with the key tiles instead of
@@ -1247,14 +1273,15 @@ __global__ __launch_bounds__(kKeyBlockH16) void bwd_key_h16_kernel(BwdArgs a, Sl
     }
     bid -= kNumXcd;
   }
+  constexpr int NCH = D / key_chunk_h16(D, G);
   if constexpr (G == 1) {
-    key_half_body<D, 1, 2>(a, st, xcd_tile(bid, a.tiles));  // both halves
+    key_half_body<D, 1, 2>(a, st, key_tile_order(bid, a.tiles, 1, a.nblk, NCH).tile);  // both halves
   } else {
-    const int t2 = xcd_tile(bid, 2 * a.tiles);
-    if (t2 < a.tiles)
-      key_half_body<D, G, 0>(a, st, t2);
+    const KeyTile kt = key_tile_order(bid, a.tiles, 2, a.nblk, NCH);
+    if (kt.part == 0)
+      key_half_body<D, G, 0>(a, st, kt.tile);
     else
-      key_half_body<D, G, 1>(a, st, t2 - a.tiles);
+      key_half_body<D, G, 1>(a, st, kt.tile);
   }
 }
 

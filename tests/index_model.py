@@ -58,6 +58,24 @@ def lpt_seq_block(ids, total, nblk):
     return seq, nblk - 1 - rank, seq * nblk + rank
 
 
+def key_tile_order(ids, T, halves, nblk, nch):
+    """sfa_bwd.hip key_tile_order: dispatch id -> (part, tile) of the key pass."""
+    t = xcd_tile(ids, halves * T)
+    if T % NUM_XCD:
+        return (t >= T).astype(int), np.where(t >= T, t - T, t)
+    h = T // NUM_XCD
+    per = halves * h
+    x, r = t // per, t % per
+    part = (r >= h).astype(int)
+    rr = r - part * h
+    spx = h // (nblk * nch)
+    tile = x * h + rr
+    if spx * nblk * nch == h:
+        rank, rem = rr // (spx * nch), rr % (spx * nch)
+        tile = ((x * spx + rem // nch) * nblk + rank) * nch + rem % nch
+    return part, tile
+
+
 # ------------------------------------------------------------ slot table
 
 def build_slots(window, lo, frac, merge=False):

@@ -141,3 +141,28 @@ def test_tile_order_is_a_longest_first_bijection(nseq, nblk):
                 assert np.all(np.diff(blk[on]) <= 0)
                 for s_ in np.unique(seq[on]):
                     assert np.all(seq[ids % im.NUM_XCD != x] != s_)
+
+
+@pytest.mark.parametrize("halves", [1, 2])
+@pytest.mark.parametrize("nseq,nblk,nch", [(64, 8, 4), (8, 16, 4), (32, 16, 4), (3, 5, 4), (16, 8, 4), (2, 1, 4),
+                                           (1, 1, 1), (6, 4, 2), (24, 3, 4)])
+def test_key_tile_order_is_a_balanced_bijection(halves, nseq, nblk, nch):
+    # Each kind of key-pass workgroup covers its T tiles exactly once; with
+    # T a multiple of the XCD count every XCD takes T / 8 tiles of each kind
+    # (never only the cheaper one), and with whole sequences per XCD its
+    # tiles of a kind run longest key block (block 0) first.
+    T = nseq * nblk * nch
+    ids = np.arange(halves * T)
+    part, tile = im.key_tile_order(ids, T, halves, nblk, nch)
+    assert part.min() >= 0 and part.max() < halves
+    for p_ in range(halves):
+        assert np.array_equal(np.sort(tile[part == p_]), np.arange(T))
+    if T % im.NUM_XCD == 0:
+        xcd = ids % im.NUM_XCD
+        for x in range(im.NUM_XCD):
+            for p_ in range(halves):
+                sel = (xcd == x) & (part == p_)
+                assert sel.sum() == T // im.NUM_XCD
+                if (T // im.NUM_XCD) % (nblk * nch) == 0:
+                    blk = (tile[sel] // nch) % nblk
+                    assert np.all(np.diff(blk) >= 0)
