@@ -393,6 +393,18 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// ------------------------------------------------------- online softmax
+
+// The forward kernels' online softmax keeps a running reference per (query,
+// head) and raises it only when some lane of the wave sees a logit more than
+// this many log2 units above its reference (one ballot per chunk of slots).
+// Below that the weights exp2(s - ref) stay at most 2^8 in fp32, and the
+// rescale of the output accumulators (an exp, its spread to the lane's heads
+// and a multiply per accumulator) is skipped.  The output is the same up to
+// rounding: o and l share the reference, and lse = ref + log2 l.  (Page-1
+// learned forward 68.3 -> 65.8 us, Christoffel forward 89.7 -> 85.3 us.)
+constexpr float kRescaleSlack = 8.f;
+
 // ------------------------------------------------------------ tile order
 
 // Workgroups are dispatched round-robin over the XCDs.  Give each XCD a

@@ -220,8 +220,20 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
       float mx = m;
 #pragma unroll
       for (int j = 0; j < SC; ++j) mx = fmaxf(mx, sl[j]);
-      const float mref = (mx == neg_inf()) ? 0.f : mx;
-      const float corr = __builtin_amdgcn_exp2f(m - mref);
+      // the reference moves only past kRescaleSlack (one ballot per chunk)
+      if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+        const float mr = (mx == neg_inf()) ? 0.f : mx;
+        const float corr = __builtin_amdgcn_exp2f(m - mr);
+        l *= corr;
+        m = mx;
+        float ch[G];
+        Bcast<G, LPQ>::run(corr, ch);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int x = 0; x < DC; ++x) o[h][x] *= ch[h];
+      }
+      const float mref = (m == neg_inf()) ? 0.f : m;
       float p[SC];
       float ps = 0.f;
 #pragma unroll
@@ -230,14 +242,7 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
         if (s0 + j < e) p[j] *= mult_c[j];
         ps += p[j];
       }
-      l = l * corr + ps;
-      m = mx;
-      float ch[G];
-      Bcast<G, LPQ>::run(corr, ch);
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int x = 0; x < DC; ++x) o[h][x] *= ch[h];
+      l += ps;
 #pragma unroll
       for (int j = 0; j < SC; ++j) {
         const int sj = s0 + j;
@@ -470,8 +475,20 @@ __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Sl
       float mx = m;
 #pragma unroll
       for (int j = 0; j < SC; ++j) mx = fmaxf(mx, sl[j]);
-      const float mref = (mx == neg_inf()) ? 0.f : mx;
-      const float corr = __builtin_amdgcn_exp2f(m - mref);
+      // the reference moves only past kRescaleSlack (one ballot per chunk)
+      if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+        const float mr = (mx == neg_inf()) ? 0.f : mx;
+        const float corr = __builtin_amdgcn_exp2f(m - mr);
+        l *= corr;
+        m = mx;
+        float ch[G];
+        HS::bcast(corr, ch);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int x = 0; x < DC; ++x) o[h][x] *= ch[h];
+      }
+      const float mref = (m == neg_inf()) ? 0.f : m;
       float p[SC];
       float ps = 0.f;
 #pragma unroll
@@ -480,14 +497,7 @@ __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Sl
         if (s0 + j < e) p[j] *= mult_c[j];
         ps += p[j];
       }
-      l = l * corr + ps;
-      m = mx;
-      float ch[G];
-      HS::bcast(corr, ch);
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int x = 0; x < DC; ++x) o[h][x] *= ch[h];
+      l += ps;
 #pragma unroll
       for (int j = 0; j < SC; ++j) {
         const int sj = s0 + j;
@@ -640,8 +650,20 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
     float mx = m;
 #pragma unroll
     for (int j = 0; j < ESC; ++j) mx = fmaxf(mx, sl[j]);
-    const float mref = (mx == neg_inf()) ? 0.f : mx;
-    const float corr = __builtin_amdgcn_exp2f(m - mref);
+    // the reference moves only past kRescaleSlack (one ballot per chunk)
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+      const float mr = (mx == neg_inf()) ? 0.f : mx;
+      const float corr = __builtin_amdgcn_exp2f(m - mr);
+      l *= corr;
+      m = mx;
+      float ch[G];
+      Bcast<G, LPQ>::run(corr, ch);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int x = 0; x < DC; ++x) o[h][x] *= ch[h];
+    }
+    const float mref = (m == neg_inf()) ? 0.f : m;
     float p[ESC];
     float ps = 0.f;
 #pragma unroll
@@ -649,14 +671,7 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
       p[j] = __builtin_amdgcn_exp2f(sl[j] - mref);
       ps += p[j];
     }
-    l = l * corr + ps;
-    m = mx;
-    float ch[G];
-    Bcast<G, LPQ>::run(corr, ch);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int x = 0; x < DC; ++x) o[h][x] *= ch[h];
+    l += ps;
 #pragma unroll
     for (int j = 0; j < ESC; ++j) {
       float vt[DC];
