@@ -238,8 +238,9 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < SC; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(sl[j] - mref);
-        if (s0 + j < e) p[j] *= mult_c[j];
+        // a slot past the stage has sl = -inf, so p = 0 whatever its
+        // (clamped) multiplicity: no per-slot condition
+        p[j] = __builtin_amdgcn_exp2f(sl[j] - mref) * mult_c[j];
         ps += p[j];
       }
       l += ps;
@@ -493,8 +494,9 @@ __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Sl
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < SC; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(sl[j] - mref);
-        if (s0 + j < e) p[j] *= mult_c[j];
+        // a slot past the stage has sl = -inf, so p = 0 whatever its
+        // (clamped) multiplicity: no per-slot condition
+        p[j] = __builtin_amdgcn_exp2f(sl[j] - mref) * mult_c[j];
         ps += p[j];
       }
       l += ps;
