@@ -1,5 +1,6 @@
-"""Seeded random configurations of the shared-offset path, on the GPU,
-through the C ABI, against the oracle at the stated tolerances.
+"""Seeded random configurations of every key set, on the GPU, through the C
+ABI, against the oracle at the stated tolerances: shared offsets (below),
+power-law edge lists and signed (bidirectional) offsets (further below).
 
 Each case draws its own shape and offset table: fp32 or bf16; 1, 2, 4 or 8
 query heads per KV head over one or two KV heads; head dim 16, 32 or 64; one
@@ -53,3 +54,66 @@ def test_random_configuration(idx):
     case = P.Case(c["B"], c["n"], c["hq"], c["hkv"], c["D"], c["dtype"], seed=c["seed"], rope_theta=c["theta"])
     P._fwd_check(case, c["W"], lo, frac)
     P._bwd_check(case, c["W"], lo, frac, c["alpha"], c["base"], want_dd=c["want_dd"])
+
+
+N_EDGE_CASES = 24
+N_SIGNED_CASES = 24
+
+
+def _draw_edges(idx):
+    rng = np.random.default_rng(SEED + 104729 + 7919 * idx)
+    dtype = ["f32", "bf16"][int(rng.integers(2))]
+    G = int(rng.choice([1, 2, 4]))
+    hkv = int(rng.integers(1, 3))
+    D = int(rng.choice([16, 32, 64]))
+    n = int(rng.integers(2, 301))
+    r = int(rng.integers(0, 5))
+    draws = int(rng.integers(0, 21))
+    width = min(64, 2 * r + 1 + draws + int(rng.integers(0, 9)))
+    return dict(dtype=dtype, hq=G * hkv, hkv=hkv, D=D, B=int(rng.integers(1, 3)), n=n, r=r,
+                sigma=float(rng.uniform(0.5, 1.5)), draws=draws, width=width, theta=[1e4, 0.0][int(rng.integers(2))],
+                edge_seed=int(rng.integers(0, 1 << 30)), seed=int(rng.integers(1, 10_000)))
+
+
+@pytest.mark.parametrize("idx", range(N_EDGE_CASES))
+def test_random_edge_lists(idx):
+    # Power-law edge lists (window radius 0-4, 0-20 draws, width up to 64)
+    # over random shapes: forward and backward against the oracle.
+    c = _draw_edges(idx)
+    sfa = P._sfa()
+    print("edge case %d: %s" % (idx, c), flush=True)
+    edges, count = sfa.edges_powerlaw(c["n"], c["r"], c["sigma"], c["draws"], c["width"], c["edge_seed"])
+    case = P.Case(c["B"], c["n"], c["hq"], c["hkv"], c["D"], c["dtype"], seed=c["seed"], rope_theta=c["theta"])
+    P._edge_bwd_check(case, edges, count)
+
+
+def _draw_signed(idx):
+    rng = np.random.default_rng(SEED + 1299709 + 7919 * idx)
+    dtype = ["f32", "bf16"][int(rng.integers(2))]
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.integers(1, 3))
+    n = int(rng.integers(1, 231))
+    k = int(rng.integers(1, 25))
+    d = np.sort(rng.uniform(-1.5 * n - 2, 1.5 * n + 2, size=k))
+    if rng.integers(2):
+        d = np.round(d)  # integer distances, some negative
+    lo = np.floor(d).astype(np.int32)
+    frac = np.minimum((d - lo).astype(np.float32), np.float32(1.0 - 2.0 ** -24))  # below 1 after rounding
+    return dict(dtype=dtype, hq=G * hkv, hkv=hkv, D=int(rng.choice([16, 32, 64])), B=int(rng.integers(1, 3)), n=n,
+                W=int(rng.integers(0, 12)), lo=lo, frac=frac, base=rng.integers(1, 50, size=k).astype(np.int32),
+                alpha=float(rng.uniform(0.6, 1.4)), theta=[1e4, 0.0][int(rng.integers(2))],
+                want_dd=bool(rng.integers(2)), seed=int(rng.integers(1, 10_000)))
+
+
+@pytest.mark.parametrize("idx", range(N_SIGNED_CASES))
+def test_random_signed_offsets(idx):
+    # Offsets on both sides of the query (a negative offset names the later
+    # row i - lo), interpolated or integer, with the causal window, through
+    # SFA_FLAG_SIGNED_OFFSETS; the dtheta check takes an arbitrary base and
+    # alpha (it is the chain rule through the fractions either way).
+    c = _draw_signed(idx)
+    print("signed case %d: %s" % (idx, {k: (v.tolist() if isinstance(v, np.ndarray) else v) for k, v in c.items()}),
+          flush=True)
+    case = P.Case(c["B"], c["n"], c["hq"], c["hkv"], c["D"], c["dtype"], seed=c["seed"], rope_theta=c["theta"])
+    P._fwd_check(case, c["W"], c["lo"], c["frac"], signed=True)
+    P._bwd_check(case, c["W"], c["lo"], c["frac"], c["alpha"], c["base"], want_dd=c["want_dd"], signed=True)
