@@ -569,10 +569,14 @@ __global__ __launch_bounds__(kReduceThreads) void bwd_reduce_kernel(ReduceArgs a
   reduce_body(a, sdd, kReduceThreads);
 }
 
-// bf16 key pass: workgroups of 128 keys of two kinds in one launch, dK
-// (staging q~) and dV (staging dO).  Words per staged row: the chunk of
-// every head as f16 head pairs, plus a 4-word pad against bank conflicts.
-constexpr int kKeyBlockH16 = 128;
+// bf16 key pass: workgroups of 256 keys (four waves) of two kinds in one
+// launch, dK (staging q~) and dV (staging dO).  Words per staged row: the
+// chunk of every head as f16 head pairs, plus a 4-word pad against bank
+// conflicts.  A stage stages the block's rows plus the slots' spread, so a
+// longer block re-stages fewer rows per key: against 128 keys (two waves,
+// the same 16 waves per CU) the page-1 key pass went 83.1 -> 80.1 us and the
+// Christoffel one 122.3 -> 102.0 us; 512 keys were slower than 256 on both.
+constexpr int kKeyBlockH16 = 256;
 // Dims per bf16 key-pass tile (and per chunk of the packed rows the query
 // pass writes).  32-dim tiles at one head per KV head were measured slower
 // (Christoffel key pass 199 -> 263 us).

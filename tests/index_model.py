@@ -17,7 +17,7 @@ import numpy as np
 MAX_SLOTS = 320
 BQ_FWD_F32 = 64      # sfa_fwd.hip: BQ
 CAP = 128            # sfa_fwd.hip / sfa_bwd.hip: kCap
-KB_H16 = 128         # sfa_bwd.hip: kKeyBlockH16
+KB_H16 = 256         # sfa_bwd.hip: kKeyBlockH16
 
 
 class IndexModelError(AssertionError):
