@@ -50,6 +50,14 @@ constexpr int kCap = 128;
 
 // Dims per key-pass tile (and per chunk of a packed key-pass row).
 constexpr int key_chunk(int D) { return D >= 16 ? 16 : D; }
+// Dims per bf16 key-pass tile (and per chunk of the packed rows the query
+// pass writes).  With four or more heads per KV head, 32 dims: each of a
+// key's chunk tiles loads and converts the same step weights, so wider
+// tiles do that work for more dims (page-1 key pass 80.1 -> 78.7 us at 8
+// waves per CU instead of 16).  With fewer heads 16: 32-dim tiles at one
+// head per KV head were measured slower (Christoffel key pass 199 ->
+// 263 us).
+constexpr int key_chunk_h16(int D, int G) { return G >= 4 && D >= 32 ? 32 : key_chunk(D); }
 
 // Queries per bwd_query workgroup and rows per stage.  With fewer than 4
 // heads per KV head, 8-lane queries in blocks of 64 (8 waves) with 128-row
@@ -380,7 +388,7 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
   // register holds the odd head (v_perm with a per-lane selector).
   if constexpr (sizeof(T) == 2 && G >= 2) {
     if (active && a.xq) {
-      constexpr int KC = key_chunk(D);
+      constexpr int KC = key_chunk_h16(D, G);
       constexpr int GW = G / 2;
       static_assert(KC % DC == 0, "a lane's dims lie in one chunk");
       const int ch = (c * DC) / KC, x0 = (c * DC) % KC;
@@ -577,10 +585,6 @@ __global__ __launch_bounds__(kReduceThreads) void bwd_reduce_kernel(ReduceArgs a
 // the same 16 waves per CU) the page-1 key pass went 83.1 -> 80.1 us and the
 // Christoffel one 122.3 -> 102.0 us; 512 keys were slower than 256 on both.
 constexpr int kKeyBlockH16 = 256;
-// Dims per bf16 key-pass tile (and per chunk of the packed rows the query
-// pass writes).  32-dim tiles at one head per KV head were measured slower
-// (Christoffel key pass 199 -> 263 us).
-constexpr int key_chunk_h16(int D, int G) { return key_chunk(D); }
 // Words per staged row: the chunk of every head as f16 head pairs (G >= 2,
 // one half of the pass per workgroup), or with one head per KV head the fp32
 // chunks of q~ and dO together (both halves in one workgroup); plus a 4-word

@@ -235,9 +235,14 @@ def query_pass(n, window, lo, frac, D, G, want_dd=True, batch_kv=1):
 
 # ------------------------------------------------------------ key passes
 
+def key_chunk_h16(D, G):
+    """sfa_bwd.hip key_chunk_h16: dims per bf16 key-pass tile."""
+    return 32 if G >= 4 and D >= 32 else min(16, D)
+
+
 def key_half_cap(G, D):
     """sfa_bwd.hip key_half_cap."""
-    kc = 16
+    kc = key_chunk_h16(D, G)
     rw = 2 * kc + 4 if G == 1 else kc * ((G + 1) // 2) + 4
     cap = (163840 * (KB_H16 // 64) // 16) // (4 * rw)
     return min(max(cap, KB_H16 + 12), KB_H16 + 64)
