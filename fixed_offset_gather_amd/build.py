@@ -25,13 +25,15 @@ HIP_SOURCES = ["sfa_api.hip", "sfa_fwd.hip", "sfa_bwd.hip", "sfa_noalloc.hip"]
 CXX_SOURCES = ["sfa_producers.cpp"]
 
 # Packed FP32 instructions are disabled for all device code.  The tied
-# two-operand v_dot2c_f32_f16 is disabled too: a dot that starts from zero
-# then needs a v_mov per accumulator, while the three-operand
-# v_dot2_f32_f16 (same issue rate) takes the 0 as an inline constant.
+# two-operand v_dot2c_f32_f16 and v_dot2c_f32_bf16 are disabled too: a dot
+# that starts from zero then needs a v_mov per accumulator, while the
+# three-operand v_dot2_f32_f16 and v_dot2_f32_bf16 (same issue rate) take
+# the 0 as an inline constant.
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Xclang", "-target-feature", "-Xclang", "-dot5-insts",
+    "-Xclang", "-target-feature", "-Xclang", "-dot13-insts",
     "-Wno-unused-command-line-argument",
 ]
 

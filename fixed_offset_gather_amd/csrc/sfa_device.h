@@ -200,6 +200,11 @@ __device__ __forceinline__ float dot2_h(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false);
 }
 
+// The same with bfloat16 halves (each product exact in fp32).
+__device__ __forceinline__ float dot2_bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // a + w (b - a) on both halves (packed f16 arithmetic).
 __device__ __forceinline__ uint32_t lerp_h2(uint32_t a, uint32_t b, half2_t w) {
   const half2_t x = as_h2(a), y = as_h2(b);

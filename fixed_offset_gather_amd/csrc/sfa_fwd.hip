@@ -297,9 +297,13 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_offsets_kernel(FwdArgs a, SlotTab
 // in fp32.  Register j of a lane holds head HeadSlice::head(c, j), so the
 // per-slot logit is a reduce-scatter (each lane ends with its own head's
 // sum) and p is spread back with G - 1 DPP moves; BQH queries per
-// workgroup.
-template <int D, int G, int LPQ, int BQH, int CAP, bool INTERP>
+// workgroup.  RAWK (integer offsets without rotation): K rows are staged as
+// the bf16 input words, unconverted, the query is packed as bf16 pairs
+// (exact) and the logits use v_dot2_f32_bf16, whose products are exact, then
+// take scale*log2(e) after the sum (Christoffel forward 84.1 -> 81.1 us).
+template <int D, int G, int LPQ, int BQH, int CAP, bool INTERP, bool RAWK>
 __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, SlotTable st) {
+  static_assert(!(RAWK && INTERP), "raw bf16 K rows are not interpolated");
   constexpr int DC = D / LPQ;  // dims per lane
   constexpr int DW = DC / 2;   // f16 pairs per lane
   constexpr int RW = D / 2 + 4;  // 32-bit words per LDS row (16-byte pad)
@@ -367,7 +371,9 @@ __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Sl
       for (int x = 0; x < DC; ++x) qf[x] = 0.f;
     }
 #pragma unroll
-    for (int x = 0; x < DW; ++x) qh[h][x] = pack_h2(qf[2 * x] * a.scale_log2, qf[2 * x + 1] * a.scale_log2);
+    for (int x = 0; x < DW; ++x)
+      qh[h][x] = RAWK ? pack_bf2(qf[2 * x], qf[2 * x + 1])
+                      : pack_h2(qf[2 * x] * a.scale_log2, qf[2 * x + 1] * a.scale_log2);
   }
 
   float o[G][DC];
@@ -404,16 +410,24 @@ __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Sl
       const int row = t / CPR, cc = t % CPR;
       const int pos = r0 + row;
       float kf[8], vf[8];
+      uint4 kraw = make_uint4(0, 0, 0, 0);
       if (pos >= 0 && pos < n) {
-        load_vec<8>(Kseq + size_t(pos) * kv_row + cc * 8, kf);
+        if constexpr (RAWK) {
+          kraw = *reinterpret_cast<const uint4*>(Kseq + size_t(pos) * kv_row + cc * 8);
+        } else {
+          load_vec<8>(Kseq + size_t(pos) * kv_row + cc * 8, kf);
+          if (a.rope) rotate_pairs<8, 1>(kf, a.rope + size_t(pos) * D, cc * 8);
+        }
         load_vec<8>(Vseq + size_t(pos) * kv_row + cc * 8, vf);
-        if (a.rope) rotate_pairs<8, 1>(kf, a.rope + size_t(pos) * D, cc * 8);
       } else {
 #pragma unroll
         for (int x = 0; x < 8; ++x) kf[x] = vf[x] = 0.f;
       }
-      *reinterpret_cast<uint4*>(Ks + row * RW + cc * 4) =
-          make_uint4(pack_h2(kf[0], kf[1]), pack_h2(kf[2], kf[3]), pack_h2(kf[4], kf[5]), pack_h2(kf[6], kf[7]));
+      if constexpr (RAWK)
+        *reinterpret_cast<uint4*>(Ks + row * RW + cc * 4) = kraw;
+      else
+        *reinterpret_cast<uint4*>(Ks + row * RW + cc * 4) =
+            make_uint4(pack_h2(kf[0], kf[1]), pack_h2(kf[2], kf[3]), pack_h2(kf[4], kf[5]), pack_h2(kf[6], kf[7]));
       *reinterpret_cast<uint4*>(Vs + row * RW + cc * 4) =
           make_uint4(pack_h2(vf[0], vf[1]), pack_h2(vf[2], vf[3]), pack_h2(vf[4], vf[5]), pack_h2(vf[6], vf[7]));
     }
@@ -459,10 +473,10 @@ __global__ __launch_bounds__(BQH* LPQ) void fwd_offsets_h16_kernel(FwdArgs a, Sl
           for (int h = 0; h < G; ++h) {
             float acc = 0.f;
 #pragma unroll
-            for (int x = 0; x < DW; ++x) acc = dot2_h(qh[h][x], kw[x], acc);
+            for (int x = 0; x < DW; ++x) acc = RAWK ? dot2_bf(qh[h][x], kw[x], acc) : dot2_h(qh[h][x], kw[x], acc);
             part[h] = acc;
           }
-          const float mine = HS::reduce(part);
+          const float mine = RAWK ? HS::reduce(part) * a.scale_log2 : HS::reduce(part);
           // The nearer row i - lo exists (i >= lo + frac, and below n for a
           // negative offset): mn <= i - lo <= n - 1 with mn = 1 for an
           // interpolated slot (integer arithmetic on the fraction's bits,
@@ -744,8 +758,13 @@ void launch_fwd_offsets_i(const SlotTable& t, const FwdArgs& a0, hipStream_t st)
     FwdArgs a = a0;
     a.nblk = (a.n + BQH - 1) / BQH;
     a.tiles = a.nblk * a.tiles_per_blk;
-    hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, BQH, kCap, INTERP>),
-                       dim3(a.tiles), dim3(BQH * LPQ), 3 * 4 * t.count, st, a, t);
+    // Integer offsets without rotation read the bf16 K rows as they are.
+    if (!INTERP && a.rope == nullptr)
+      hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, BQH, kCap, false, true>),
+                         dim3(a.tiles), dim3(BQH * LPQ), 3 * 4 * t.count, st, a, t);
+    else
+      hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, BQH, kCap, INTERP, false>),
+                         dim3(a.tiles), dim3(BQH * LPQ), 3 * 4 * t.count, st, a, t);
   } else {
     constexpr int LPQ = fwd_lpq<D, G>();
     const FwdArgs& a = a0;
