@@ -66,6 +66,23 @@ __device__ __forceinline__ float own_logit(const float (&qv)[G][DC], const float
   return mine;
 }
 
+// The same over raw bfloat16 pairs: v_dot2_f32_bf16, each product exact.
+template <int G, int LPQ, int DW>
+__device__ __forceinline__ float own_logit_bf(const uint32_t (&qb)[G][DW], const uint32_t (&kw)[DW], int own) {
+  float part[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float acc = 0.f;
+#pragma unroll
+    for (int x = 0; x < DW; ++x) acc = dot2_bf(qb[h][x], kw[x], acc);
+    part[h] = group_sum<LPQ>(acc);
+  }
+  float mine = part[0];
+#pragma unroll
+  for (int h = 1; h < G; ++h) mine = (own == h) ? part[h] : mine;
+  return mine;
+}
+
 template <int G, int LPQ>
 struct Bcast {
   template <int H = 0>
@@ -588,9 +605,15 @@ struct EdgeArgs {
   float scale_log2;
 };
 
-template <typename T, int D, int G, int LPQ>
+// RAWK (bf16 without rotation): the query and the listed K and V rows stay
+// bf16 words; the logits use v_dot2_f32_bf16 (exact products), and a chunk's
+// V rows are requested together with its K rows, so the chunk waits for
+// memory once instead of twice (power-law forward 26.8 -> 24.8 us).
+template <typename T, int D, int G, int LPQ, bool RAWK>
 __global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
+  static_assert(!RAWK || sizeof(T) == 2, "raw rows are bf16");
   constexpr int DC = D / LPQ;
+  constexpr int DW = DC / 2;
   const int tid = threadIdx.x;
   const int qq = tid / LPQ;
   const int c = tid % LPQ;
@@ -611,10 +634,19 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
   const T* Vseq = V + size_t(b) * n * kv_row + size_t(g) * D + c * DC;
 
   float qv[G][DC];
+  uint32_t qb[G][DW];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    if (active) {
-      load_vec<DC>(Q + ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC, qv[h]);
+    const size_t qoff = ((size_t(b) * n + i) * a.hq + size_t(g) * G + h) * D + c * DC;
+    if constexpr (RAWK) {
+      if (active) {
+        load_words<DW>(reinterpret_cast<const uint32_t*>(Q + qoff), qb[h]);
+      } else {
+#pragma unroll
+        for (int x = 0; x < DW; ++x) qb[h][x] = 0u;
+      }
+    } else if (active) {
+      load_vec<DC>(Q + qoff, qv[h]);
       if (a.rope) rotate_pairs<DC, 1>(qv[h], a.rope + size_t(i) * D, c * DC);
     } else {
 #pragma unroll
@@ -651,17 +683,34 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
     for (int j = 0; j < ESC; ++j) knext[j] = erow[min(t0 + ESC + j, a.width - 1)];
     float sl[ESC];
     int jj[ESC];
+    uint32_t vraw[RAWK ? ESC : 1][DW];
+    if constexpr (RAWK) {
+      uint32_t kw[ESC][DW];
 #pragma unroll
-    for (int j = 0; j < ESC; ++j) {
-      const int t = t0 + j;
-      const int key = keys[j];
-      const bool valid = t < cnt && key >= 0 && key < n;
-      jj[j] = valid ? key : 0;
-      float kt[DC];
-      load_vec<DC>(Kseq + size_t(jj[j]) * kv_row, kt);
-      if (a.rope) rotate_pairs<DC, 1>(kt, a.rope + size_t(jj[j]) * D, c * DC);
-      const float mine = own_logit<G, LPQ, DC>(qv, kt, own);
-      sl[j] = valid ? mine * a.scale_log2 : neg_inf();
+      for (int j = 0; j < ESC; ++j) {
+        const int t = t0 + j;
+        const int key = keys[j];
+        const bool valid = t < cnt && key >= 0 && key < n;
+        jj[j] = valid ? key : 0;
+        load_words<DW>(reinterpret_cast<const uint32_t*>(Kseq + size_t(jj[j]) * kv_row), kw[j]);
+        load_words<DW>(reinterpret_cast<const uint32_t*>(Vseq + size_t(jj[j]) * kv_row), vraw[j]);
+        sl[j] = valid ? 0.f : neg_inf();
+      }
+#pragma unroll
+      for (int j = 0; j < ESC; ++j) sl[j] += own_logit_bf<G, LPQ, DW>(qb, kw[j], own) * a.scale_log2;
+    } else {
+#pragma unroll
+      for (int j = 0; j < ESC; ++j) {
+        const int t = t0 + j;
+        const int key = keys[j];
+        const bool valid = t < cnt && key >= 0 && key < n;
+        jj[j] = valid ? key : 0;
+        float kt[DC];
+        load_vec<DC>(Kseq + size_t(jj[j]) * kv_row, kt);
+        if (a.rope) rotate_pairs<DC, 1>(kt, a.rope + size_t(jj[j]) * D, c * DC);
+        const float mine = own_logit<G, LPQ, DC>(qv, kt, own);
+        sl[j] = valid ? mine * a.scale_log2 : neg_inf();
+      }
     }
     float mx = m;
 #pragma unroll
@@ -691,7 +740,15 @@ __global__ __launch_bounds__(BQ* LPQ) void fwd_edges_kernel(EdgeArgs a) {
 #pragma unroll
     for (int j = 0; j < ESC; ++j) {
       float vt[DC];
-      load_vec<DC>(Vseq + size_t(jj[j]) * kv_row, vt);  // p[j] = 0 for a masked entry
+      if constexpr (RAWK) {
+#pragma unroll
+        for (int x = 0; x < DW; ++x) {
+          vt[2 * x] = bf16_lo(vraw[j][x]);
+          vt[2 * x + 1] = bf16_hi(vraw[j][x]);
+        }
+      } else {
+        load_vec<DC>(Vseq + size_t(jj[j]) * kv_row, vt);  // p[j] = 0 for a masked entry
+      }
       float ph[G];
       Bcast<G, LPQ>::run(p[j], ph);
 #pragma unroll
@@ -791,7 +848,13 @@ int launch_fwd_offsets_t(const Problem& p, const SlotTable& t, const FwdArgs& a,
 template <typename T, int D, int G>
 int launch_fwd_edges_t(const EdgeArgs& a, hipStream_t st) {
   constexpr int LPQ = fwd_lpq<D, G>();
-  hipLaunchKernelGGL((fwd_edges_kernel<T, D, G, LPQ>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a);
+  if constexpr (sizeof(T) == 2) {
+    if (a.rope == nullptr) {  // bf16 without rotation: raw rows
+      hipLaunchKernelGGL((fwd_edges_kernel<T, D, G, LPQ, true>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a);
+      return int(hipGetLastError());
+    }
+  }
+  hipLaunchKernelGGL((fwd_edges_kernel<T, D, G, LPQ, false>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a);
   return int(hipGetLastError());
 }
 
