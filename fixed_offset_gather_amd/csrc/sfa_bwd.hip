@@ -1510,56 +1510,66 @@ __global__ __launch_bounds__(kEdgeBQ* LPQ) void bwd_edges_query_kernel(EdgeBwdAr
   float psum = 0.f;  // l = sum p (1 up to the forward's lse)
 
   // Branch-free over the wave's longest list: a padding entry (or a key
-  // outside [0, n)) reads row 0 and is masked by p = 0.  Software pipeline:
-  // the K and V rows of entry t + 1 are loaded while entry t is computed,
-  // and the list entry t + 2 is read with them, so neither the rows' nor
-  // the index's L2 latency sits on the step's dependency chain.
+  // outside [0, n)) reads row 0 and is masked by p = 0.  Entries run in
+  // chunks of ECH: the K and V rows of a chunk are requested together as
+  // raw words (converted where they are used), so the chunk waits for its
+  // gathered rows once, and the list entries of the next chunk are read
+  // with them, off the chunk's dependency chain (power-law query side
+  // 42.2 -> 39.7 us against one entry of rows loaded ahead).
   auto row_of = [&](int t) {
-    const int key = t < cnt ? erow[t] : -1;
+    const int key = t < cnt ? erow[min(t, a.width - 1)] : -1;
     return (key >= 0 && key < n) ? key : -1;  // -1: masked
   };
-  int key = row_of(0);
-  int key_next = row_of(1);
-  float kt[DC], vt[DC];
-  load_vec<DC>(Kseq + size_t(max(key, 0)) * kv_row, kt);
-  load_vec<DC>(Vseq + size_t(max(key, 0)) * kv_row, vt);
-  for (int t = 0; t < cmax; ++t) {
-    const bool valid = key >= 0;
-    const int kc = valid ? key : 0;
-    // the next entry's rows and the entry after it
-    const int key_after = row_of(t + 2);
-    float kn[DC], vn[DC];
-    load_vec<DC>(Kseq + size_t(max(key_next, 0)) * kv_row, kn);
-    load_vec<DC>(Vseq + size_t(max(key_next, 0)) * kv_row, vn);
-    if (a.rope) rotate_pairs<DC, 1>(kt, a.rope + size_t(kc) * D, c * DC);
-    const float sdot = own_dot<G, LPQ, DC>(qv, kt);
-    const float dp = own_dot<G, LPQ, DC>(dov, vt);
-    const float ex = __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2);
-    const float p = valid ? ex : 0.f;
-    const float pdp = p * dp;
-    dvec += pdp;
-    psum += p;
-    if (valid && HS::writer(c)) {
-      a.P[(wrow + t) * G + own] = p;
-      a.dP[(wrow + t) * G + own] = dp;
+  constexpr int EW = DC * int(sizeof(T)) / 4;  // 32-bit words of a lane's row chunk
+  constexpr int ECH = 4;
+  int keys[ECH];
+#pragma unroll
+  for (int j = 0; j < ECH; ++j) keys[j] = row_of(j);
+  for (int t0 = 0; t0 < cmax; t0 += ECH) {
+    uint32_t kw[ECH][EW], vw[ECH][EW];
+#pragma unroll
+    for (int j = 0; j < ECH; ++j) {
+      const size_t r = size_t(max(keys[j], 0)) * kv_row;
+      load_words<EW>(reinterpret_cast<const uint32_t*>(Kseq + r), kw[j]);
+      load_words<EW>(reinterpret_cast<const uint32_t*>(Vseq + r), vw[j]);
     }
-    float ph[G], pdh[G];
-    HS::bcast(p, ph);
-    HS::bcast(pdp, pdh);
+    int knext[ECH];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int j = 0; j < ECH; ++j) knext[j] = row_of(t0 + ECH + j);
 #pragma unroll
-      for (int x = 0; x < DC; ++x) {
-        acc_pd[h][x] = fmaf(pdh[h], kt[x], acc_pd[h][x]);
-        acc_p[h][x] = fmaf(ph[h], kt[x], acc_p[h][x]);
+    for (int j = 0; j < ECH; ++j) {
+      const int t = t0 + j;
+      if (t >= cmax) break;  // uniform
+      const bool valid = keys[j] >= 0;
+      const int kc = valid ? keys[j] : 0;
+      float kt[DC], vt[DC];
+      words_to_floats<T, DC>(kw[j], kt);
+      words_to_floats<T, DC>(vw[j], vt);
+      if (a.rope) rotate_pairs<DC, 1>(kt, a.rope + size_t(kc) * D, c * DC);
+      const float sdot = own_dot<G, LPQ, DC>(qv, kt);
+      const float dp = own_dot<G, LPQ, DC>(dov, vt);
+      const float ex = __builtin_amdgcn_exp2f(sdot * a.scale_log2 - lse2);
+      const float p = valid ? ex : 0.f;
+      const float pdp = p * dp;
+      dvec += pdp;
+      psum += p;
+      if (valid && HS::writer(c)) {
+        a.P[(wrow + t) * G + own] = p;
+        a.dP[(wrow + t) * G + own] = dp;
       }
+      float ph[G], pdh[G];
+      HS::bcast(p, ph);
+      HS::bcast(pdp, pdh);
 #pragma unroll
-    for (int x = 0; x < DC; ++x) {
-      kt[x] = kn[x];
-      vt[x] = vn[x];
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int x = 0; x < DC; ++x) {
+          acc_pd[h][x] = fmaf(pdh[h], kt[x], acc_pd[h][x]);
+          acc_p[h][x] = fmaf(ph[h], kt[x], acc_p[h][x]);
+        }
     }
-    key = key_next;
-    key_next = key_after;
+#pragma unroll
+    for (int j = 0; j < ECH; ++j) keys[j] = knext[j];
   }
 
   // p relative to l = sum p, as in the offset query pass

@@ -84,6 +84,22 @@ __device__ __forceinline__ void load_vec(const bf16_t* __restrict__ p, float (&o
   }
 }
 
+// N elements of T held as raw 32-bit words (N * sizeof(T) / 4 of them),
+// widened to float.
+template <typename T, int N>
+__device__ __forceinline__ void words_to_floats(const uint32_t (&w)[N * sizeof(T) / 4], float (&out)[N]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int x = 0; x < N / 2; ++x) {
+      out[2 * x] = bf16_lo(w[x]);
+      out[2 * x + 1] = bf16_hi(w[x]);
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < N; ++x) out[x] = __uint_as_float(w[x]);
+  }
+}
+
 // One element widened to float.
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ float load1(const bf16_t* p) { return __uint_as_float(uint32_t(*p) << 16); }
