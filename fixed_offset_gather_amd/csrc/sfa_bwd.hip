@@ -39,6 +39,8 @@
 //   dalpha = sum f_k dd_k; dtheta = (alpha - 1/2)(3/2 - alpha) dalpha.
 // The edge-list backward (bwd_edges_query, bwd_edges_key, further below)
 // does the same per query and per key over explicit lists.
+#include <cstring>
+
 #include "sfa_device.h"
 #include "sfa_internal.h"
 
@@ -593,6 +595,39 @@ constexpr int key_half_row_words(int G, int D) {
   return G == 1 ? 2 * key_chunk_h16(D, G) + 4 : key_chunk_h16(D, G) * ((G + 1) / 2) + 4;
 }
 
+// The (slot, tap) steps of the bf16 key pass in order, built on the host
+// from the slot table and passed by value like it (the same size): per step
+// the row delta min(lo, n) + tap, and the tap weight (1 - frac for the
+// nearer row, frac for the farther one, 1 for an integer slot) with its sign
+// bit, free since the weight is positive, set on a slot's first step.  lo of
+// the first and last slot bound the rows whose dS bounds scale the dK
+// weights.
+struct StepTable {
+  int32_t count;  // steps
+  int32_t lo_first, lo_last;
+  int32_t pad_;
+  uint2 rec[2 * SFA_MAX_SLOTS];
+};
+static_assert(sizeof(StepTable) == sizeof(SlotTable), "steps travel like the slots");
+
+inline StepTable make_step_table(const SlotTable& t, int n) {
+  StepTable st{};
+  for (int x = 0; x < t.count; ++x) {
+    const int d0 = t.s[x].lo < n ? t.s[x].lo : n;
+    const float fr = t.s[x].frac;
+    float w0 = 1.f;
+    if (fr > 0.f) w0 = 1.f - fr;
+    uint32_t b0, b1;
+    std::memcpy(&b0, &w0, 4);
+    std::memcpy(&b1, &fr, 4);
+    st.rec[st.count++] = make_uint2(uint32_t(d0), b0 | 0x80000000u);
+    if (fr > 0.f) st.rec[st.count++] = make_uint2(uint32_t(d0 + 1), b1);
+  }
+  st.lo_first = t.count > 0 ? t.s[0].lo : 0;
+  st.lo_last = t.count > 0 ? t.s[t.count - 1].lo : 0;
+  return st;
+}
+
 // Rows per stage of a bf16 key-pass half.  As many as let 16 waves per CU
 // share the 160 KiB of LDS, but at least the block plus 12 rows (a window
 // of 10 and the interpolation tap in one stage; with offsets 8 apart, as in
@@ -782,12 +817,12 @@ __global__ __launch_bounds__(key_block(sizeof(T), G, D)) void bwd_key_kernel(Bwd
 // f16 word empty, so there the staged words hold the fp32 rows and the
 // weights stay fp32 (one FMA per dim and step instead of a dot2 doing one
 // useful MAC), and PART 2 does both halves in one workgroup: a step is then
-// 32 FMAs (dK and dV) for one set of per-step bookkeeping (slot cursor,
+// 32 FMAs (dK and dV) for one set of per-step bookkeeping (step record,
 // weight loads, ring address), which is scalar work that otherwise bounds
 // the pass (more SALU than VALU instructions per wave with the halves
 // apart).
 template <int D, int G, int PART>
-__device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable& st, const int tile) {
+__device__ __forceinline__ void key_half_body(const BwdArgs& a, const StepTable& st, const int tile) {
   constexpr int KB = kKeyBlockH16;
   constexpr int KC = key_chunk_h16(D, G);
   constexpr int NCH = D / KC;
@@ -804,7 +839,6 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   // Dynamic LDS: a.kcap staged rows of RW words.
   extern __shared__ __align__(16) uint32_t key_smem[];
   uint32_t* Ws = key_smem;
-  constexpr int NQ = (SFA_MAX_SLOTS + 63) / 64;  // slot-table columns of 64 slots
 
   const int tid = threadIdx.x;
   const int c = tile % NCH;
@@ -836,8 +870,8 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
     if (a.wmax && st.count > 0) {
       constexpr int BQQ = bwd_bq<G>();
       const int nq = (n + BQQ - 1) / BQQ;
-      const int ilo = max(j0 + max(st.s[0].lo, -n), 0);
-      const int ihi = min(j0 + KB + min(st.s[st.count - 1].lo, n), n - 1);
+      const int ilo = max(j0 + max(st.lo_first, -n), 0);
+      const int ihi = min(j0 + KB + min(st.lo_last, n), n - 1);
       float u = 0.f;
       if (ilo <= ihi) {
         const float* wm = a.wmax + size_t(seq) * nq;
@@ -860,66 +894,52 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
 #pragma unroll
   for (int x = 0; x < (BOTH ? KC : 1); ++x) accv[x] = 0.f;
 
-  // The slot table lives in VGPRs (lane l holds slot l of each 64-slot
-  // column) and is read with v_readlane: no scalar memory access inside the
-  // step loop, whose waits would also drain the LDS reads (both count on
-  // lgkmcnt, and scalar loads return out of order).  Per slot: 2 min(lo, n)
-  // + taps - 1 (|lo| < 2^30, so the doubling fits) and the fraction bits.
-  // Only the prefetch cursor reads it, in slot order: it reads column 0 and
-  // shifts the columns down by one when it crosses into the next (static
-  // register indices only).  The step loop takes each step's row delta and
-  // slot from the queue entry the cursor filled; the stage bounds read the
-  // kernel-argument table between barriers.
-  const int S = st.count;
-  const int lane = tid & 63;
-  int vpk[NQ], vfr[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int sl = q * 64 + lane;
-    const bool in = sl < S;
-    const int sc = in ? sl : 0;
-    const float fr = in ? st.s[sc].frac : 0.f;
-    vpk[q] = 2 * (in ? min(st.s[sc].lo, n) : n) + (fr > 0.f ? 1 : 0);
-    vfr[q] = __float_as_int(fr);
-  }
-  auto slot_lo = [&](int sj) { return min(st.s[sj].lo, n); };  // stage bounds only
+  // The step loop reads one record of the step table per step (a scalar
+  // load issued a step ahead): no per-step cursor branches, and the p and dp
+  // planes move to the next slot's by a scalar select on a slot's first
+  // step (page-1 key pass 79.1 -> 75.6 us against a cursor over the slots).
+  const int nsteps = st.count;
+  auto first_of_slot = [&](int t) { return (st.rec[t].y >> 31) != 0u; };
 
-  // p and 1/l (and for dK dp and Dvec / l) of one (slot, tap) step, loaded
-  // without a branch: the row is clamped to n - 1, and every clamped row is
-  // one the query pass wrote (a slot is only reached while j0 + lo <= n - 1).
-  // A step past the end reloads the last slot's rows; masked steps get zero
-  // weights in convert().  raw: p, 1/l (dV); p, dp, Dvec / l, 1/l (dK).
+  // p and 1/l (and for dK dp and Dvec / l) of one step, loaded without a
+  // branch: the row is clamped to n - 1, and every clamped row is one the
+  // query pass wrote (a slot is only reached while j0 + lo <= n - 1).  A step
+  // past the end reloads the last step's rows; masked steps get zero weights
+  // in convert().  raw: p, 1/l (dV); p, dp, Dvec / l, 1/l (dK).
   constexpr int NR = PART == 1 ? 2 : 4;
   constexpr int RL = NR - 1;  // the 1/l entry
   constexpr int NWT = BOTH ? 2 : GW;  // weight words per step
   // Scalar bases of this sequence's p, dp and Dvec; a slot's plane is a
-  // scalar byte offset from them (advanced by one plane per slot), the row a
-  // 32-bit lane offset.
+  // scalar byte offset from them, the row a 32-bit lane offset.
   const float* const Pseq = uniform_ptr(a.P + size_t(seq) * a.S * n * G);
   const float* const dPseq = uniform_ptr(a.dP + size_t(seq) * a.S * n * G);
   const float* const Dseq = uniform_ptr(a.Dvec + size_t(seq) * n * G);
   const float* const Lseq = uniform_ptr(a.Linv + size_t(seq) * n * G);
   const unsigned plane_b = unsigned(n) * unsigned(G * 4);
-  // the prefetch cursor: step (fs, ft), its slot's min(lo, n), taps and
-  // fraction, and the byte offset of its slot's plane (kept at the last
-  // slot once past the end)
-  int fs = 0, ft = 0, flo = 0, ftaps = 1;
-  float fw = 0.f;
-  unsigned fplane = 0;
-  // A queue entry: the loads of one (slot, tap) step, its weight factor
-  // (the tap weight wt, 1 - frac for the nearer row and frac for the farther
-  // one, or 0 for a masked step), its slot (S past the end) and its row
+  // The loader: the step whose loads are queued next, the byte offset of its
+  // slot's plane (one plane before slot 0 until step 0 moves it there; kept
+  // at the last slot once past the end) and its record.
+  int fstep = 0;
+  unsigned fplane = 0u - plane_b;
+  uint2 frec = make_uint2(0u, 0u);
+  if (nsteps > 0) frec = st.rec[0];
+  // A queue entry: the loads of one step, its weight factor (the tap weight,
+  // or 0 for a masked step), its index (nsteps past the end) and its row
   // delta lo + tap.
   struct QE {
     float raw[NR][G];
     float ws;
-    int slot, delta;
+    int step, delta;
   };
-  // The three loads share the lane's 32-bit byte offset i * G * 4 from
-  // uniform bases (the slot's planes of p and dp, and Dvec), so the address
+  // The loads share the lane's 32-bit byte offset i * G * 4 from uniform
+  // bases (the slot's planes of p and dp, and Dvec), so the address
   // arithmetic is scalar except for that offset.
   auto load_step = [&](QE& q) {
-    const int i = min(max(j + flo + ft, 0), n - 1);
+    const int delta = int(frec.x);
+    const uint32_t wb = frec.y;
+    const bool live = fstep < nsteps;
+    fplane += live && (wb >> 31) ? plane_b : 0u;
+    const int i = min(max(j + delta, 0), n - 1);
     const unsigned ioff = unsigned(i) * unsigned(G * 4);
     load_global_at<G>(Pseq, fplane + ioff, q.raw[0]);
     if constexpr (PART != 1) {
@@ -927,11 +947,12 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
       load_global_at<G>(Dseq, ioff, q.raw[2]);
     }
     load_global_at<G>(Lseq, ioff, q.raw[RL]);
-    const bool valid = fs < S && unsigned(j + flo + ft) < unsigned(n);
-    const float wt = ft ? fw : 1.f - fw;
-    q.ws = valid ? wt : 0.f;
-    q.slot = fs;
-    q.delta = flo + ft;
+    const bool valid = live && unsigned(j + delta) < unsigned(n);
+    q.ws = valid ? __uint_as_float(wb & 0x7fffffffu) : 0.f;
+    q.step = fstep;
+    q.delta = delta;
+    fstep += live ? 1 : 0;
+    frec = st.rec[min(fstep, nsteps - 1)];  // the next record, a step ahead
   };
   // f16 weight pairs of a queued step (G = 1: one fp32 weight): ws dS, dS =
   // p/l (dp - Dvec/l), for dK, ws p/l for dV.  Every loaded value is finite
@@ -958,53 +979,22 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
       }
     }
   };
-  // advance the cursor one step; it stays at (S, 0) once past the end
-  auto set_cursor_slot = [&]() {  // fs < S
-    if ((fs & 63) == 0 && fs > 0) {  // into the next column: shift them down
-#pragma unroll
-      for (int q = 0; q + 1 < NQ; ++q) {
-        vpk[q] = vpk[q + 1];
-        vfr[q] = vfr[q + 1];
-      }
-    }
-    const int x = __builtin_amdgcn_readlane(vpk[0], fs & 63);
-    flo = x >> 1;
-    ftaps = (x & 1) + 1;
-    fw = ftaps > 1 ? __int_as_float(__builtin_amdgcn_readlane(vfr[0], fs & 63)) : 0.f;
-  };
-  auto advance = [&]() {
-    if (ft + 1 < ftaps) {
-      ++ft;
-    } else if (fs < S) {
-      ++fs;
-      ft = 0;
-      if (fs < S) {
-        set_cursor_slot();
-        fplane += plane_b;
-      }
-    }
-  };
 
-  // Software pipeline along the (slot, tap) sequence, straight across stage
-  // boundaries: wts holds the weights of the step being computed and the
-  // queue the loads of the PF steps after it (the cursor is the last of
-  // them).  The end of each step converts the queue's head into the next
-  // weights, shifts the queue and loads the step PF ahead, so every load has
-  // PF steps to arrive.
+  // Software pipeline along the steps, straight across stage boundaries:
+  // wts holds the weights of the step being computed and the queue the loads
+  // of the PF steps after it.  The end of each step converts the queue's
+  // head into the next weights, shifts the queue and loads the step PF
+  // ahead, so every load has PF steps to arrive.
   uint32_t wts[NWT] = {};
-  int wslot = S, wdelta = 0;  // slot and row delta of the step being computed
+  int wstep = nsteps, wdelta = 0;  // step being computed and its row delta
   QE que[PF];
-  if (S > 0) {
-    set_cursor_slot();
+  if (nsteps > 0) {
     load_step(que[0]);
     convert(que[0], wts);
-    wslot = que[0].slot;
+    wstep = que[0].step;
     wdelta = que[0].delta;
 #pragma unroll
-    for (int k = 0; k < PF; ++k) {
-      advance();
-      load_step(que[k]);
-    }
+    for (int k = 0; k < PF; ++k) load_step(que[k]);
   }
   // The staged rows form a ring in LDS: query j0 + q sits in slot
   // (q - q0) mod kcap, q0 the first stage's first row.  Stages run in
@@ -1020,17 +1010,17 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
   asm volatile("" : "+v"(tid_b));
   int q0 = 0, have_hi = 0;
   bool first_stage = true;
-  int s = 0;
-  while (s < S) {
-    const int lo0 = slot_lo(s);
+  int ts = 0;  // the stage's first step (a slot's first)
+  while (ts < nsteps) {
+    const int lo0 = int(st.rec[ts].x);  // min(lo, n) of the stage's first slot
     if (j0 + lo0 > n - 1) break;
     int lomax = lo0;
-    int e = s;
-    while (e < S) {
-      const int le = slot_lo(e);
+    int te = ts;  // a stage holds whole slots: steps [ts, te)
+    while (te < nsteps) {
+      const int le = int(st.rec[te].x);
       if (j0 + le > n - 1 || le - lo0 + KB + 1 > kcap) break;
       lomax = le;
-      ++e;
+      te += te + 1 < nsteps && !first_of_slot(te + 1) ? 2 : 1;
     }
     const int r0 = j0 + lo0;
     const int nrows = min(lomax - lo0 + KB + 1, n - r0);
@@ -1165,9 +1155,13 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
     __syncthreads();
     have_hi = max(have_hi, hi);
 
-    // every step of the slots [s, e): the steps are in slot order
-    while (wslot < e) {
+    // every step of the stage
+    while (wstep < te) {
       {
+        // The next record's scalar load lands here, before the row reads:
+        // with it still in flight every wait on the row reads would have to
+        // drain all LDS reads.
+        asm volatile("" ::"s"(frec.x), "s"(frec.y));
         const int delta = wdelta;
         // Query j + delta; the query pass stored p = 0 where the slot has no
         // row for it.  Masked steps read ring slot 0 with zero weights.
@@ -1211,18 +1205,22 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const SlotTable&
           }
         }
 
-        // weights of the next step, then the loads of the step PF ahead
+        // weights of the next step, then the loads of the step PF ahead.
+        // The barrier keeps the conversion, which waits for the queued
+        // loads, after this step's row reads and dot products: hoisted above
+        // them it made every step wait for its weights before reading its
+        // rows (page-1 key pass 84.2 against 79 us).
+        __builtin_amdgcn_sched_barrier(0);
         convert(que[0], wts);
-        wslot = que[0].slot;
+        wstep = que[0].step;
         wdelta = que[0].delta;
 #pragma unroll
         for (int k = 0; k + 1 < PF; ++k) que[k] = que[k + 1];
         __builtin_amdgcn_sched_barrier(0);
-        advance();
         load_step(que[PF - 1]);
       }
     }
-    s = e;
+    ts = te;
   }
   if (activej) {
     if constexpr (PART == 0 && !BOTH) {
@@ -1271,7 +1269,7 @@ __device__ __forceinline__ KeyTile key_tile_order(int bid, int T, int halves, in
 // as a kernel after them; the others return at once, so every key tile
 // keeps its XCD.
 template <int D, int G>
-__global__ __launch_bounds__(kKeyBlockH16) void bwd_key_h16_kernel(BwdArgs a, SlotTable st, ReduceArgs ra) {
+__global__ __launch_bounds__(kKeyBlockH16) void bwd_key_h16_kernel(BwdArgs a, StepTable st, ReduceArgs ra) {
   int bid = blockIdx.x;
   if (ra.n_rungs > 0) {
     if (bid < kNumXcd) {
@@ -1387,12 +1385,13 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, const ReduceArgs* ra, hi
     a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk_h16(D, G));
     a.kcap = key_half_cap(G, D);
     const size_t lds = size_t(a.kcap) * key_half_row_words(G, D) * 4;
+    const StepTable steps = make_step_table(t, a.n);
     static_assert(sizeof(double) * SFA_MAX_OFFSETS <= size_t(kKeyBlockH16 + 12) * 4 * key_half_row_words(G, D),
                   "the reduce workgroup's doubles fit the key pass's LDS");
     ReduceArgs r{};  // n_rungs = 0: no reduce workgroups
     if (ra) r = *ra;
     const int grid = (G == 1 ? a.tiles : 2 * a.tiles) + (r.n_rungs > 0 ? kNumXcd : 0);
-    hipLaunchKernelGGL((bwd_key_h16_kernel<D, G>), dim3(grid), dim3(KB), lds, st, a, t, r);
+    hipLaunchKernelGGL((bwd_key_h16_kernel<D, G>), dim3(grid), dim3(KB), lds, st, a, steps, r);
   } else {
     constexpr int KB = key_block(sizeof(T), G, D);
     a.nblk = (a.n + KB - 1) / KB;

@@ -240,12 +240,32 @@ def key_chunk_h16(D, G):
     return 32 if G >= 4 and D >= 32 else min(16, D)
 
 
+def key_half_row_words(G, D):
+    """sfa_bwd.hip key_half_row_words."""
+    kc = key_chunk_h16(D, G)
+    return 2 * kc + 4 if G == 1 else kc * ((G + 1) // 2) + 4
+
+
 def key_half_cap(G, D):
     """sfa_bwd.hip key_half_cap."""
-    kc = key_chunk_h16(D, G)
-    rw = 2 * kc + 4 if G == 1 else kc * ((G + 1) // 2) + 4
-    cap = (163840 * (KB_H16 // 64) // 16) // (4 * rw)
+    cap = (163840 * (KB_H16 // 64) // 16) // (4 * key_half_row_words(G, D))
     return min(max(cap, KB_H16 + 12), KB_H16 + 64)
+
+
+def key_step_table(sl, n):
+    """sfa_bwd.hip make_step_table: the (slot, tap) steps in order as (delta,
+    tap weight, first step of a slot); at most twice the slot capacity."""
+    table = []
+    for x in sl:
+        lo, fr = x[0], x[1]
+        d0 = min(lo, n)
+        if fr > 0.0:
+            table.append((d0, np.float32(1.0) - np.float32(fr), True))
+            table.append((d0 + 1, np.float32(fr), False))
+        else:
+            table.append((d0, np.float32(1.0), True))
+    check(len(table) <= 2 * MAX_SLOTS, "step table capacity")
+    return table
 
 
 def key_pass_h16(n, window, lo, frac, G, D=64, batch_kv=1):
@@ -255,7 +275,10 @@ def key_pass_h16(n, window, lo, frac, G, D=64, batch_kv=1):
     and plane offsets of the weight loads.  Returns the number of steps."""
     sl = build_slots(window, lo, frac)
     S = len(sl)
+    table = key_step_table(sl, n)
+    nsteps = len(table)
     kcap = key_half_cap(G, D)
+    check(kcap * key_half_row_words(G, D) * 4 <= 163840, "key-pass LDS of a workgroup")
     KB = KB_H16
     nblk = (n + KB - 1) // KB
     tid = np.arange(KB)
@@ -275,12 +298,25 @@ def key_pass_h16(n, window, lo, frac, G, D=64, batch_kv=1):
             check(0 <= ilo // bq <= ihi // bq < nq, "dS bound tiles inside the sequence")
         ring = np.full(kcap, -(10 ** 9), dtype=np.int64)  # query held by each ring slot
         q0, have_hi, first = 0, 0, True
-        # the prefetch cursor's weight loads run over every step of the table
-        # (rows clamped to [0, n); the last sequence bounds the others)
-        for fs in range(S):
-            i = np.clip(j + lo_c[fs] + np.arange(taps[fs])[:, None], 0, n - 1)
-            check((fs * n * G + i * G >= 0) & (((batch_kv - 1) * S + fs) * n * G + i * G + G <= p_size),
-                  "key-pass weight load offset")
+        # the loader's weight loads run over every step of the table and
+        # once more past the end (rows clamped to [0, n); the plane advances
+        # on a slot's first step and stays once past the end; the last
+        # sequence bounds the others)
+        slot_of = [sj for sj in range(S) for _ in range(taps[sj])]
+        tap_of = [tp for sj in range(S) for tp in range(taps[sj])]
+        plane = -1
+        for fstep in range(nsteps + 2):
+            d, w, first_of_slot = table[min(fstep, nsteps - 1)]
+            live = fstep < nsteps
+            if live and first_of_slot:
+                plane += 1
+            if live:
+                sj = slot_of[fstep]
+                wt = np.float32(sl[sj][1]) if tap_of[fstep] else np.float32(1.0) - np.float32(sl[sj][1])
+                check(plane == sj and d == lo_c[sj] + tap_of[fstep] and w == wt, "step record of its slot and tap")
+            i = np.clip(j + d, 0, n - 1)
+            check((0 <= plane < S) & np.all(plane * n * G + i * G >= 0) &
+                  np.all(((batch_kv - 1) * S + plane) * n * G + i * G + G <= p_size), "key-pass weight load offset")
         s = 0
         while s < S:
             lo0 = lo_c[s]
@@ -312,9 +348,15 @@ def key_pass_h16(n, window, lo, frac, G, D=64, batch_kv=1):
             check(rn + rows < n, "staged query rows below n")
             ring[slot] = rn + rows  # rows before the sequence are staged as zeros
             have_hi = max(have_hi, hi)
+            ts = sum(taps[:s])
+            te = ts + sum(taps[s:e])
+            check(te <= nsteps and table[ts][2] and (te == nsteps or table[te][2]), "stage step range")
+            t = ts
             for sj in range(s, e):
                 for tap in range(taps[sj]):
                     delta = lo_c[sj] + tap
+                    check(table[t][0] == delta, "step record delta")
+                    t += 1
                     valid = (j + delta >= 0) & (j + delta < n)
                     soff = delta - lo0 + base
                     wrap = tid >= kcap - soff

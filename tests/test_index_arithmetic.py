@@ -107,14 +107,15 @@ def test_negative_offset_rotary_row_mistake_is_caught():
 def test_ring_wrap_mistake_is_caught(monkeypatch):
     # The same ring without the wrap at kcap reads past the ring.
     orig = np.where
+    n, W, lo, fr = TABLES["page1_learned"]
+    kcap = im.key_half_cap(4, 64)
 
     def no_wrap(cond, a, b):
-        if np.isscalar(a) and a == im.key_half_cap(4, 64) and np.isscalar(b) and b == 0:
+        if np.isscalar(a) and a == kcap and np.isscalar(b) and b == 0:
             return np.zeros_like(cond, dtype=np.int64)
         return orig(cond, a, b)
 
     monkeypatch.setattr(im.np, "where", no_wrap)
-    n, W, lo, fr = TABLES["page1_learned"]
     with pytest.raises(im.IndexModelError):
         im.key_pass_h16(n, W, lo, fr, 4)
 
@@ -166,3 +167,25 @@ def test_key_tile_order_is_a_balanced_bijection(halves, nseq, nblk, nch):
                 if (T // im.NUM_XCD) % (nblk * nch) == 0:
                     blk = (tile[sel] // nch) % nblk
                     assert np.all(np.diff(blk) >= 0)
+
+
+def test_step_table_mistake_is_caught(monkeypatch):
+    # A step table that gives the farther tap the nearer tap's weight (1 -
+    # frac for both) no longer names its slot's taps.
+    orig = im.key_step_table
+
+    def wrong_weight_any(sl, n):
+        t = orig(sl, n)
+        fr = [x[1] for x in sl if x[1] > 0.0]
+        out, k = [], 0
+        for d, w, first in t:
+            if not first:
+                w = np.float32(1.0) - np.float32(fr[k])
+                k += 1
+            out.append((d, w, first))
+        return out
+
+    monkeypatch.setattr(im, "key_step_table", wrong_weight_any)
+    n, W, lo, fr = TABLES["page1_learned"]
+    with pytest.raises(im.IndexModelError, match="step record"):
+        im.key_pass_h16(n, W, lo, fr, 4)
