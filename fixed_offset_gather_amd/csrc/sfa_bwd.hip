@@ -65,7 +65,7 @@ constexpr int key_chunk_h16(int D, int G) { return G >= 4 && D >= 32 ? 32 : key_
 // heads per KV head, 8-lane queries in blocks of 64 (8 waves) with 128-row
 // stages: two workgroups share a CU (Christoffel query pass 210 -> 163 us
 // against 32-query blocks).  With G >= 4 a query takes 16 lanes, and blocks
-// of 16 queries (4 waves) with 72-row stages (39.7 KB of LDS) put four
+// of 16 queries (4 waves) with 72-row stages (30.6 KB of LDS) put four
 // workgroups on a CU: the same 16 waves as two of 32 queries with 128-row
 // stages, in workgroups half as long, so the launch's tail (the CUs left
 // idle while its last workgroups finish) is half as long too (page-1 query
@@ -144,16 +144,23 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
   constexpr int RW_DD = RPL * ND;   // rungs whose dd one launch sums
   using HS = HeadSlice<G, LPQ>;
   static_assert((ND & (ND - 1)) == 0 && NT % 64 == 0, "lane groups");
-  // K and V rows of a stage in one LDS array, each led by a pad row:
-  // [pad][K rows 0..CAP-1][pad][V rows 0..CAP-1].  Row r - 1 of a slot (its
-  // interpolation partner, or a pad row when r = 0) is then never below the
-  // array, and the four rows a slot reads lie at fixed byte offsets from it,
-  // so one address per slot serves all of them.
-  constexpr int VOFF = (CAP + 1) * KS;  // floats from a K row to the same V row
-  static_assert((VOFF + KS) * 4 < 65536, "row offsets fit a ds_read offset");
-  __shared__ __align__(16) float KV[(2 * CAP + 2) * KS];
+  // bf16: V rows stay the bf16 input words and dO is held as bf16 pairs, so
+  // dp = dO . V takes v_dot2_f32_bf16 (exact products, fp32 sums).  V rows
+  // are never interpolated: a slot that reads rows r and r - 1 forms
+  // dO . V[r] and dO . V[r - 1] and lerps the two sums (the offset gradient
+  // needs both anyway).  fp32 tensors: fp32 V rows, the same sums by FMA.
+  constexpr bool kRawV = sizeof(T) == 2;
+  constexpr int VWL = kRawV ? DC / 2 : DC;     // V words per lane
+  constexpr int KSV = kRawV ? D / 2 + 4 : KS;  // words per V row (16-byte pad)
+  // K and V rows of a stage, each array led by a pad row: [pad][K rows
+  // 0..CAP-1][pad][V rows 0..CAP-1].  Row r - 1 of a slot (its
+  // interpolation partner, or a pad row when r = 0) is then never below its
+  // array, and a slot's two K rows (and its two V rows) lie at fixed byte
+  // offsets from one address.
+  constexpr int VOFF = (CAP + 1) * KS;  // words from the K array to the V array
+  __shared__ __align__(16) float KV[(CAP + 1) * KS + (CAP + 1) * KSV];
   float* const Ks = KV + KS;
-  float* const Vs = Ks + VOFF;
+  uint32_t* const Vw = reinterpret_cast<uint32_t*>(KV + VOFF) + KSV;
 
   const int tid = threadIdx.x;
   const int qq = tid / LPQ;
@@ -177,17 +184,21 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
 
   // acc_pd = sum p dp k~, acc_p = sum p k~ ; dq~ = scale (acc_pd - Dvec acc_p)
   // Register j of a lane holds head HS::head(c, j) of the group.
-  float qv[G][DC], dov[G][DC], acc_pd[G][DC], acc_p[G][DC];
+  // dO: VWL words per head, bf16 pairs (bf16) or fp32 bits (fp32).
+  float qv[G][DC], acc_pd[G][DC], acc_p[G][DC];
+  uint32_t dow[G][VWL];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
     if (active) {
       const size_t off = ((size_t(b) * n + i) * a.hq + size_t(g) * G + HS::head(c, j)) * D + c * DC;
       load_vec<DC>(Q + off, qv[j]);
       if (a.rope) rotate_pairs<DC, 1>(qv[j], a.rope + size_t(i) * D, c * DC);
-      load_vec<DC>(dO + off, dov[j]);
+      load_words<VWL>(reinterpret_cast<const uint32_t*>(dO + off), dow[j]);
     } else {
 #pragma unroll
-      for (int x = 0; x < DC; ++x) qv[j][x] = dov[j][x] = 0.f;
+      for (int x = 0; x < DC; ++x) qv[j][x] = 0.f;
+#pragma unroll
+      for (int x = 0; x < VWL; ++x) dow[j][x] = 0u;
     }
 #pragma unroll
     for (int x = 0; x < DC; ++x) acc_pd[j][x] = acc_p[j][x] = 0.f;
@@ -242,22 +253,38 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
     for (int t = tid; t < nrows * CPR; t += NT) {
       const int row = t / CPR, cc = t % CPR;
       const int pos = r0 + row;
-      float kf[E], vf[E];
+      float kf[E];
+      uint32_t vw[4];  // 16 bytes of V as they are
       if (pos >= 0 && pos < n) {
         load_vec<E>(Kseq + size_t(pos) * kv_row + cc * E, kf);
-        load_vec<E>(Vseq + size_t(pos) * kv_row + cc * E, vf);
+        load_words<4>(reinterpret_cast<const uint32_t*>(Vseq + size_t(pos) * kv_row + cc * E), vw);
         if (a.rope) rotate_pairs<E, 1>(kf, a.rope + size_t(pos) * D, cc * E);
       } else {
 #pragma unroll
-        for (int x = 0; x < E; ++x) kf[x] = vf[x] = 0.f;
+        for (int x = 0; x < E; ++x) kf[x] = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) vw[x] = 0u;
       }
       store_vec<E>(Ks + row * KS + cc * E, kf);
-      store_vec<E>(Vs + row * KS + cc * E, vf);
+      store_words<4>(Vw + row * KSV + cc * 4, vw);
     }
     __syncthreads();
 
-    // K row r - 1 of the slot at lo = 0; a slot's rows are lo rows earlier.
-    const float* const lane_kv = Ks + (i - r0 - 1) * KS + c * DC;
+    // K and V rows r - 1 of the slot at lo = 0; a slot's rows are lo rows
+    // earlier.
+    const float* const lane_k = Ks + (i - r0 - 1) * KS + c * DC;
+    const uint32_t* const lane_v = Vw + (i - r0 - 1) * KSV + c * VWL;
+    // dO . V over the lane's dims of every head (register order)
+    auto dov_dot = [&](const uint32_t (&vr)[VWL], float (&out)[G]) {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int x = 0; x < VWL; ++x)
+          acc = kRawV ? dot2_bf(dow[j][x], vr[x], acc) : fmaf(__uint_as_float(dow[j][x]), __uint_as_float(vr[x]), acc);
+        out[j] = acc;
+      }
+    };
     for (int sj = s; sj < e; ++sj) {
       const Slot cur = st.s[sj];  // one 16-byte scalar load
       const int lo = cur.lo;
@@ -266,63 +293,56 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
       const int wbits = __float_as_int(cur.frac);
       const float w = __int_as_float(wbits);
       const bool interp = wbits != 0;
-      const float* const kp = lane_kv - lo * KS;  // K row r - 1
+      const float* const kp = lane_k - lo * KS;      // K row r - 1
+      const uint32_t* const vp = lane_v - lo * KSV;  // V row r - 1
       const bool dds = dd_of(cur);
-      float kt[DC], vt[DC], dk[DC], dv[DC];
+      const bool two = interp || dds;  // reads rows r and r - 1
+      float kt[DC], dk[DC];
+      uint32_t vt[VWL], vb[VWL];
       load_vec<DC>(kp + KS, kt);
-      load_vec<DC>(kp + KS + VOFF, vt);
-      if (interp || dds) {
-        // dK = row r - 1 minus row r: the lerp's slope and dd's factor.  A
-        // dd slot keeps both V rows as they are (dv = row r - 1): dp and
-        // dO . dV then follow from the two row dots, and V needs no lerp.
-        float kb[DC], vb[DC];
+      load_words<VWL>(vp + KSV, vt);
+      if (two) {
+        // dK = row r - 1 minus row r: the lerp's slope and dd's factor
+        float kb[DC];
         load_vec<DC>(kp, kb);
-        load_vec<DC>(kp + VOFF, vb);
+        load_words<VWL>(vp, vb);
 #pragma unroll
-        for (int x = 0; x < DC; ++x) {
-          dk[x] = kb[x] - kt[x];
-          dv[x] = dds ? vb[x] : vb[x] - vt[x];
-        }
+        for (int x = 0; x < DC; ++x) dk[x] = kb[x] - kt[x];
         if (interp) {
 #pragma unroll
-          for (int x = 0; x < DC; ++x) {
-            kt[x] = fmaf(w, dk[x], kt[x]);
-            if (!dds) vt[x] = fmaf(w, dv[x], vt[x]);
-          }
+          for (int x = 0; x < DC; ++x) kt[x] = fmaf(w, dk[x], kt[x]);
         }
       }
       float sp[G], dps[G];
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        float s1 = 0.f, s2 = 0.f;
+        float s1 = 0.f;
 #pragma unroll
-        for (int x = 0; x < DC; ++x) {
-          s1 = fmaf(qv[j][x], kt[x], s1);
-          s2 = fmaf(dov[j][x], vt[x], s2);
-        }
+        for (int x = 0; x < DC; ++x) s1 = fmaf(qv[j][x], kt[x], s1);
         sp[j] = s1;
-        dps[j] = s2;
       }
+      dov_dot(vt, dps);
       const float sdot = HS::reduce(sp);
-      float dp = HS::reduce(dps);  // a dd slot: dO . V[r], the nearer row
-      // dd slot: sd = q~ . dK and vd = dO . dV of the own head, fp32
+      float dp = HS::reduce(dps);  // dO . V[r], the nearer row
+      // Rows r and r - 1: vd = dO . (V[r - 1] - V[r]) and, for a dd slot,
+      // sd = q~ . dK of the own head, fp32
       float sd = 0.f, vd = 0.f;
-      if (dds) {
-        float sdp[G], vdp[G];
+      if (two) {
+        float vbp[G];
+        dov_dot(vb, vbp);
+        vd = HS::reduce(vbp) - dp;
+        dp = fmaf(w, vd, dp);  // dO . lerp(V[r], V[r - 1], frac)
+        if (dds) {
+          float sdp[G];
 #pragma unroll
-        for (int j = 0; j < G; ++j) {
-          float s1 = 0.f, s2 = 0.f;
+          for (int j = 0; j < G; ++j) {
+            float s1 = 0.f;
 #pragma unroll
-          for (int x = 0; x < DC; ++x) {
-            s1 = fmaf(qv[j][x], dk[x], s1);
-            s2 = fmaf(dov[j][x], dv[x], s2);
+            for (int x = 0; x < DC; ++x) s1 = fmaf(qv[j][x], dk[x], s1);
+            sdp[j] = s1;
           }
-          sdp[j] = s1;
-          vdp[j] = s2;
+          sd = HS::reduce(sdp);
         }
-        sd = HS::reduce(sdp);
-        vd = HS::reduce(vdp) - dp;  // dO . V[r - 1] - dO . V[r]
-        dp = fmaf(w, vd, dp);       // dO . lerp(V[r], V[r - 1], frac)
       }
       // The nearer row i - lo exists when mn <= i - lo <= n - 1, mn = 1 for
       // an interpolated slot (its farther row i - lo - 1 must exist too):
@@ -395,13 +415,16 @@ void bwd_query_kernel(BwdArgs a, SlotTable st) {
       static_assert(KC % DC == 0, "a lane's dims lie in one chunk");
       const int ch = (c * DC) / KC, x0 = (c * DC) % KC;
       const size_t wrow = ((size_t(seq) * n + i) * (D / KC) + ch) * (GW * KC) + x0;
+      float dof[G][DC];
+#pragma unroll
+      for (int j = 0; j < G; ++j) words_to_floats<T, DC>(dow[j], dof[j]);
       uint32_t pq[GW][DC], pd[GW][DC];
 #pragma unroll
       for (int m = 0; m < GW; ++m)
 #pragma unroll
         for (int x = 0; x < DC; ++x) {
           pq[m][x] = pack_h2(qv[2 * m][x], qv[2 * m + 1][x]);
-          pd[m][x] = pack_h2(dov[2 * m][x], dov[2 * m + 1][x]);
+          pd[m][x] = pack_h2(dof[2 * m][x], dof[2 * m + 1][x]);
         }
 #pragma unroll
       for (int hp = 0; hp < GW; ++hp) {
