@@ -74,9 +74,15 @@ template <int G>
 constexpr int bwd_bq() {
   return G >= 4 ? 16 : 64;
 }
-template <int G>
+// Rows per stage: 72 with G >= 4 (four 16-query workgroups per CU).  With
+// fewer heads, as many as let two 64-query workgroups share the 160 KiB of
+// LDS: bf16 V rows take half the bytes of fp32 ones, so a bf16 stage holds
+// 188 rows (180 beside the dd partials of a many-rung launch), more slots
+// per staging round (Christoffel query pass 151.8 -> 148.4 us causal,
+// 322.3 -> 312.6 us bidirectional, against 128).
+template <typename T, int G, int RPL>
 constexpr int bwd_query_cap() {
-  return G >= 4 ? 72 : kCap;
+  return G >= 4 ? 72 : sizeof(T) == 4 ? kCap : RPL > 4 ? 180 : 188;
 }
 
 struct BwdArgs {
@@ -1387,12 +1393,12 @@ int launch_query_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
   a.want_dd = dd ? 1 : 0;
   a.r0 = 0;
   if (!dd || t.n_rungs <= RS * ND) {
-    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<G>(), BQ, RS>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<T, G, RS>(), BQ, RS>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
     return int(hipGetLastError());
   }
   for (int r0 = 0; r0 < t.n_rungs; r0 += kRplLarge * ND) {
     a.r0 = r0;
-    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<G>(), BQ, kRplLarge>), dim3(a.tiles), dim3(BQ * LPQ), 0, st,
+    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<T, G, kRplLarge>(), BQ, kRplLarge>), dim3(a.tiles), dim3(BQ * LPQ), 0, st,
                        a, t);
     if (hipError_t e = hipGetLastError()) return int(e);
   }

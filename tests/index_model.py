@@ -167,22 +167,42 @@ def bwd_bq(G):
     return 16 if G >= 4 else 64
 
 
-def bwd_query_cap(G):
+def bwd_query_cap(G, esize=2, rpl=1):
     """sfa_bwd.hip bwd_query_cap: rows per query-pass stage."""
-    return 72 if G >= 4 else CAP
+    if G >= 4:
+        return 72
+    if esize == 4:
+        return CAP
+    return 180 if rpl > 4 else 188
 
 
-def query_pass(n, window, lo, frac, D, G, want_dd=True, batch_kv=1):
+def bwd_query_lds(D, G, esize, rpl):
+    """Bytes of LDS of a bwd_query workgroup: the K rows (fp32), the V rows
+    (the input words), each array led by a pad row, the dd partials and the
+    |dS| bound slots."""
+    lpq, bq = bwd_lpq(D, G), bwd_bq(G)
+    cap = bwd_query_cap(G, esize, rpl)
+    ks = D + 4
+    ksv = D // 2 + 4 if esize == 2 else ks
+    nwv = bq * lpq // 64
+    return (cap + 1) * (ks + ksv) * 4 + nwv * rpl * (lpq // G) * 4 + nwv * 4
+
+
+def query_pass(n, window, lo, frac, D, G, want_dd=True, batch_kv=1, esize=2):
     """bwd_query_kernel: stages (slots with a second row: interpolated or dd),
     the LDS rows each query reads, the p / dp workspace offsets of the writer
     lanes and the dd partial indices (one launch per rung window)."""
     sl = build_slots(window, lo, frac)
     S = len(sl)
     n_rungs = len(lo)
-    lpq, bq, qcap = bwd_lpq(D, G), bwd_bq(G), bwd_query_cap(G)
+    lpq, bq = bwd_lpq(D, G), bwd_bq(G)
     nd = lpq // G
     rpl_small = 1 if nd >= 16 else 16 // nd
     rpl = rpl_small if (not want_dd or n_rungs <= rpl_small * nd) else 16
+    qcap = bwd_query_cap(G, esize, rpl)
+    # a CU holds two workgroups of 64 queries (fewer than 4 heads per KV
+    # head) or four of 16
+    check(bwd_query_lds(D, G, esize, rpl) * (2 if G < 4 else 4) <= 163840, "query-pass LDS per CU")
     windows = [0] if (not want_dd or n_rungs <= rpl * nd) else list(range(0, n_rungs, rpl * nd))
     nblk = (n + bq - 1) // bq
     tiles = nblk * batch_kv

@@ -68,6 +68,7 @@ def test_query_pass_stages_rows_and_workspace(name):
     for D, G in ((64, 4), (64, 1), (32, 2), (16, 8)):
         im.query_pass(n, W, lo, fr, D, G, want_dd=True, batch_kv=2)
         im.query_pass(n, W, lo, fr, D, G, want_dd=False)
+        im.query_pass(n, W, lo, fr, D, G, want_dd=True, esize=4)
 
 
 def test_query_pass_rung_windows():
