@@ -926,7 +926,7 @@ __device__ __forceinline__ void key_half_body(const BwdArgs& a, const StepTable&
   // The step loop reads one record of the step table per step (a scalar
   // load issued a step ahead): no per-step cursor branches, and the p and dp
   // planes move to the next slot's by a scalar select on a slot's first
-  // step (page-1 key pass 79.1 -> 75.6 us against a cursor over the slots).
+  // step (page-1 key pass 78.9 -> 73.2 us against a cursor over the slots).
   const int nsteps = st.count;
   auto first_of_slot = [&](int t) { return (st.rec[t].y >> 31) != 0u; };
 
