@@ -25,8 +25,12 @@ int validate_problem(const sfa_attn* a, Problem* p) {
   const int G = a->hq / a->hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8)
     return fail(SFA_ERR_UNSUPPORTED, "group size hq/hkv = %d not in {1,2,4,8}", G);
-  if (a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64)
-    return fail(SFA_ERR_UNSUPPORTED, "head_dim %d not in {16,32,64}", a->head_dim);
+  if (a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
+    return fail(SFA_ERR_UNSUPPORTED, "head_dim %d not in {16,32,64,128}", a->head_dim);
+  // fp32 rows of 128 dims would put a stage's V rows beyond the reach of an
+  // LDS instruction's offset from its K rows; only bf16 tensors are built there.
+  if (a->head_dim == 128 && a->dtype == SFA_F32)
+    return fail(SFA_ERR_UNSUPPORTED, "head_dim 128 is built for bf16 tensors only");
   if (a->head_dim / G < 2) return fail(SFA_ERR_UNSUPPORTED, "head_dim / group < 2");
   if (a->dtype != SFA_F32 && a->dtype != SFA_BF16) return fail(SFA_ERR_ARG, "unknown dtype %d", a->dtype);
   if (a->window < 0) return fail(SFA_ERR_ARG, "window must be >= 0");

@@ -1443,8 +1443,10 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, const ReduceArgs* ra, hi
     else if (d_ == 32) SFA_DISPATCH_G(T, 32, FN, g_, __VA_ARGS__); \
     else SFA_DISPATCH_G(T, 16, FN, g_, __VA_ARGS__);             \
   } while (0)
+// bf16 tensors also come with 128 dims (fp32 ones are refused there).
 #define SFA_DISPATCH(FN, P, ...)                                 \
   do {                                                           \
+    if ((P).dtype == SFA_BF16 && (P).D == 128) SFA_DISPATCH_G(bf16_t, 128, FN, (P).G, __VA_ARGS__); \
     if ((P).dtype == SFA_BF16) SFA_DISPATCH_D(bf16_t, FN, (P).D, (P).G, __VA_ARGS__); \
     else SFA_DISPATCH_D(float, FN, (P).D, (P).G, __VA_ARGS__);   \
   } while (0)

@@ -863,6 +863,7 @@ int launch_fwd_edges_t(const EdgeArgs& a, hipStream_t st) {
   do {                                                                                \
     const int d_ = (P).D, g_ = (P).G;                                                 \
     if ((P).dtype == SFA_BF16) {                                                      \
+      if (d_ == 128) SFA_DISPATCH_G(bf16_t, 128, FN, g_, __VA_ARGS__); /* bf16 only */ \
       SFA_DISPATCH_D(bf16_t, FN, d_, g_, __VA_ARGS__);                                \
     } else {                                                                          \
       SFA_DISPATCH_D(float, FN, d_, g_, __VA_ARGS__);                                 \

@@ -243,7 +243,7 @@ typedef struct sfa_attn {
   int32_t seqlen;   /* n >= 0 */
   int32_t hq;       /* query heads, multiple of hkv */
   int32_t hkv;      /* key/value heads; group size hq/hkv in {1, 2, 4, 8} */
-  int32_t head_dim; /* D in {16, 32, 64}, D/(hq/hkv) >= 2 */
+  int32_t head_dim; /* D in {16, 32, 64, 128} (128: bf16 only), D/(hq/hkv) >= 2 */
   int32_t dtype;    /* SFA_F32 or SFA_BF16, for Q, K, V, O, dO, dQ, dK, dV */
   int32_t window;   /* W >= 0: distances 0..W, self always present ([P1]) */
   int32_t n_off;    /* shared offsets, 0..SFA_MAX_OFFSETS */

@@ -201,8 +201,10 @@ def query_pass(n, window, lo, frac, D, G, want_dd=True, batch_kv=1, esize=2):
     rpl = rpl_small if (not want_dd or n_rungs <= rpl_small * nd) else 16
     qcap = bwd_query_cap(G, esize, rpl)
     # a CU holds two workgroups of 64 queries (fewer than 4 heads per KV
-    # head) or four of 16
-    check(bwd_query_lds(D, G, esize, rpl) * (2 if G < 4 else 4) <= 163840, "query-pass LDS per CU")
+    # head) or four of 16 at head dims up to 64; at 128 (bf16) a workgroup
+    # fits on its own
+    per_cu = (2 if G < 4 else 4) if D <= 64 else 1
+    check(bwd_query_lds(D, G, esize, rpl) * per_cu <= 163840, "query-pass LDS per CU")
     windows = [0] if (not want_dd or n_rungs <= rpl * nd) else list(range(0, n_rungs, rpl * nd))
     nblk = (n + bq - 1) // bq
     tiles = nblk * batch_kv

@@ -129,7 +129,8 @@ def _fwd(a, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None):
     (dict(hq=6, hkv=4), sfa.SFA_ERR_ARG),
     (dict(hq=0), sfa.SFA_ERR_ARG),
     (dict(hq=16, hkv=1), sfa.SFA_ERR_UNSUPPORTED),
-    (dict(head_dim=128), sfa.SFA_ERR_UNSUPPORTED),
+    (dict(head_dim=128, dtype=sfa.SFA_F32), sfa.SFA_ERR_UNSUPPORTED),
+    (dict(head_dim=256), sfa.SFA_ERR_UNSUPPORTED),
     (dict(head_dim=48), sfa.SFA_ERR_UNSUPPORTED),
     (dict(dtype=7), sfa.SFA_ERR_ARG),
     (dict(window=-1), sfa.SFA_ERR_ARG),
