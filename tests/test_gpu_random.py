@@ -1,6 +1,7 @@
 """Seeded random configurations of every key set, on the GPU, through the C
 ABI, against the oracle at the stated tolerances: shared offsets (below),
-power-law edge lists and signed (bidirectional) offsets (further below).
+power-law edge lists and signed (bidirectional) offsets (further below), and
+shared offsets at head dim 128 (bf16, last).
 
 Each case draws its own shape and offset table: fp32 or bf16; 1, 2, 4 or 8
 query heads per KV head over one or two KV heads; head dim 16, 32 or 64; one
@@ -117,3 +118,32 @@ def test_random_signed_offsets(idx):
     case = P.Case(c["B"], c["n"], c["hq"], c["hkv"], c["D"], c["dtype"], seed=c["seed"], rope_theta=c["theta"])
     P._fwd_check(case, c["W"], c["lo"], c["frac"], signed=True)
     P._bwd_check(case, c["W"], c["lo"], c["frac"], c["alpha"], c["base"], want_dd=c["want_dd"], signed=True)
+
+
+N_D128_CASES = 16
+
+
+def _draw_d128(idx):
+    # bf16 only (fp32 is refused at head dim 128)
+    rng = np.random.default_rng(SEED + 15485863 + 7919 * idx)
+    G = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.integers(1, 3))
+    n = int(rng.integers(1, 221))
+    n_rungs = int(rng.integers(0, 17))
+    base = np.sort(rng.choice(np.arange(1, max(2 * n, 4) + 1), size=min(n_rungs, max(2 * n, 4)), replace=False))
+    alpha = float(rng.uniform(0.55, 1.45))
+    return dict(dtype="bf16", hq=G * hkv, hkv=hkv, D=128, B=int(rng.integers(1, 3)), n=n, W=int(rng.integers(0, 13)),
+                base=base.astype(np.int32), alpha=alpha, theta=[1e4, 0.0][int(rng.integers(2))],
+                want_dd=bool(rng.integers(2)) and len(base) > 0, seed=int(rng.integers(1, 10_000)))
+
+
+@pytest.mark.parametrize("idx", range(N_D128_CASES))
+def test_random_head_dim_128(idx):
+    c = _draw_d128(idx)
+    sfa = P._sfa()
+    lo, frac = sfa.offsets_scaled(c["base"], c["alpha"])
+    print("d128 case %d: %s" % (idx, {k: (v.tolist() if isinstance(v, np.ndarray) else v) for k, v in c.items()}),
+          flush=True)
+    case = P.Case(c["B"], c["n"], c["hq"], c["hkv"], c["D"], c["dtype"], seed=c["seed"], rope_theta=c["theta"])
+    P._fwd_check(case, c["W"], lo, frac)
+    P._bwd_check(case, c["W"], lo, frac, c["alpha"], c["base"], want_dd=c["want_dd"])
