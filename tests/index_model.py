@@ -185,7 +185,7 @@ def bwd_query_lds(D, G, esize, rpl):
     ks = D + 4
     ksv = D // 2 + 4 if esize == 2 else ks
     nwv = bq * lpq // 64
-    return (cap + 1) * (ks + ksv) * 4 + nwv * rpl * (lpq // G) * 4 + nwv * 4
+    return (cap + 1) * (ks + ksv) * 4 + nwv * max(rpl * (lpq // G), 1) * 4 + nwv * 4
 
 
 def query_pass(n, window, lo, frac, D, G, want_dd=True, batch_kv=1, esize=2):
@@ -198,7 +198,9 @@ def query_pass(n, window, lo, frac, D, G, want_dd=True, batch_kv=1, esize=2):
     lpq, bq = bwd_lpq(D, G), bwd_bq(G)
     nd = lpq // G
     rpl_small = 1 if nd >= 16 else 16 // nd
-    rpl = rpl_small if (not want_dd or n_rungs <= rpl_small * nd) else 16
+    # no offset gradient: the RPL = 0 instantiation
+    dd_on = want_dd and n_rungs > 0
+    rpl = 0 if not dd_on else (rpl_small if n_rungs <= rpl_small * nd else 16)
     qcap = bwd_query_cap(G, esize, rpl)
     # a CU holds two workgroups of 64 queries (fewer than 4 heads per KV
     # head) or four of 16 at head dims up to 64; at 128 (bf16) a workgroup
