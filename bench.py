@@ -13,10 +13,11 @@ Cache) so HBM, not the cache, serves them.
 
 Prints ONE JSON line: queries/s of the whole step (value), the step's
 algorithmic HBM GB/s, a roofline object for the dominant kernel (timed with
-HIP events on its launch stream over the timed region; only that kernel's
-launches are bracketed there, since each recorded launch adds event packets
-that hold back the next kernel; the per-kernel breakdown comes from a second
-pass of the same steps with every launch recorded), the forward alone on
+HIP events on its launch stream over the timed region, taken by the
+dispatch itself as its start and end timestamps; only that kernel's launches
+are recorded there, since recording every launch lengthens the step; the
+per-kernel breakdown comes from a second pass of the same steps with every
+launch recorded), the forward alone on
 the fixed-alpha page-1 layer (window 8, integer rungs), and the fp64 CPU
 oracle timed on a bounded sample of the same step on one core, and on the
 whole batch over all host cores (one worker process per core, at most 16).
@@ -315,10 +316,11 @@ def main():
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
-    # Per-kernel breakdown: the same number of steps with every launch
-    # bracketed by HIP events on its stream.  Each recorded launch adds two
-    # event packets that also hold back the next kernel (about 35 us per
-    # step with all five kernels recorded), so this pass is not the timed one.
+    # Per-kernel breakdown: the same number of steps with every launch timed
+    # by HIP events on its stream.  With every kernel recorded the step runs
+    # longer and each kernel's average reads higher than with that kernel
+    # alone selected (page-1 query pass 139 against 129 us), so this pass is
+    # not the timed one.
     sfa.profile_reset()
     sfa.profile_enable(True)
     for t in range(args.steps):

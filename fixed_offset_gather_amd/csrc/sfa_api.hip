@@ -12,6 +12,7 @@
 
 #include "sfa_device.h"
 #include "sfa_internal.h"
+#include "sfa_launch.h"
 
 namespace sfa {
 
@@ -127,23 +128,38 @@ hipEvent_t take_event() {
 }
 }  // namespace
 
-ProfileScope::ProfileScope(const char* nm, void* st) : name(nm), stream(st), ev0(nullptr) {
+thread_local ProfileScope* tl_scope = nullptr;
+
+ProfileScope* active_profile_scope() { return tl_scope; }
+
+ProfileScope::ProfileScope(const char* nm, void* st) : name(nm), stream(st), ev0(nullptr), ev1(nullptr), launches(0) {
   if (!g_prof_on || !nm) return;  // a null name records nothing
   if (!g_prof_only.empty() && g_prof_only != nm) return;
-  hipEvent_t e = take_event();
-  if (e && hipEventRecord(e, static_cast<hipStream_t>(stream)) == hipSuccess) ev0 = e;
+  hipEvent_t a = take_event(), b = take_event();
+  if (!a || !b) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (a) g_free.push_back(a);
+    if (b) g_free.push_back(b);
+    return;
+  }
+  ev0 = a;
+  ev1 = b;
+  tl_scope = this;
 }
 
 ProfileScope::~ProfileScope() {
   if (!ev0) return;
-  hipEvent_t e = take_event();
+  tl_scope = nullptr;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  bool ok = launches > 0;  // the first launch took the pair
+  if (launches > 1) ok = hipEventRecord(static_cast<hipEvent_t>(ev1), st) == hipSuccess;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!e || hipEventRecord(e, static_cast<hipStream_t>(stream)) != hipSuccess) {
+  if (!ok) {
     g_free.push_back(static_cast<hipEvent_t>(ev0));
-    if (e) g_free.push_back(e);
+    g_free.push_back(static_cast<hipEvent_t>(ev1));
     return;
   }
-  g_pending.push_back({name, static_cast<hipEvent_t>(ev0), e});
+  g_pending.push_back({name, static_cast<hipEvent_t>(ev0), static_cast<hipEvent_t>(ev1)});
 }
 
 static void drain_pending() {
@@ -244,10 +260,10 @@ extern "C" int sfa_absmax(const void* x, int64_t count, int dtype, uint32_t* res
   const int blocks = int(std::min<int64_t>((count + per_block - 1) / per_block, 2048));
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == SFA_BF16)
-    hipLaunchKernelGGL(absmax_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, static_cast<const bf16_t*>(x), count,
+    SFA_LAUNCH(absmax_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, static_cast<const bf16_t*>(x), count,
                        reinterpret_cast<unsigned*>(result));
   else
-    hipLaunchKernelGGL(absmax_kernel<float>, dim3(blocks), dim3(256), 0, st, static_cast<const float*>(x), count,
+    SFA_LAUNCH(absmax_kernel<float>, dim3(blocks), dim3(256), 0, st, static_cast<const float*>(x), count,
                        reinterpret_cast<unsigned*>(result));
   return hip_status(int(hipGetLastError()), "sfa_absmax launch");
 }

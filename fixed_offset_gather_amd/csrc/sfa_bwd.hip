@@ -43,6 +43,7 @@
 
 #include "sfa_device.h"
 #include "sfa_internal.h"
+#include "sfa_launch.h"
 
 namespace sfa {
 
@@ -1398,16 +1399,16 @@ int launch_query_t(const BwdArgs& a0, const SlotTable& t, hipStream_t st) {
   // 312 -> 268 us bidirectional, against the dd-capable kernel with the
   // gradient switched off at run time).
   if (!dd) {
-    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<T, G, 0>(), BQ, 0>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+    SFA_LAUNCH((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<T, G, 0>(), BQ, 0>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
     return int(hipGetLastError());
   }
   if (t.n_rungs <= RS * ND) {
-    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<T, G, RS>(), BQ, RS>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
+    SFA_LAUNCH((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<T, G, RS>(), BQ, RS>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a, t);
     return int(hipGetLastError());
   }
   for (int r0 = 0; r0 < t.n_rungs; r0 += kRplLarge * ND) {
     a.r0 = r0;
-    hipLaunchKernelGGL((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<T, G, kRplLarge>(), BQ, kRplLarge>), dim3(a.tiles), dim3(BQ * LPQ), 0, st,
+    SFA_LAUNCH((bwd_query_kernel<T, D, G, LPQ, bwd_query_cap<T, G, kRplLarge>(), BQ, kRplLarge>), dim3(a.tiles), dim3(BQ * LPQ), 0, st,
                        a, t);
     if (hipError_t e = hipGetLastError()) return int(e);
   }
@@ -1429,12 +1430,12 @@ int launch_key_t(const BwdArgs& a0, const SlotTable& t, const ReduceArgs* ra, hi
     ReduceArgs r{};  // n_rungs = 0: no reduce workgroups
     if (ra) r = *ra;
     const int grid = (G == 1 ? a.tiles : 2 * a.tiles) + (r.n_rungs > 0 ? kNumXcd : 0);
-    hipLaunchKernelGGL((bwd_key_h16_kernel<D, G>), dim3(grid), dim3(KB), lds, st, a, steps, r);
+    SFA_LAUNCH((bwd_key_h16_kernel<D, G>), dim3(grid), dim3(KB), lds, st, a, steps, r);
   } else {
     constexpr int KB = key_block(sizeof(T), G, D);
     a.nblk = (a.n + KB - 1) / KB;
     a.tiles = a.nblk * (a0.tiles / a0.nblk) * (D / key_chunk(D));
-    hipLaunchKernelGGL((bwd_key_kernel<T, D, G>), dim3(a.tiles), dim3(KB), 0, st, a, t);
+    SFA_LAUNCH((bwd_key_kernel<T, D, G>), dim3(a.tiles), dim3(KB), 0, st, a, t);
   }
   return int(hipGetLastError());
 }
@@ -1765,7 +1766,7 @@ int launch_edges_t(const EdgeBwdArgs& a0, hipStream_t st) {
     ProfileScope ps("bwd_edges_query", st);
     a.nblk = (a.n + kEdgeBQ - 1) / kEdgeBQ;
     a.tiles = a.nblk * seqs;
-    hipLaunchKernelGGL((bwd_edges_query_kernel<T, D, G, LPQ>), dim3(a.tiles), dim3(kEdgeBQ * LPQ), 0, st, a);
+    SFA_LAUNCH((bwd_edges_query_kernel<T, D, G, LPQ>), dim3(a.tiles), dim3(kEdgeBQ * LPQ), 0, st, a);
   }
   if (hipError_t e = hipGetLastError()) return int(e);
   {
@@ -1773,7 +1774,7 @@ int launch_edges_t(const EdgeBwdArgs& a0, hipStream_t st) {
     constexpr int KPW = kEdgeKB / (D / key_chunk(D));
     a.nblk = (a.n + KPW - 1) / KPW;
     a.tiles = a.nblk * seqs;
-    hipLaunchKernelGGL((bwd_edges_key_kernel<T, D, G>), dim3(a.tiles), dim3(kEdgeKB), 0, st, a);
+    SFA_LAUNCH((bwd_edges_key_kernel<T, D, G>), dim3(a.tiles), dim3(kEdgeKB), 0, st, a);
   }
   return int(hipGetLastError());
 }
@@ -1858,7 +1859,7 @@ int launch_bwd_reduce(const SlotTable& t, const BwdWorkspace& ws, const float* b
                       float* dtheta, void* stream) {
   ReduceArgs a{};
   fill_reduce_args(&a, t, ws, base_f, alpha, dd, dtheta);
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, static_cast<hipStream_t>(stream), a);
+  SFA_LAUNCH(bwd_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, static_cast<hipStream_t>(stream), a);
   return int(hipGetLastError());
 }
 

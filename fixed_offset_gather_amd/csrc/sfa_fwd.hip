@@ -25,6 +25,7 @@
 // from global memory (L2-resident) with the same lane layout.
 #include "sfa_device.h"
 #include "sfa_internal.h"
+#include "sfa_launch.h"
 
 namespace sfa {
 
@@ -817,15 +818,15 @@ void launch_fwd_offsets_i(const SlotTable& t, const FwdArgs& a0, hipStream_t st)
     a.tiles = a.nblk * a.tiles_per_blk;
     // Integer offsets without rotation read the bf16 K rows as they are.
     if (!INTERP && a.rope == nullptr)
-      hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, BQH, kCap, false, true>),
+      SFA_LAUNCH((fwd_offsets_h16_kernel<D, G, LPQ, BQH, kCap, false, true>),
                          dim3(a.tiles), dim3(BQH * LPQ), 3 * 4 * t.count, st, a, t);
     else
-      hipLaunchKernelGGL((fwd_offsets_h16_kernel<D, G, LPQ, BQH, kCap, INTERP, false>),
+      SFA_LAUNCH((fwd_offsets_h16_kernel<D, G, LPQ, BQH, kCap, INTERP, false>),
                          dim3(a.tiles), dim3(BQH * LPQ), 3 * 4 * t.count, st, a, t);
   } else {
     constexpr int LPQ = fwd_lpq<D, G>();
     const FwdArgs& a = a0;
-    hipLaunchKernelGGL((fwd_offsets_kernel<T, D, G, LPQ, kCap, INTERP>), dim3(a.tiles), dim3(BQ * LPQ),
+    SFA_LAUNCH((fwd_offsets_kernel<T, D, G, LPQ, kCap, INTERP>), dim3(a.tiles), dim3(BQ * LPQ),
                        3 * 4 * t.count, st, a,
                        t);
   }
@@ -850,11 +851,11 @@ int launch_fwd_edges_t(const EdgeArgs& a, hipStream_t st) {
   constexpr int LPQ = fwd_lpq<D, G>();
   if constexpr (sizeof(T) == 2) {
     if (a.rope == nullptr) {  // bf16 without rotation: raw rows
-      hipLaunchKernelGGL((fwd_edges_kernel<T, D, G, LPQ, true>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a);
+      SFA_LAUNCH((fwd_edges_kernel<T, D, G, LPQ, true>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a);
       return int(hipGetLastError());
     }
   }
-  hipLaunchKernelGGL((fwd_edges_kernel<T, D, G, LPQ, false>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a);
+  SFA_LAUNCH((fwd_edges_kernel<T, D, G, LPQ, false>), dim3(a.tiles), dim3(BQ * LPQ), 0, st, a);
   return int(hipGetLastError());
 }
 

@@ -110,12 +110,22 @@ int bwd_impl(const sfa_attn* a, const void* q, const void* k, const void* v, con
 size_t bwd_workspace_bytes(const sfa_attn* a);
 
 // Event-pair bracketing for sfa_profile_*; no-ops while profiling is off.
+// While a scope records, the first launch inside it (through SFA_LAUNCH)
+// takes the pair as the dispatch's own start and end timestamps
+// (hipExtLaunchKernelGGL), so no event packets enter the stream to hold
+// back the next kernel.  A scope with more launches re-records its end
+// event after the last one; a scope without a launch records nothing.
 struct ProfileScope {
   ProfileScope(const char* name, void* stream);
   ~ProfileScope();
   const char* name;
   void* stream;
   void* ev0;
+  void* ev1;
+  int launches;  // launches made through SFA_LAUNCH inside the scope
 };
+
+// The recording scope of this thread, or null.
+ProfileScope* active_profile_scope();
 
 }  // namespace sfa

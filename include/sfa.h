@@ -354,16 +354,18 @@ int sfa_bwd_edges(const sfa_attn* a, const int32_t* edges, const int32_t* count,
 /* ------------------------------------------------------------------ */
 
 /*
- * When enabled, every kernel launch is bracketed by two HIP events recorded
- * on its launch stream.  sfa_profile_read synchronises the recorded events
+ * When enabled, every kernel launch is timed by two HIP events on its launch
+ * stream, which the dispatch itself takes as its start and end timestamps
+ * (a call that launches one kernel several times re-records the end event
+ * after the last launch).  sfa_profile_read synchronises the recorded events
  * and returns the accumulated milliseconds and launch count of the named
  * kernel ("fwd_offsets", "fwd_edges", "bwd_query", "bwd_key",
  * "bwd_edges_query", "bwd_edges_key", "bwd_reduce"; with bf16 tensors the
  * dd reduction runs inside the "bwd_key" launch);
  * sfa_profile_reset drops all records.  sfa_profile_select(name) restricts
- * the recording to the launches of the named kernel (each recorded launch
- * adds two event packets to its stream, which also delay the stream's next
- * kernel); sfa_profile_select(NULL) records every kernel again.  Not
+ * the recording to the launches of the named kernel (recording every kernel
+ * lengthens a step, and each kernel's average reads higher than with that
+ * kernel alone selected); sfa_profile_select(NULL) records every kernel again.  Not
  * thread-safe with concurrent launches.
  */
 int sfa_profile_enable(int on);
